@@ -1,0 +1,128 @@
+/*
+ * wqbmm.h -- C ABI of the MI355X (gfx950) A16W4 per-group MSD matmul.
+ *
+ *     y = MSD(x, dequant(w))        x: fp16 [M][K], w: int4 [K][N], y: fp16 [M][N]
+ *
+ * The operation is the one specified on the page "WeightQuantBatchMatmulExperiment
+ * 算子深度解析：A16W4 PerGroup 伪量化 MatMul 的 MSD 算法与双模板流水设计"
+ * (lpnh.cn/news/2294145, "the WQBMM-Exp page"):
+ *   - §4.2 (算子规格): x1 M x K fp16 ND, x2 K x N int4 ND, antiquant_scale
+ *     GroupNum x N fp16 ND, y M x N fp16 ND; only these dtypes are accepted.
+ *   - §4.1 (MSD 伪量化算法): per (row, K-group) A_max = max|x|; three rounds of
+ *     round(7.49*x/A_max), round(residual*14.98), round(residual*14.98) give
+ *     int4-range matrices A1, A2, A3; each is contracted with the group's int4
+ *     weights in integer arithmetic; the three results are combined as
+ *     (Y1/7.49 + Y2/(7.49*14.98) + Y3/(7.49*14.98^2)) * A_max * scale and
+ *     accumulated over groups.
+ *   - §4.3: int4 weights are stored two per byte.
+ *
+ * Conventions for every entry point:
+ *   - Array pointers are DEVICE pointers (HIP device memory of the current
+ *     device) owned by the caller; the library never retains or frees them.
+ *     Row-major ("ND") layouts, no padding between rows.
+ *   - fp16 arrays hold IEEE binary16 values.
+ *   - w_packed_int4 is uint8 [K][N/2]: byte (k, j) holds column 2j in bits 0-3
+ *     and column 2j+1 in bits 4-7, each a 4-bit two's-complement value in [-8, 7].
+ *   - stream is a hipStream_t (NULL = the legacy default stream).  All work is
+ *     enqueued asynchronously on it; nothing synchronizes the host.  Faults in
+ *     device code surface at the caller's next synchronization, as with any
+ *     stream API.
+ *   - Arguments are validated on the host before any device work, in the
+ *     order: null pointers -> shapes -> support.  On error nothing is launched
+ *     and outputs are untouched.
+ *   - Shape rules: M >= 0 (M == 0 is a no-op returning WQBMM_OK; the arrays
+ *     with an M extent -- x, y, a_int, a_max, y_int -- may then be NULL), K >= 1,
+ *     N >= 1, K % group_size == 0, N % 32 == 0, M <= 2^24, K <= 2^20,
+ *     N <= 2^20, every pointer 16-byte aligned.
+ *   - group_size must be 64 or 128 (other positive values: WQBMM_ERR_UNSUPPORTED).
+ *   - The library keeps a per-(device, stream) workspace that it allocates on
+ *     first use and grows on demand (hipMalloc; a growth synchronizes that
+ *     stream first).  Calls on different streams do not share workspace.
+ *   - Results are deterministic: the same inputs give bit-identical outputs.
+ *   - Only gfx950 (MI355X) is supported: other devices give WQBMM_ERR_UNSUPPORTED.
+ *   - Finite inputs are assumed; Inf/NaN inputs give unspecified outputs.
+ */
+#ifndef WQBMM_H
+#define WQBMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum wqbmm_status {
+  WQBMM_OK = 0,
+  WQBMM_ERR_NULLPTR = 1,     /* a required pointer is NULL                       */
+  WQBMM_ERR_INVALID = 2,     /* a shape / alignment rule above is violated       */
+  WQBMM_ERR_UNSUPPORTED = 3, /* group_size not 64/128, or the device is not gfx950 */
+  WQBMM_ERR_LAUNCH = 4,      /* a HIP call or kernel launch failed               */
+  WQBMM_ERR_ALLOC = 5        /* workspace allocation failed                      */
+} wqbmm_status;
+
+/* Kernel path selector for the *_path / *_yint entry points. */
+typedef enum wqbmm_path {
+  WQBMM_PATH_AUTO = 0,     /* what wqbmm_a16w4_msd picks (wqbmm_select_path)      */
+  WQBMM_PATH_DECODE = 1,   /* fused split-K decode kernel; valid for M <= 16     */
+  WQBMM_PATH_PREFILL = 2   /* MSD pre-pass + int8 MFMA GEMM; any M               */
+} wqbmm_path;
+
+/*
+ * The operator (WQBMM-Exp page §4.1 steps 1-11, §4.2).
+ *   x               fp16  [M][K]
+ *   w_packed_int4   uint8 [K][N/2]            (format above)
+ *   antiquant_scale fp16  [K/group_size][N]   (per group of K, per column)
+ *   y               fp16  [M][N]              (write-only, fully overwritten)
+ * y[m][n] is the round-to-nearest-even fp16 of the fp32 sum over groups.
+ */
+wqbmm_status wqbmm_a16w4_msd(const void* x, const void* w_packed_int4,
+                             const void* antiquant_scale, int64_t group_size,
+                             int64_t M, int64_t K, int64_t N, void* y,
+                             void* stream);
+
+/* Same operation with an explicit kernel path (WQBMM_PATH_*).  The decode
+ * path with M > 16 returns WQBMM_ERR_INVALID. */
+wqbmm_status wqbmm_a16w4_msd_path(const void* x, const void* w_packed_int4,
+                                  const void* antiquant_scale, int64_t group_size,
+                                  int64_t M, int64_t K, int64_t N, void* y,
+                                  int path, void* stream);
+
+/*
+ * Steps 1-8 alone (WQBMM-Exp page §4.1: A_max, tmp1..tmp3, A1..A3, A_int),
+ * computed by the same device routine every path uses.
+ *   x      fp16 [M][K]
+ *   a_int  int8 [3][M][K]   level-major: A1 rows, then A2 rows, then A3 rows
+ *   a_max  fp32 [M][K/group_size]
+ * Each level value lies in [-7, 7].  A group whose A_max is 0 gives zeros.
+ */
+wqbmm_status wqbmm_a16w4_msd_prepass(const void* x, int64_t group_size,
+                                     int64_t M, int64_t K, int8_t* a_int,
+                                     float* a_max, void* stream);
+
+/*
+ * Steps 1-9 for the groups [g_begin, g_end) (WQBMM-Exp page §4.1 step 9:
+ * Y_int = A_int . Weight_group), through the same kernels as the chosen path,
+ * stopping before the fp32 combine.
+ *   y_int  int32 [g_end-g_begin][3][M][N]
+ *          y_int[g-g_begin][l][m][n] = sum over k in group g of A_l[m][k]*w[k][n]
+ * Requires 0 <= g_begin < g_end <= K/group_size (else WQBMM_ERR_INVALID).
+ */
+wqbmm_status wqbmm_a16w4_msd_yint(const void* x, const void* w_packed_int4,
+                                  int64_t group_size, int64_t M, int64_t K,
+                                  int64_t N, int64_t g_begin, int64_t g_end,
+                                  int32_t* y_int, int path, void* stream);
+
+/* The path wqbmm_a16w4_msd takes for this shape (WQBMM_PATH_DECODE or
+ * WQBMM_PATH_PREFILL).  Pure host function. */
+int wqbmm_select_path(int64_t M, int64_t K, int64_t N, int64_t group_size);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* wqbmm_status_string(int status);
+
+/* Library ABI version: major*10000 + minor*100 + patch. */
+int wqbmm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* WQBMM_H */

@@ -1,0 +1,292 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Method: the page "WeightQuantBatchMatmulExperiment 算子深度解析：A16W4 PerGroup
+伪量化 MatMul 的 MSD 算法与双模板流水设计" (lpnh.cn/news/2294145), §4.1.
+
+Bars:
+  * A_int (steps 1-8) byte-identical and A_max bit-identical to the oracle;
+  * Y_int (step 9) word-identical to the oracle, on both kernel paths;
+  * y (steps 10-11, fp16) against the oracle's fp32 Y32:
+        ||y - Y32||_2 / ||Y32||_2 <= 1e-3   and   max|y - Y32| <= 2e-2 * max|Y32|;
+  * run-to-run bit-identical y.
+Inputs are the seeded synthetic workloads of weight_only_quantized_msd_amd.datagen.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from weight_only_quantized_msd_amd import datagen
+
+pytestmark = pytest.mark.gpu
+
+REL_L2 = 1e-3
+MAX_ABS_FRAC = 2e-2
+
+DECODE, PREFILL, AUTO = 1, 2, 0
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import weight_only_quantized_msd_amd as W  # noqa: F401  (loads libwqbmm.so)
+    W.lib()
+    return torch
+
+
+def announce(msg):
+    print(f"\n[gpu case] {msg}", flush=True)
+
+
+_cache = {}
+
+
+def workload(name, M=None):
+    key = (name, M)
+    if key not in _cache:
+        _cache[key] = datagen.make_inputs(name, M=M)
+    return _cache[key]
+
+
+def to_dev(torch, d):
+    return (torch.from_numpy(d["x"]).cuda(), torch.from_numpy(d["w_packed"]).cuda(),
+            torch.from_numpy(d["scale"]).cuda())
+
+
+def check_y(y, y32, what):
+    y = y.astype(np.float64)
+    ref = y32.astype(np.float64)
+    nref = np.linalg.norm(ref)
+    rel = np.linalg.norm(y - ref) / max(nref, 1e-30)
+    mabs = np.abs(y - ref).max() if y.size else 0.0
+    lim = MAX_ABS_FRAC * (np.abs(ref).max() if ref.size else 0.0)
+    assert rel <= REL_L2 or nref == 0, f"{what}: rel-L2 {rel:.3e}"
+    assert mabs <= lim or nref == 0, f"{what}: max-abs {mabs:.3e} > {lim:.3e}"
+    if nref == 0:
+        assert np.count_nonzero(y) == 0, what
+
+
+def sample_rows(M, n, seed):
+    if M <= n:
+        return np.arange(M)
+    rng = np.random.default_rng(seed)
+    rest = rng.choice(np.arange(1, M - 1), n - 2, replace=False)
+    return np.sort(np.concatenate([[0, M - 1], rest]))
+
+
+ALL = ["tiny", "decode_m1", "decode_m16", "ffn_up_m16", "prefill_m2048", "outlier_m128",
+       "pages_sample_m1"]
+
+
+# ------------------------------------------------------------------ steps 1-8
+
+@pytest.mark.parametrize("name", ALL)
+def test_prepass_bit_exact(torch_dev, name):
+    import weight_only_quantized_msd_amd as W
+    torch = torch_dev
+    d = workload(name)
+    gs = d["group_size"]
+    announce(f"prepass {name} M={d['M']} K={d['K']} gs={gs}")
+    a_int, a_max = W.wqbmm_a16w4_msd_prepass(torch.from_numpy(d["x"]).cuda(), gs)
+    torch.cuda.synchronize()
+    ra, rm = oracle.decompose(d["x"], gs)
+    assert np.array_equal(a_int.cpu().numpy(), ra)
+    assert np.array_equal(a_max.cpu().numpy().view(np.uint32), rm.view(np.uint32))
+
+
+def adversarial_x(seed, M, K, gs):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    x[0, :gs] = 0.0                                    # all-zero group
+    x[0, gs:2 * gs] *= 1e-5                            # fp16 subnormals
+    if M > 1:
+        x[1, ::5] *= 500.0                             # outlier channels
+        x[1, 2 * gs:3 * gs] = 0.75                     # constant group
+    if M > 2:
+        x[2] = -np.abs(x[2])
+    x = x.astype(np.float16)
+    # exact-tie and op-order vectors (element, its group max) at the start of a group
+    import json, os
+    fx = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "msd_tie_vectors.json")))
+    pairs = fx["vectors"] + fx["order_vectors"]
+    for i, v in enumerate(pairs):
+        r, g = (i % M), (3 + i // M)
+        if (g + 1) * gs > K:
+            break
+        a = np.uint16(int(v["a"], 16)).view(np.float16)
+        m = np.uint16(int(v["amax"], 16)).view(np.float16)
+        blk = np.zeros(gs, np.float16)
+        blk[0], blk[1] = a, m
+        x[r, g * gs:(g + 1) * gs] = blk
+    return x
+
+
+@pytest.mark.parametrize("M,K,gs", [(1, 64, 64), (3, 1024, 64), (5, 2048, 128), (33, 1920, 128)])
+def test_prepass_edge_cases(torch_dev, M, K, gs):
+    import weight_only_quantized_msd_amd as W
+    torch = torch_dev
+    x = adversarial_x(M * 7 + K, M, K, gs)
+    announce(f"prepass edge M={M} K={K} gs={gs}")
+    a_int, a_max = W.wqbmm_a16w4_msd_prepass(torch.from_numpy(x).cuda(), gs)
+    torch.cuda.synchronize()
+    ra, rm = oracle.decompose(x, gs)
+    assert np.array_equal(a_int.cpu().numpy(), ra)
+    assert np.array_equal(a_max.cpu().numpy().view(np.uint32), rm.view(np.uint32))
+
+
+# ------------------------------------------------------------------ step 9
+
+YINT_CASES = [
+    ("tiny", DECODE, None), ("tiny", PREFILL, None),
+    ("decode_m1", DECODE, None), ("decode_m1", PREFILL, (0, 5)),
+    ("decode_m16", DECODE, None), ("decode_m16", PREFILL, (7, 12)),
+    ("ffn_up_m16", DECODE, (0, 32)),
+    ("prefill_m2048", PREFILL, (0, 1)), ("prefill_m2048", PREFILL, (31, 32)),
+    ("outlier_m128", PREFILL, (0, 2)), ("outlier_m128", PREFILL, (126, 128)),
+    ("pages_sample_m1", DECODE, (0, 64)),
+]
+
+
+@pytest.mark.parametrize("name,path,grange", YINT_CASES,
+                         ids=[f"{c[0]}-{'dec' if c[1] == 1 else 'pre'}-{c[2]}" for c in YINT_CASES])
+def test_yint_word_exact(torch_dev, name, path, grange):
+    import weight_only_quantized_msd_amd as W
+    torch = torch_dev
+    d = workload(name)
+    gs, G = d["group_size"], d["K"] // d["group_size"]
+    gb, ge = grange if grange else (0, G)
+    x, w, _ = to_dev(torch, d)
+    announce(f"yint {name} path={path} groups=[{gb},{ge})")
+    yi = W.wqbmm_a16w4_msd_yint(x, w, gs, gb, ge, path=path)
+    torch.cuda.synchronize()
+    ra, _ = oracle.decompose(d["x"], gs)
+    ref = oracle.yint(ra, d["w"], gs, gb, ge)
+    got = yi.cpu().numpy()
+    assert np.array_equal(got, ref), f"{np.count_nonzero(got != ref)} words differ"
+
+
+# ------------------------------------------------------------------ steps 10-11
+
+Y_CASES = [
+    ("tiny", AUTO, None), ("tiny", PREFILL, None),
+    ("decode_m1", AUTO, None), ("decode_m1", PREFILL, None),
+    ("decode_m16", AUTO, None), ("decode_m16", PREFILL, None),
+    ("ffn_up_m16", AUTO, None),
+    ("prefill_m2048", AUTO, 24),
+    ("outlier_m128", AUTO, 8),
+    ("pages_sample_m1", AUTO, None),
+]
+
+
+@pytest.mark.parametrize("name,path,nrows", Y_CASES,
+                         ids=[f"{c[0]}-{['auto', 'dec', 'pre'][c[1]]}" for c in Y_CASES])
+def test_y_within_tolerance(torch_dev, name, path, nrows):
+    import weight_only_quantized_msd_amd as W
+    torch = torch_dev
+    d = workload(name)
+    gs = d["group_size"]
+    x, w, s = to_dev(torch, d)
+    announce(f"y {name} path={path} M={d['M']} K={d['K']} N={d['N']}")
+    y = W.wqbmm_a16w4_msd_path(x, w, s, gs, path)
+    torch.cuda.synchronize()
+    rows = None if nrows is None else sample_rows(d["M"], nrows, 17)
+    y32, _ = oracle.matmul(d["x"], d["w_packed"], d["scale"], gs, rows=rows)
+    got = y.cpu().numpy()
+    got = got if rows is None else got[rows]
+    check_y(got, y32, name)
+
+
+RAGGED = [  # (M, K, N, gs)
+    (1, 64, 32, 64), (2, 128, 96, 128), (3, 192, 160, 64), (4, 640, 288, 128),
+    (5, 576, 4128, 64), (13, 1024, 416, 128), (16, 2560, 544, 128), (17, 512, 160, 64),
+    (130, 384, 288, 128), (257, 256, 128, 64),
+]
+
+
+@pytest.mark.parametrize("M,K,N,gs", RAGGED, ids=[f"M{c[0]}K{c[1]}N{c[2]}g{c[3]}" for c in RAGGED])
+def test_ragged_shapes(torch_dev, M, K, N, gs):
+    import weight_only_quantized_msd_amd as W
+    torch = torch_dev
+    d = datagen.random_case(M, K, N, gs, seed=M * 1000 + N)
+    d["x"] = adversarial_x(M + K, M, K, gs) if K >= 4 * gs else d["x"]
+    x, w, s = to_dev(torch, d)
+    y32, _ = oracle.matmul(d["x"], d["w_packed"], d["scale"], gs)
+    ra, _ = oracle.decompose(d["x"], gs)
+    G = K // gs
+    ref_yi = oracle.yint(ra, d["w"], gs, 0, G)
+    paths = (DECODE, PREFILL) if M <= 16 else (PREFILL,)
+    for p in paths:
+        announce(f"ragged M={M} K={K} N={N} gs={gs} path={p}")
+        y = W.wqbmm_a16w4_msd_path(x, w, s, gs, p)
+        yi = W.wqbmm_a16w4_msd_yint(x, w, gs, 0, G, path=p)
+        torch.cuda.synchronize()
+        check_y(y.cpu().numpy(), y32, f"path {p}")
+        assert np.array_equal(yi.cpu().numpy(), ref_yi), f"path {p} Y_int"
+
+
+def test_zero_weights_give_exact_zero(torch_dev):
+    import weight_only_quantized_msd_amd as W
+    torch = torch_dev
+    d = datagen.random_case(16, 1024, 256, 128, seed=3)
+    x = torch.from_numpy(d["x"]).cuda()
+    w = torch.zeros((1024, 128), dtype=torch.uint8, device="cuda")
+    s = torch.from_numpy(d["scale"]).cuda()
+    for p in (DECODE, PREFILL):
+        announce(f"zero weights path={p}")
+        y = W.wqbmm_a16w4_msd_path(x, w, s, 128, p)
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(y).item() == 0
+
+
+# ------------------------------------------------------------------ determinism, streams, reuse
+
+@pytest.mark.parametrize("name,path", [("decode_m16", DECODE), ("ffn_up_m16", DECODE),
+                                       ("prefill_m2048", PREFILL), ("decode_m1", PREFILL)])
+def test_run_to_run_bit_identical(torch_dev, name, path):
+    import weight_only_quantized_msd_amd as W
+    torch = torch_dev
+    d = workload(name)
+    x, w, s = to_dev(torch, d)
+    announce(f"determinism {name} path={path}")
+    y1 = W.wqbmm_a16w4_msd_path(x, w, s, d["group_size"], path)
+    y2 = W.wqbmm_a16w4_msd_path(x, w, s, d["group_size"], path)
+    y3 = W.wqbmm_a16w4_msd_path(x, w, s, d["group_size"], path)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(y1.view(torch.int16), y3.view(torch.int16))
+
+
+def test_side_stream_and_alternating_shapes(torch_dev):
+    """The split-K counters re-arm themselves: alternating shapes on one stream
+    and a second stream with its own workspace give the same results."""
+    import weight_only_quantized_msd_amd as W
+    torch = torch_dev
+    outs = {}
+    for name in ("decode_m16", "ffn_up_m16", "decode_m1"):
+        d = workload(name)
+        x, w, s = to_dev(torch, d)
+        announce(f"reference {name}")
+        outs[name] = (x, w, s, d["group_size"], W.wqbmm_a16w4_msd(x, w, s, d["group_size"]).clone())
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    for rep in range(3):
+        for name, (x, w, s, gs, ref) in outs.items():
+            announce(f"repeat {rep} {name}")
+            y = W.wqbmm_a16w4_msd(x, w, s, gs)
+            with torch.cuda.stream(side):
+                y_side = W.wqbmm_a16w4_msd(x, w, s, gs)
+            torch.cuda.synchronize()
+            assert torch.equal(y.view(torch.int16), ref.view(torch.int16)), name
+            assert torch.equal(y_side.view(torch.int16), ref.view(torch.int16)), name
+
+
+def test_empty_batch_is_noop(torch_dev):
+    import weight_only_quantized_msd_amd as W
+    torch = torch_dev
+    x = torch.empty((0, 256), dtype=torch.float16, device="cuda")
+    w = torch.zeros((256, 64), dtype=torch.uint8, device="cuda")
+    s = torch.ones((4, 128), dtype=torch.float16, device="cuda")
+    y = W.wqbmm_a16w4_msd(x, w, s, 64)
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (0, 128)

@@ -1,0 +1,107 @@
+"""A16W4 per-group MSD weight-quantized matmul for AMD MI355X (gfx950).
+
+    y = wqbmm_a16w4_msd(x, w_packed_int4, antiquant_scale, group_size)
+
+x: fp16 [M][K]; w_packed_int4: uint8 [K][N/2] (two int4 per byte, column 2j in
+the low nibble); antiquant_scale: fp16 [K/group_size][N]; y: fp16 [M][N].
+
+The method is the multi-step decomposition (MSD) of the page
+"WeightQuantBatchMatmulExperiment 算子深度解析：A16W4 PerGroup 伪量化 MatMul 的
+MSD 算法与双模板流水设计" (lpnh.cn/news/2294145), §4.1.  Everything runs in
+the HIP kernels of libwqbmm.so behind the C ABI of include/wqbmm.h; these
+wrappers only check tensor metadata and pass device pointers and the
+current HIP stream.  PyTorch supplies device memory and streams.
+"""
+from __future__ import annotations
+
+from ._lib import (WQBMM_ERR_ALLOC, WQBMM_ERR_INVALID, WQBMM_ERR_LAUNCH,  # noqa: F401
+                   WQBMM_ERR_NULLPTR, WQBMM_ERR_UNSUPPORTED, WQBMM_OK, WQBMM_PATH_AUTO,
+                   WQBMM_PATH_DECODE, WQBMM_PATH_PREFILL, WqbmmError, check, lib,
+                   status_string, wqbmm_select_path, wqbmm_version)
+
+__all__ = [
+    "wqbmm_a16w4_msd", "wqbmm_a16w4_msd_path", "wqbmm_a16w4_msd_prepass",
+    "wqbmm_a16w4_msd_yint", "wqbmm_select_path", "wqbmm_status_string", "wqbmm_version",
+    "WqbmmError",
+]
+
+
+def wqbmm_status_string(status: int) -> str:
+    return status_string(status)
+
+
+def _stream_ptr(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream)
+
+
+def _require(t, dtype, ndim, name):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {ndim}-D tensor")
+
+
+def wqbmm_a16w4_msd_path(x, w_packed_int4, antiquant_scale, group_size: int, path: int,
+                         y=None, stream=None):
+    import torch
+    _require(x, torch.float16, 2, "x")
+    _require(w_packed_int4, torch.uint8, 2, "w_packed_int4")
+    _require(antiquant_scale, torch.float16, 2, "antiquant_scale")
+    M, K = x.shape
+    N = w_packed_int4.shape[1] * 2
+    if w_packed_int4.shape[0] != K or antiquant_scale.shape[1] != N or (
+            group_size > 0 and antiquant_scale.shape[0] * group_size != K):
+        raise ValueError("inconsistent shapes: x [M][K], w [K][N/2], scale [K/gs][N]")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    else:
+        _require(y, torch.float16, 2, "y")
+        if tuple(y.shape) != (M, N):
+            raise ValueError("y must be [M][N]")
+    st = lib().wqbmm_a16w4_msd_path(x.data_ptr(), w_packed_int4.data_ptr(),
+                                    antiquant_scale.data_ptr(), int(group_size), M, K, N,
+                                    y.data_ptr(), int(path), _stream_ptr(stream))
+    check(st, "wqbmm_a16w4_msd")
+    return y
+
+
+def wqbmm_a16w4_msd(x, w_packed_int4, antiquant_scale, group_size: int, y=None, stream=None):
+    """The operator; returns y (fp16 [M][N]).  Asynchronous on the current stream."""
+    return wqbmm_a16w4_msd_path(x, w_packed_int4, antiquant_scale, group_size,
+                                WQBMM_PATH_AUTO, y=y, stream=stream)
+
+
+def wqbmm_a16w4_msd_prepass(x, group_size: int, stream=None):
+    """Steps 1-8: returns (a_int int8 [3][M][K], a_max fp32 [M][K/gs])."""
+    import torch
+    _require(x, torch.float16, 2, "x")
+    M, K = x.shape
+    a_int = torch.empty((3, M, K), dtype=torch.int8, device=x.device)
+    a_max = torch.empty((M, K // max(int(group_size), 1)), dtype=torch.float32, device=x.device)
+    st = lib().wqbmm_a16w4_msd_prepass(x.data_ptr(), int(group_size), M, K, a_int.data_ptr(),
+                                       a_max.data_ptr(), _stream_ptr(stream))
+    check(st, "wqbmm_a16w4_msd_prepass")
+    return a_int, a_max
+
+
+def wqbmm_a16w4_msd_yint(x, w_packed_int4, group_size: int, g_begin: int, g_end: int,
+                         path: int = WQBMM_PATH_AUTO, stream=None):
+    """Steps 1-9 for groups [g_begin, g_end): int32 [g_end-g_begin][3][M][N]."""
+    import torch
+    _require(x, torch.float16, 2, "x")
+    _require(w_packed_int4, torch.uint8, 2, "w_packed_int4")
+    M, K = x.shape
+    N = w_packed_int4.shape[1] * 2
+    y_int = torch.empty((max(g_end - g_begin, 0), 3, M, N), dtype=torch.int32, device=x.device)
+    st = lib().wqbmm_a16w4_msd_yint(x.data_ptr(), w_packed_int4.data_ptr(), int(group_size),
+                                    M, K, N, int(g_begin), int(g_end), y_int.data_ptr(),
+                                    int(path), _stream_ptr(stream))
+    check(st, "wqbmm_a16w4_msd_yint")
+    return y_int

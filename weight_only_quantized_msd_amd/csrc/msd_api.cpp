@@ -1,0 +1,235 @@
+// msd_api.cpp -- host side of the C ABI declared in include/wqbmm.h:
+// argument validation, kernel-path dispatch and the library-owned workspace.
+//
+// Operator: the page "WeightQuantBatchMatmulExperiment 算子深度解析：A16W4 PerGroup
+// 伪量化 MatMul 的 MSD 算法与双模板流水设计" (lpnh.cn/news/2294145), §4.1-§4.2.
+// Its host tiling rejects anything but 2-D fp16 x / int4 weight / fp16 y
+// (§4.2, last sentence); the dtypes here are fixed by the entry points and the
+// shape rules are checked before any device call, in the order null pointer ->
+// shape -> support, like the aclnn parameter checks (nullptr, then invalid
+// shape, then unsupported product) described on the page "CANN
+// ops-math：aclnnCalculateMatmulWeightSizeV2 接口详解" (zskr.cn/news/2299903),
+// section 返回值说明.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "../../include/wqbmm.h"
+#include "msd_launch.hpp"
+
+namespace {
+
+using wqbmm::DecodePlan;
+
+constexpr int64_t kMaxM = int64_t(1) << 24;
+constexpr int64_t kMaxK = int64_t(1) << 20;
+constexpr int64_t kMaxN = int64_t(1) << 20;
+constexpr int kDecodeMaxM = 16;
+// Counter words for the decode split-K reduction live in a fixed prefix of the
+// workspace that no other kernel writes: one per 128-column block.
+constexpr size_t kCounterBytes = size_t(kMaxN / 128) * sizeof(uint32_t);
+
+// NULL counts as aligned: it is only accepted where the array is empty (M == 0).
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+wqbmm_status check_shape(int64_t gs, int64_t M, int64_t K, int64_t N) {
+  if (gs <= 0 || M < 0 || K <= 0 || N <= 0) return WQBMM_ERR_INVALID;
+  if (M > kMaxM || K > kMaxK || N > kMaxN) return WQBMM_ERR_INVALID;
+  if (K % gs != 0 || N % 32 != 0) return WQBMM_ERR_INVALID;
+  return WQBMM_OK;
+}
+
+wqbmm_status check_support(int64_t gs) {
+  return (gs == 64 || gs == 128) ? WQBMM_OK : WQBMM_ERR_UNSUPPORTED;
+}
+
+// ---- device check (gfx950 only), cached per device
+std::mutex g_mu;
+std::map<int, bool> g_arch_ok;
+
+wqbmm_status check_device(int* dev_out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return WQBMM_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lk(g_mu);
+  auto it = g_arch_ok.find(dev);
+  if (it == g_arch_ok.end()) {
+    hipDeviceProp_t prop;
+    bool ok = false;
+    if (hipGetDeviceProperties(&prop, dev) == hipSuccess)
+      ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    it = g_arch_ok.emplace(dev, ok).first;
+  }
+  *dev_out = dev;
+  return it->second ? WQBMM_OK : WQBMM_ERR_UNSUPPORTED;
+}
+
+// ---- per-(device, stream) workspace: [counters | scratch], grown on demand
+struct Workspace {
+  void* base = nullptr;
+  size_t bytes = 0;
+};
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Returns the scratch region (after the counter prefix) of at least `scratch`
+// bytes, and the counter prefix.  Growth synchronizes `stream` so that no
+// launch still using the old buffer is pending, then zeroes the counters.
+wqbmm_status get_workspace(int dev, hipStream_t stream, size_t scratch, uint32_t** counters,
+                           uint8_t** scratch_ptr) {
+  const size_t prefix = round_up(kCounterBytes, 256);
+  const size_t need = prefix + round_up(scratch, 256);
+  std::lock_guard<std::mutex> lk(g_mu);
+  Workspace& ws = g_ws[std::make_pair(dev, stream)];
+  if (ws.bytes < need) {
+    if (ws.base) {
+      if (hipStreamSynchronize(stream) != hipSuccess) return WQBMM_ERR_LAUNCH;
+      (void)hipFree(ws.base);
+      ws.base = nullptr;
+      ws.bytes = 0;
+    }
+    const size_t grow = need + need / 4;
+    void* p = nullptr;
+    if (hipMalloc(&p, grow) != hipSuccess) return WQBMM_ERR_ALLOC;
+    if (hipMemsetAsync(p, 0, prefix, stream) != hipSuccess) {
+      (void)hipFree(p);
+      return WQBMM_ERR_LAUNCH;
+    }
+    ws.base = p;
+    ws.bytes = grow;
+  }
+  *counters = static_cast<uint32_t*>(ws.base);
+  *scratch_ptr = static_cast<uint8_t*>(ws.base) + prefix;
+  return WQBMM_OK;
+}
+
+int resolve_path(int path, int64_t M, int64_t K, int64_t N, int64_t gs) {
+  if (path == WQBMM_PATH_AUTO) return wqbmm_select_path(M, K, N, gs);
+  return path;
+}
+
+wqbmm_status launch_status(hipError_t e) { return e == hipSuccess ? WQBMM_OK : WQBMM_ERR_LAUNCH; }
+
+// Steps 1-11 (or 1-9 with y_int) on one of the two kernel paths.
+wqbmm_status run(const void* x, const void* w, const void* scale, int64_t gs, int64_t M,
+                 int64_t K, int64_t N, int64_t g_begin, int64_t g_end, void* y, int32_t* y_int,
+                 int path, hipStream_t stream) {
+  int dev = -1;
+  wqbmm_status st = check_device(&dev);
+  if (st != WQBMM_OK) return st;
+  if (path == WQBMM_PATH_DECODE) {
+    const DecodePlan plan = wqbmm::decode_plan((int)gs, M, K, N, g_begin, g_end);
+    uint32_t* counters = nullptr;
+    uint8_t* scratch = nullptr;
+    const size_t pbytes = y_int ? 0 : wqbmm::decode_partials_bytes(plan, M, N);
+    st = get_workspace(dev, stream, pbytes, &counters, &scratch);
+    if (st != WQBMM_OK) return st;
+    return launch_status(wqbmm::launch_decode(x, w, scale, (int)gs, M, K, N, g_begin, g_end, y,
+                                              y_int, reinterpret_cast<float*>(scratch), counters,
+                                              plan, stream));
+  }
+  // prefill: pre-pass into the workspace, then the MFMA GEMM
+  const int64_t G = K / gs;
+  const size_t aint_bytes = round_up((size_t)(3 * M * K), 256);
+  const size_t amax_bytes = round_up((size_t)(M * G) * sizeof(float), 256);
+  uint32_t* counters = nullptr;
+  uint8_t* scratch = nullptr;
+  st = get_workspace(dev, stream, aint_bytes + amax_bytes, &counters, &scratch);
+  if (st != WQBMM_OK) return st;
+  int8_t* a_int = reinterpret_cast<int8_t*>(scratch);
+  float* a_max = reinterpret_cast<float*>(scratch + aint_bytes);
+  st = launch_status(wqbmm::launch_prepass(x, (int)gs, M, K, a_int, a_max, stream));
+  if (st != WQBMM_OK) return st;
+  return launch_status(wqbmm::launch_prefill_gemm(a_int, a_max, w, scale, (int)gs, M, K, N,
+                                                  g_begin, g_end, y, y_int, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int wqbmm_select_path(int64_t M, int64_t K, int64_t N, int64_t group_size) {
+  (void)K; (void)N; (void)group_size;
+  return M <= kDecodeMaxM ? WQBMM_PATH_DECODE : WQBMM_PATH_PREFILL;
+}
+
+const char* wqbmm_status_string(int status) {
+  switch (status) {
+    case WQBMM_OK: return "WQBMM_OK";
+    case WQBMM_ERR_NULLPTR: return "WQBMM_ERR_NULLPTR: a required pointer is NULL";
+    case WQBMM_ERR_INVALID: return "WQBMM_ERR_INVALID: shape, range or alignment rule violated";
+    case WQBMM_ERR_UNSUPPORTED: return "WQBMM_ERR_UNSUPPORTED: group_size not 64/128 or device not gfx950";
+    case WQBMM_ERR_LAUNCH: return "WQBMM_ERR_LAUNCH: a HIP call or kernel launch failed";
+    case WQBMM_ERR_ALLOC: return "WQBMM_ERR_ALLOC: workspace allocation failed";
+    default: return "WQBMM_ERR_UNKNOWN: not a wqbmm_status value";
+  }
+}
+
+int wqbmm_version(void) { return 1 * 10000 + 0 * 100 + 0; }
+
+wqbmm_status wqbmm_a16w4_msd_path(const void* x, const void* w_packed_int4,
+                                  const void* antiquant_scale, int64_t group_size, int64_t M,
+                                  int64_t K, int64_t N, void* y, int path, void* stream) {
+  // x and y have no elements when M == 0 and may then be NULL
+  if ((!x && M != 0) || !w_packed_int4 || !antiquant_scale || (!y && M != 0))
+    return WQBMM_ERR_NULLPTR;
+  wqbmm_status st = check_shape(group_size, M, K, N);
+  if (st != WQBMM_OK) return st;
+  if (!aligned16(x) || !aligned16(w_packed_int4) || !aligned16(antiquant_scale) || !aligned16(y))
+    return WQBMM_ERR_INVALID;
+  if (path < WQBMM_PATH_AUTO || path > WQBMM_PATH_PREFILL) return WQBMM_ERR_INVALID;
+  const int p = resolve_path(path, M, K, N, group_size);
+  if (p == WQBMM_PATH_DECODE && M > kDecodeMaxM) return WQBMM_ERR_INVALID;
+  st = check_support(group_size);
+  if (st != WQBMM_OK) return st;
+  if (M == 0) return WQBMM_OK;
+  return run(x, w_packed_int4, antiquant_scale, group_size, M, K, N, 0, K / group_size, y,
+             nullptr, p, static_cast<hipStream_t>(stream));
+}
+
+wqbmm_status wqbmm_a16w4_msd(const void* x, const void* w_packed_int4,
+                             const void* antiquant_scale, int64_t group_size, int64_t M,
+                             int64_t K, int64_t N, void* y, void* stream) {
+  return wqbmm_a16w4_msd_path(x, w_packed_int4, antiquant_scale, group_size, M, K, N, y,
+                              WQBMM_PATH_AUTO, stream);
+}
+
+wqbmm_status wqbmm_a16w4_msd_prepass(const void* x, int64_t group_size, int64_t M, int64_t K,
+                                     int8_t* a_int, float* a_max, void* stream) {
+  if (M != 0 && (!x || !a_int || !a_max)) return WQBMM_ERR_NULLPTR;
+  wqbmm_status st = check_shape(group_size, M, K, 32);
+  if (st != WQBMM_OK) return st;
+  if (!aligned16(x) || !aligned16(a_int) || !aligned16(a_max)) return WQBMM_ERR_INVALID;
+  st = check_support(group_size);
+  if (st != WQBMM_OK) return st;
+  if (M == 0) return WQBMM_OK;
+  int dev = -1;
+  st = check_device(&dev);
+  if (st != WQBMM_OK) return st;
+  return launch_status(wqbmm::launch_prepass(x, (int)group_size, M, K, a_int, a_max,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+wqbmm_status wqbmm_a16w4_msd_yint(const void* x, const void* w_packed_int4, int64_t group_size,
+                                  int64_t M, int64_t K, int64_t N, int64_t g_begin,
+                                  int64_t g_end, int32_t* y_int, int path, void* stream) {
+  if ((!x && M != 0) || !w_packed_int4 || (!y_int && M != 0)) return WQBMM_ERR_NULLPTR;
+  wqbmm_status st = check_shape(group_size, M, K, N);
+  if (st != WQBMM_OK) return st;
+  if (!aligned16(x) || !aligned16(w_packed_int4) || !aligned16(y_int)) return WQBMM_ERR_INVALID;
+  if (g_begin < 0 || g_end > K / group_size || g_begin >= g_end) return WQBMM_ERR_INVALID;
+  if (path < WQBMM_PATH_AUTO || path > WQBMM_PATH_PREFILL) return WQBMM_ERR_INVALID;
+  const int p = resolve_path(path, M, K, N, group_size);
+  if (p == WQBMM_PATH_DECODE && M > kDecodeMaxM) return WQBMM_ERR_INVALID;
+  st = check_support(group_size);
+  if (st != WQBMM_OK) return st;
+  if (M == 0) return WQBMM_OK;
+  return run(x, w_packed_int4, nullptr, group_size, M, K, N, g_begin, g_end, nullptr, y_int, p,
+             static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,132 @@
+// msd_device.hpp -- gfx950 device helpers shared by every MSD kernel.
+//
+// Method: the page "WeightQuantBatchMatmulExperiment 算子深度解析：A16W4 PerGroup
+// 伪量化 MatMul 的 MSD 算法与双模板流水设计" (lpnh.cn/news/2294145), called the
+// WQBMM-Exp page below.  §4.1 gives the eleven MSD formulas; §4.3 the int4
+// storage (two per byte); the kernel there keeps the expansion factors as the
+// fp32 literals 7.49f, 14.98f, 14.98f.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wqbmm {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// Expansion factors (WQBMM-Exp page §4.1, fp32 as the page's kernel keeps them).
+constexpr float kF1 = 7.49f;
+constexpr float kF2 = 14.98f;
+
+// Step-10 weights of the three levels, with the 1/16 that undoes the
+// high-nibble int4 unpack (each weight enters the contraction as 16*w).
+constexpr float kC1 = (float)(1.0 / (16.0 * (double)kF1));
+constexpr float kC2 = (float)(1.0 / (16.0 * (double)(kF1 * kF2)));
+constexpr float kC3 = (float)(1.0 / (16.0 * (double)(kF1 * kF2 * kF2)));
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t h16) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, (uint16_t)h16));
+}
+
+__device__ __forceinline__ uint16_t float_to_half_bits(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));  // RNE
+}
+
+// WQBMM-Exp page §4.1 steps 2-7 for one element of a group whose maximum
+// |x| is amax > 0: tmp1 = 7.49*a/A_max, A1 = round(tmp1),
+// tmp2 = (tmp1-A1)*14.98, A2 = round(tmp2), tmp3 = (tmp2-A2)*14.98,
+// A3 = round(tmp3).  Every operation is one IEEE fp32 rounding in this order
+// (no contraction; '/' is the correctly rounded divide), round is
+// half-to-even (v_rndne_f32).  |A_l| <= 7 follows from 7.49 < 7.5 and
+// |residual| <= 0.5.
+__device__ __forceinline__ void msd_expand(float a, float amax, int& A1, int& A2, int& A3) {
+#pragma clang fp contract(off)
+  const float t1 = (kF1 * a) / amax;
+  const float r1 = __builtin_rintf(t1);
+  const float t2 = (t1 - r1) * kF2;
+  const float r2 = __builtin_rintf(t2);
+  const float t3 = (t2 - r2) * kF2;
+  const float r3 = __builtin_rintf(t3);
+  A1 = (int)r1;
+  A2 = (int)r2;
+  A3 = (int)r3;
+}
+
+// Maximum over `width` consecutive lanes (width a power of two <= 64, lane
+// groups aligned to width).  Every lane of the wave must call it.
+template <int WIDTH>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+  for (int off = WIDTH / 2; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, WIDTH));
+  return v;
+}
+
+// Steps 1-8 for 8 consecutive elements of one row (one 16-byte fp16 chunk).
+// The group's GS elements are held by GS/8 consecutive, aligned lanes; every
+// lane of the wave must call this (the max is a cross-lane reduction).
+// Out: the 8 levels of each of A1..A3 packed as int8 bytes in two dwords each,
+// and the group's A_max (step 1: rowMax(|A_group|), exact in fp32).
+template <int GS>
+__device__ __forceinline__ void msd_decompose8(const uint4 xv, uint32_t (&lv)[3][2], float& amax) {
+  const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+  float a[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[2 * i] = half_bits_to_float(xw[i] & 0xffffu);
+    a[2 * i + 1] = half_bits_to_float(xw[i] >> 16);
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(a[i]));
+  amax = group_max<GS / 8>(m);
+#pragma unroll
+  for (int l = 0; l < 3; ++l) lv[l][0] = lv[l][1] = 0u;
+  if (amax > 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      int A1, A2, A3;
+      msd_expand(a[i], amax, A1, A2, A3);
+      const int sh = 8 * (i & 3);
+      lv[0][i >> 2] |= (uint32_t)(A1 & 0xff) << sh;
+      lv[1][i >> 2] |= (uint32_t)(A2 & 0xff) << sh;
+      lv[2][i >> 2] |= (uint32_t)(A3 & 0xff) << sh;
+    }
+  }
+}
+
+// ---- int4 weights -> int8 MFMA operands --------------------------------------
+//
+// A dword read from row k of the [K][N/2] storage holds 8 columns (bytes b=0..3,
+// column 2b in the low nibble, 2b+1 in the high nibble).  The MFMA B operand
+// wants 4 consecutive k of ONE column per dword.  transpose4x4 turns the dwords
+// of rows k..k+3 into e[b] = (byte b of row k, of row k+1, of row k+2, of row
+// k+3): column pair b, four rows.  lo16/hi16 then isolate one nibble per byte
+// in the high half, i.e. the int8 value 16*w (exact; the 1/16 is folded into
+// the step-10 weights kC1..kC3).
+
+__device__ __forceinline__ void transpose4x4(uint32_t d0, uint32_t d1, uint32_t d2, uint32_t d3,
+                                             uint32_t& e0, uint32_t& e1, uint32_t& e2, uint32_t& e3) {
+  // v_perm_b32(s0, s1, sel): selector byte 0-3 picks s1's bytes, 4-7 s0's.
+  const uint32_t t01l = __builtin_amdgcn_perm(d1, d0, 0x05010400u);  // d0.b0 d1.b0 d0.b1 d1.b1
+  const uint32_t t01h = __builtin_amdgcn_perm(d1, d0, 0x07030602u);  // d0.b2 d1.b2 d0.b3 d1.b3
+  const uint32_t t23l = __builtin_amdgcn_perm(d3, d2, 0x05010400u);
+  const uint32_t t23h = __builtin_amdgcn_perm(d3, d2, 0x07030602u);
+  e0 = __builtin_amdgcn_perm(t23l, t01l, 0x05040100u);               // d0.b0 d1.b0 d2.b0 d3.b0
+  e1 = __builtin_amdgcn_perm(t23l, t01l, 0x07060302u);               // d0.b1 d1.b1 d2.b1 d3.b1
+  e2 = __builtin_amdgcn_perm(t23h, t01h, 0x05040100u);
+  e3 = __builtin_amdgcn_perm(t23h, t01h, 0x07060302u);
+}
+
+__device__ __forceinline__ uint32_t lo16(uint32_t e) { return (e << 4) & 0xF0F0F0F0u; }  // even column, 16*w
+__device__ __forceinline__ uint32_t hi16(uint32_t e) { return e & 0xF0F0F0F0u; }         // odd column, 16*w
+
+// v_mfma_i32_16x16x64_i8: D[16][16] += A[16][64] . B[64][16] in int32.
+// Lane l supplies row (l%16) of A and column (l%16) of B, 16 bytes each, for
+// the k-block (l/16); within that block both operands use the same byte->k
+// assignment, so any consistent ordering of the 64 k values is a valid
+// contraction.  D: lane l holds column (l%16), rows 4*(l/16)+i in element i.
+__device__ __forceinline__ v4i mfma_i8(v4i a, v4i b, v4i c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+}  // namespace wqbmm
