@@ -1,0 +1,292 @@
+#!/usr/bin/env python3
+"""Throughput of the A16W4 per-group MSD matmul on one MI355X.
+
+One step = one call of the whole operator (MSD pre-pass, int8 MFMA
+contraction, fp32 combine/accumulate, fp16 store) on one synthetic batch that
+is already resident in HBM.  Steps cycle through enough distinct buffer sets
+(x, w, scale, y) that their footprint exceeds 512 MiB, twice the 256 MiB
+MALL, so every step streams its weights from HBM.  The K timed steps are
+captured once into a HIP graph and replayed, so the GPU runs them back to
+back without Python launch overhead in between; the kernels are the same as
+in an eager call.
+
+Prints ONE JSON line:  metric / value (effective TOPS = 2*M*N*K per step per
+second) / ms_per_step / roofline of the dominant kernel (HIP events on the
+launch stream) / cpu_baseline (the CPU oracle on the host cores).
+
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "A16W4 MSD matmul effective TOPS + weight GB/s (% roofline) at M=1..2048"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+I8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, published (5.0 POP/s)
+MALL_COLD_BYTES = 512 << 20
+
+
+def kernel_sources_sha() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "weight_only_quantized_msd_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(f.encode())
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic(M, K, N, gs):
+    G = K // gs
+    w_bytes = K * N // 2
+    bytes_total = w_bytes + 2 * G * N + 2 * M * K + 2 * M * N   # W + scale + x + y, once each
+    return dict(w_bytes=w_bytes, bytes=bytes_total, eff_ops=2 * M * N * K, exec_i8_ops=6 * M * N * K)
+
+
+def make_sets(torch, M, K, N, gs, nsets, seed, dist):
+    """Seeded synthetic buffer sets with the workload's distributions, drawn on
+    the GPU: x ~ N(0,1) (or U[-3,3]) fp16, int4 weights uniform over their
+    range packed two per byte, per-group scales uniform / lognormal fp16."""
+    gen = torch.Generator(device="cuda")
+    sets = []
+    G = K // gs
+    for i in range(nsets):
+        gen.manual_seed(seed * 1000003 + i)
+        if dist["x"] == "normal":
+            x = torch.randn((M, K), generator=gen, device="cuda", dtype=torch.float32)
+        else:
+            x = (torch.rand((M, K), generator=gen, device="cuda") * 6.0 - 3.0)
+        if dist.get("outlier_frac", 0) > 0:
+            idx = torch.randperm(K, generator=gen, device="cuda")[: int(round(dist["outlier_frac"] * K))]
+            x[:, idx] *= dist["outlier_mult"]
+        x = x.to(torch.float16)
+        lo, hi = dist["w"]
+        wv = torch.randint(lo, hi + 1, (K, N), generator=gen, device="cuda", dtype=torch.int16)
+        wu = wv & 0xF
+        w = (wu[:, 0::2] | (wu[:, 1::2] << 4)).to(torch.uint8).contiguous()
+        kind, p0, p1 = dist["scale"]
+        if kind == "uniform":
+            s = torch.rand((G, N), generator=gen, device="cuda") * (p1 - p0) + p0
+        else:
+            s = torch.exp(torch.randn((G, N), generator=gen, device="cuda") * p1 + p0)
+        s = s.to(torch.float16)
+        y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        sets.append(dict(x=x, w=w, s=s, y=y))
+        del wv, wu
+    return sets
+
+
+def timed_graph(torch, stream, fn_list, steps, warmup):
+    """Eager warmup, capture `steps` calls (cycling fn_list) into one graph,
+    replay once untimed, then time one replay: wall clock between
+    synchronizations, and HIP events on the launch stream."""
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            fn_list[i % len(fn_list)]()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream, capture_error_mode="relaxed"):
+        for i in range(steps):
+            fn_list[i % len(fn_list)]()
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return (t1 - t0) * 1e3 / steps, e0.elapsed_time(e1) / steps
+
+
+def cpu_baseline(name, M, K, N, gs, seconds):
+    import numpy as np
+    import oracle
+    from weight_only_quantized_msd_amd import datagen
+    d = datagen.make_inputs(name)
+    # bounded sample: all rows for small M, else a prefix of rows
+    rows = np.arange(M) if M <= 16 else np.arange(min(M, 8))
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        oracle.matmul(d["x"], d["w_packed"], d["scale"], gs, rows=rows)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 10000:
+            break
+    ops = 2.0 * len(rows) * N * K * reps
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": ops / el / 1e12, "unit": "TOPS", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{name}: rows {len(rows)} of {M}, all of K={K}, N={N}; {reps} oracle call(s) in {el:.1f} s",
+            "host_cpu": cpu, "seconds": round(el, 2)}
+
+
+def read_traffic(workload, sha):
+    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(p):
+        return None, None
+    t = json.load(open(p))
+    if t.get("kernel_sources_sha") != sha:
+        return None, "stale: kernel sources changed since the counters were taken"
+    return t.get("hbm_bytes_per_launch"), t
+
+
+def main():
+    from weight_only_quantized_msd_amd import datagen
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode_m16", choices=sorted(datagen.WORKLOADS))
+    ap.add_argument("--path", type=int, default=0, help="0 auto, 1 decode, 2 prefill")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}). Run with --gpus 1.",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+    import weight_only_quantized_msd_amd as W
+
+    wl = datagen.WORKLOADS[args.workload]
+    M, K, N, gs = wl.M, wl.K, wl.N, wl.group_size
+    alg = algorithmic(M, K, N, gs)
+    path = args.path or W.wqbmm_select_path(M, K, N, gs)
+    dist = {"x": wl.x_dist, "w": (wl.w_low, wl.w_high), "scale": wl.scale_dist,
+            "outlier_frac": wl.outlier_frac, "outlier_mult": wl.outlier_mult}
+    set_bytes = alg["bytes"] + (3 * M * K + 4 * M * (K // gs) if path == 2 else 0)
+    nsets = max(2, min(256, math.ceil(MALL_COLD_BYTES / set_bytes)))
+    torch.cuda.init()
+    sets = make_sets(torch, M, K, N, gs, nsets, wl.seed, dist)
+    stream = torch.cuda.Stream()
+    lib = W.lib()
+    sptr = int(stream.cuda_stream)
+
+    if args.calib_copy_mib:
+        src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    def call(st):
+        def f():
+            rc = lib.wqbmm_a16w4_msd_path(st["x"].data_ptr(), st["w"].data_ptr(), st["s"].data_ptr(),
+                                          gs, M, K, N, st["y"].data_ptr(), path, sptr)
+            if rc:
+                raise W.WqbmmError(rc, "wqbmm_a16w4_msd_path")
+        return f
+
+    ms_step, ev_step = timed_graph(torch, stream, [call(st) for st in sets], args.steps, args.warmup)
+    t_s = ms_step * 1e-3
+    value = alg["eff_ops"] / t_s / 1e12
+
+    extra = {}
+    sha = kernel_sources_sha()
+    traffic, tinfo = read_traffic(args.workload, sha)
+    if path == 1:
+        kern_ms = ev_step
+        achieved = alg["bytes"] / (kern_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "msd_decode_kernel", "avg_kernel_us": round(kern_ms * 1e3, 3),
+                "algorithmic_bytes_per_launch": alg["bytes"]}
+    else:
+        # the GEMM stage alone (its own captured graph), and the pre-pass alone
+        for st in sets:
+            st["a"], st["m"] = W.wqbmm_a16w4_msd_prepass(st["x"], gs)
+        torch.cuda.synchronize()
+
+        def gemm(st):
+            def f():
+                rc = lib.wqbmm_a16w4_msd_gemm(st["a"].data_ptr(), st["m"].data_ptr(), st["w"].data_ptr(),
+                                              st["s"].data_ptr(), gs, M, K, N, st["y"].data_ptr(), sptr)
+                if rc:
+                    raise W.WqbmmError(rc, "wqbmm_a16w4_msd_gemm")
+            return f
+
+        def prep(st):
+            def f():
+                rc = lib.wqbmm_a16w4_msd_prepass(st["x"].data_ptr(), gs, M, K, st["a"].data_ptr(),
+                                                 st["m"].data_ptr(), sptr)
+                if rc:
+                    raise W.WqbmmError(rc, "wqbmm_a16w4_msd_prepass")
+            return f
+
+        _, gemm_ms = timed_graph(torch, stream, [gemm(st) for st in sets], args.steps, args.warmup)
+        _, prep_ms = timed_graph(torch, stream, [prep(st) for st in sets], args.steps, args.warmup)
+        achieved = alg["exec_i8_ops"] / (gemm_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": I8_PEAK_TOPS, "unit": "TOP/s",
+                "frac": round(achieved / I8_PEAK_TOPS, 4), "traffic": traffic,
+                "kernel": "msd_prefill_kernel", "avg_kernel_us": round(gemm_ms * 1e3, 3),
+                "algorithmic_ops_per_launch": alg["exec_i8_ops"]}
+        prep_bytes = 2 * M * K + 3 * M * K + 4 * M * (K // gs)
+        extra["prepass"] = {"avg_kernel_us": round(prep_ms * 1e3, 3),
+                            "achieved_GBps": round(prep_bytes / (prep_ms * 1e-3) / 1e9, 1)}
+    if tinfo is not None and not isinstance(tinfo, str):
+        extra["traffic_detail"] = {k: tinfo[k] for k in tinfo if k != "kernel_sources_sha"}
+    elif isinstance(tinfo, str):
+        extra["traffic_detail"] = tinfo
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: M={M} K={K} N={N} group_size={gs}",
+                   "M": M, "K": K, "N": N, "group_size": gs,
+                   "path": {1: "decode", 2: "prefill"}[path],
+                   "buffer_sets": nsets, "footprint_MiB": round(nsets * set_bytes / 2 ** 20, 1),
+                   "submission": "captured HIP graph of the K steps"},
+        "weight_GBps": round(alg["w_bytes"] / t_s / 1e9, 1),
+        "weight_GBps_frac_of_hbm": round(alg["w_bytes"] / t_s / 1e9 / HBM_PEAK_GBS, 4),
+        "hbm_algorithmic_GBps": round(alg["bytes"] / t_s / 1e9, 1),
+        "exec_i8_TOPS": round(alg["exec_i8_ops"] / t_s / 1e12, 2),
+        "event_ms_per_step": round(ev_step, 6),
+        "roofline": roof,
+        "kernel_sources_sha": sha,
+    }
+    out.update(extra)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.workload, M, K, N, gs, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

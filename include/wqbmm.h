@@ -112,6 +112,21 @@ wqbmm_status wqbmm_a16w4_msd_yint(const void* x, const void* w_packed_int4,
                                   int64_t N, int64_t g_begin, int64_t g_end,
                                   int32_t* y_int, int path, void* stream);
 
+/*
+ * Steps 9-11 alone (WQBMM-Exp page §4.1 steps 9-11; the matmul and MergeY
+ * stages of §6.1) from a decomposition made by wqbmm_a16w4_msd_prepass, with
+ * the prefill kernel.  Lets several weight matrices that multiply the same
+ * activation reuse one decomposition.
+ *   a_int  int8 [3][M][K], a_max fp32 [M][K/group_size]  (prepass outputs)
+ *   w_packed_int4, antiquant_scale, y as for wqbmm_a16w4_msd.
+ * Levels outside [-7, 7] in a_int are outside the contract.
+ */
+wqbmm_status wqbmm_a16w4_msd_gemm(const int8_t* a_int, const float* a_max,
+                                  const void* w_packed_int4,
+                                  const void* antiquant_scale, int64_t group_size,
+                                  int64_t M, int64_t K, int64_t N, void* y,
+                                  void* stream);
+
 /* The path wqbmm_a16w4_msd takes for this shape (WQBMM_PATH_DECODE or
  * WQBMM_PATH_PREFILL).  Pure host function. */
 int wqbmm_select_path(int64_t M, int64_t K, int64_t N, int64_t group_size);

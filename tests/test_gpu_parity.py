@@ -281,6 +281,75 @@ def test_side_stream_and_alternating_shapes(torch_dev):
             assert torch.equal(y_side.view(torch.int16), ref.view(torch.int16)), name
 
 
+@pytest.mark.parametrize("name", ["decode_m16", "prefill_m2048", "outlier_m128"])
+def test_prepass_plus_gemm_equals_prefill_path(torch_dev, name):
+    """The two-stage entry points compose to the same bits as the one-call
+    prefill path (same kernels, same order)."""
+    import weight_only_quantized_msd_amd as W
+    torch = torch_dev
+    d = workload(name)
+    gs = d["group_size"]
+    x, w, s = to_dev(torch, d)
+    announce(f"prepass+gemm {name}")
+    a_int, a_max = W.wqbmm_a16w4_msd_prepass(x, gs)
+    y2 = W.wqbmm_a16w4_msd_gemm(a_int, a_max, w, s, gs)
+    y1 = W.wqbmm_a16w4_msd_path(x, w, s, gs, PREFILL)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+@pytest.mark.parametrize("name,path", [("decode_m16", DECODE), ("ffn_up_m16", DECODE),
+                                       ("tiny", PREFILL), ("outlier_m128", PREFILL)])
+def test_graph_replay_matches_eager(torch_dev, name, path):
+    """bench.py submits its timed steps as a captured graph: every replay, with
+    eager work and synchronizations in between, must reproduce the eager bits
+    (the split-K counters re-arm inside the graph; no memset nodes)."""
+    import weight_only_quantized_msd_amd as W
+    torch = torch_dev
+    d = workload(name)
+    gs = d["group_size"]
+    x, w, s = to_dev(torch, d)
+    announce(f"graph {name} path={path}")
+    ref = W.wqbmm_a16w4_msd_path(x, w, s, gs, path)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    y = torch.empty_like(ref)
+    with torch.cuda.stream(side):
+        W.wqbmm_a16w4_msd_path(x, w, s, gs, path, y=y, stream=side)   # warm this stream
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side, capture_error_mode="relaxed"):
+        W.wqbmm_a16w4_msd_path(x, w, s, gs, path, y=y, stream=side)
+    for rep in range(4):
+        y.fill_(7.0)
+        other = W.wqbmm_a16w4_msd_path(x, w, s, gs, path)    # eager work in between
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), ref.view(torch.int16)), rep
+        assert torch.equal(other.view(torch.int16), ref.view(torch.int16)), rep
+
+
+@pytest.mark.parametrize("name", ["decode_m16", "decode_m1", "ffn_up_m16"])
+def test_splitk_back_to_back_stress(torch_dev, name):
+    """Many split-K launches queued back to back (no host sync in between):
+    every output equals the first bit for bit, and the first is within
+    tolerance of the oracle.  Exercises the per-column-block counters that
+    each launch re-arms for the next."""
+    import weight_only_quantized_msd_amd as W
+    torch = torch_dev
+    d = workload(name)
+    gs = d["group_size"]
+    x, w, s = to_dev(torch, d)
+    announce(f"split-K stress {name}")
+    outs = [W.wqbmm_a16w4_msd_path(x, w, s, gs, DECODE) for _ in range(64)]
+    torch.cuda.synchronize()
+    for i, y in enumerate(outs[1:]):
+        assert torch.equal(y.view(torch.int16), outs[0].view(torch.int16)), i
+    y32, _ = oracle.matmul(d["x"], d["w_packed"], d["scale"], gs)
+    check_y(outs[0].cpu().numpy(), y32, name)
+
+
 def test_empty_batch_is_noop(torch_dev):
     import weight_only_quantized_msd_amd as W
     torch = torch_dev

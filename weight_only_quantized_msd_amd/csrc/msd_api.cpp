@@ -29,9 +29,10 @@ constexpr int64_t kMaxM = int64_t(1) << 24;
 constexpr int64_t kMaxK = int64_t(1) << 20;
 constexpr int64_t kMaxN = int64_t(1) << 20;
 constexpr int kDecodeMaxM = 16;
-// Counter words for the decode split-K reduction live in a fixed prefix of the
-// workspace that no other kernel writes: one per 128-column block.
-constexpr size_t kCounterBytes = size_t(kMaxN / 128) * sizeof(uint32_t);
+// Split-K counters of the decode kernel live in a fixed prefix of the
+// workspace that no other kernel writes: one word per 128-column block.
+constexpr int64_t kCounterWords = kMaxN / 128;
+constexpr size_t kCounterBytes = size_t(kCounterWords) * sizeof(uint32_t);
 
 // NULL counts as aligned: it is only accepted where the array is empty (M == 0).
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -67,7 +68,7 @@ wqbmm_status check_device(int* dev_out) {
   return it->second ? WQBMM_OK : WQBMM_ERR_UNSUPPORTED;
 }
 
-// ---- per-(device, stream) workspace: [counters | scratch], grown on demand
+// ---- per-(device, stream) workspace, grown on demand
 struct Workspace {
   void* base = nullptr;
   size_t bytes = 0;
@@ -76,13 +77,14 @@ std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Returns the scratch region (after the counter prefix) of at least `scratch`
-// bytes, and the counter prefix.  Growth synchronizes `stream` so that no
-// launch still using the old buffer is pending, then zeroes the counters.
-wqbmm_status get_workspace(int dev, hipStream_t stream, size_t scratch, uint32_t** counters,
-                           uint8_t** scratch_ptr) {
+// Returns the counter prefix and a scratch region of at least `bytes` for
+// launches on `stream`.  Growth synchronizes `stream` so that no launch still
+// using the old buffer is pending before it is freed; a new buffer gets its
+// counters zeroed by a kernel enqueued on `stream`.
+wqbmm_status get_workspace(int dev, hipStream_t stream, size_t bytes, uint32_t** counters,
+                           uint8_t** scratch) {
   const size_t prefix = round_up(kCounterBytes, 256);
-  const size_t need = prefix + round_up(scratch, 256);
+  const size_t need = prefix + round_up(bytes, 256);
   std::lock_guard<std::mutex> lk(g_mu);
   Workspace& ws = g_ws[std::make_pair(dev, stream)];
   if (ws.bytes < need) {
@@ -95,7 +97,7 @@ wqbmm_status get_workspace(int dev, hipStream_t stream, size_t scratch, uint32_t
     const size_t grow = need + need / 4;
     void* p = nullptr;
     if (hipMalloc(&p, grow) != hipSuccess) return WQBMM_ERR_ALLOC;
-    if (hipMemsetAsync(p, 0, prefix, stream) != hipSuccess) {
+    if (wqbmm::launch_zero_counters(static_cast<uint32_t*>(p), kCounterWords, stream) != hipSuccess) {
       (void)hipFree(p);
       return WQBMM_ERR_LAUNCH;
     }
@@ -103,7 +105,7 @@ wqbmm_status get_workspace(int dev, hipStream_t stream, size_t scratch, uint32_t
     ws.bytes = grow;
   }
   *counters = static_cast<uint32_t*>(ws.base);
-  *scratch_ptr = static_cast<uint8_t*>(ws.base) + prefix;
+  *scratch = static_cast<uint8_t*>(ws.base) + prefix;
   return WQBMM_OK;
 }
 
@@ -126,8 +128,10 @@ wqbmm_status run(const void* x, const void* w, const void* scale, int64_t gs, in
     uint32_t* counters = nullptr;
     uint8_t* scratch = nullptr;
     const size_t pbytes = y_int ? 0 : wqbmm::decode_partials_bytes(plan, M, N);
-    st = get_workspace(dev, stream, pbytes, &counters, &scratch);
-    if (st != WQBMM_OK) return st;
+    if (pbytes) {
+      st = get_workspace(dev, stream, pbytes, &counters, &scratch);
+      if (st != WQBMM_OK) return st;
+    }
     return launch_status(wqbmm::launch_decode(x, w, scale, (int)gs, M, K, N, g_begin, g_end, y,
                                               y_int, reinterpret_cast<float*>(scratch), counters,
                                               plan, stream));
@@ -230,6 +234,28 @@ wqbmm_status wqbmm_a16w4_msd_yint(const void* x, const void* w_packed_int4, int6
   if (M == 0) return WQBMM_OK;
   return run(x, w_packed_int4, nullptr, group_size, M, K, N, g_begin, g_end, nullptr, y_int, p,
              static_cast<hipStream_t>(stream));
+}
+
+wqbmm_status wqbmm_a16w4_msd_gemm(const int8_t* a_int, const float* a_max,
+                                  const void* w_packed_int4, const void* antiquant_scale,
+                                  int64_t group_size, int64_t M, int64_t K, int64_t N, void* y,
+                                  void* stream) {
+  if ((M != 0 && (!a_int || !a_max || !y)) || !w_packed_int4 || !antiquant_scale)
+    return WQBMM_ERR_NULLPTR;
+  wqbmm_status st = check_shape(group_size, M, K, N);
+  if (st != WQBMM_OK) return st;
+  if (!aligned16(a_int) || !aligned16(a_max) || !aligned16(w_packed_int4) ||
+      !aligned16(antiquant_scale) || !aligned16(y))
+    return WQBMM_ERR_INVALID;
+  st = check_support(group_size);
+  if (st != WQBMM_OK) return st;
+  if (M == 0) return WQBMM_OK;
+  int dev = -1;
+  st = check_device(&dev);
+  if (st != WQBMM_OK) return st;
+  return launch_status(wqbmm::launch_prefill_gemm(a_int, a_max, w_packed_int4, antiquant_scale,
+                                                  (int)group_size, M, K, N, 0, K / group_size, y,
+                                                  nullptr, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -10,6 +10,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace wqbmm {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -52,12 +54,20 @@ __device__ __forceinline__ void msd_expand(float a, float amax, int& A1, int& A2
   A3 = (int)r3;
 }
 
-// Maximum over `width` consecutive lanes (width a power of two <= 64, lane
-// groups aligned to width).  Every lane of the wave must call it.
+// Maximum over WIDTH (8 or 16) consecutive, aligned lanes, with DPP lane
+// permutations (no LDS traffic): exchange within quads (xor 1, xor 2), then
+// mirror within each half-row of 8 lanes, then within each row of 16.  max is
+// exact, so the order does not matter.  Every lane of the wave must call it.
 template <int WIDTH>
 __device__ __forceinline__ float group_max(float v) {
-#pragma unroll
-  for (int off = WIDTH / 2; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, WIDTH));
+  static_assert(WIDTH == 8 || WIDTH == 16, "group of 8 or 16 lanes");
+  auto dpp = [](float x, auto ctrl) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), decltype(ctrl)::value, 0xf, 0xf, false));
+  };
+  v = fmaxf(v, dpp(v, std::integral_constant<int, 0xB1>{}));   // quad_perm [1,0,3,2]: lane ^ 1
+  v = fmaxf(v, dpp(v, std::integral_constant<int, 0x4E>{}));   // quad_perm [2,3,0,1]: lane ^ 2
+  v = fmaxf(v, dpp(v, std::integral_constant<int, 0x141>{}));  // row_half_mirror: 8 lanes
+  if constexpr (WIDTH == 16) v = fmaxf(v, dpp(v, std::integral_constant<int, 0x140>{}));  // row_mirror
   return v;
 }
 
