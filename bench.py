@@ -181,7 +181,7 @@ def main():
     path = args.path or W.wqbmm_select_path(M, K, N, gs)
     dist = {"x": wl.x_dist, "w": (wl.w_low, wl.w_high), "scale": wl.scale_dist,
             "outlier_frac": wl.outlier_frac, "outlier_mult": wl.outlier_mult}
-    set_bytes = alg["bytes"] + (3 * M * K + 4 * M * (K // gs) if path == 2 else 0)
+    set_bytes = alg["bytes"]
     nsets = max(2, min(256, math.ceil(MALL_COLD_BYTES / set_bytes)))
     torch.cuda.init()
     sets = make_sets(torch, M, K, N, gs, nsets, wl.seed, dist)
@@ -220,37 +220,29 @@ def main():
                 "kernel": "msd_decode_kernel", "avg_kernel_us": round(kern_ms * 1e3, 3),
                 "algorithmic_bytes_per_launch": alg["bytes"]}
     else:
-        # the GEMM stage alone (its own captured graph), and the pre-pass alone
-        for st in sets:
-            st["a"], st["m"] = W.wqbmm_a16w4_msd_prepass(st["x"], gs)
-        torch.cuda.synchronize()
-
-        def gemm(st):
+        # The two kernels of the prefill path timed alone (each its own graph):
+        # the preparation kernel over the rotating sets (MALL-cold), and the
+        # GEMM kernel on the operands the last preparation left in this
+        # stream's workspace (rotating scale and y).
+        def stage(st, k):
             def f():
-                rc = lib.wqbmm_a16w4_msd_gemm(st["a"].data_ptr(), st["m"].data_ptr(), st["w"].data_ptr(),
-                                              st["s"].data_ptr(), gs, M, K, N, st["y"].data_ptr(), sptr)
+                rc = lib.wqbmm_a16w4_msd_profile_stage(st["x"].data_ptr(), st["w"].data_ptr(),
+                                                       st["s"].data_ptr(), gs, M, K, N,
+                                                       st["y"].data_ptr(), k, sptr)
                 if rc:
-                    raise W.WqbmmError(rc, "wqbmm_a16w4_msd_gemm")
+                    raise W.WqbmmError(rc, "wqbmm_a16w4_msd_profile_stage")
             return f
 
-        def prep(st):
-            def f():
-                rc = lib.wqbmm_a16w4_msd_prepass(st["x"].data_ptr(), gs, M, K, st["a"].data_ptr(),
-                                                 st["m"].data_ptr(), sptr)
-                if rc:
-                    raise W.WqbmmError(rc, "wqbmm_a16w4_msd_prepass")
-            return f
-
-        _, gemm_ms = timed_graph(torch, stream, [gemm(st) for st in sets], args.steps, args.warmup)
-        _, prep_ms = timed_graph(torch, stream, [prep(st) for st in sets], args.steps, args.warmup)
+        _, prep_ms = timed_graph(torch, stream, [stage(st, 1) for st in sets], args.steps, args.warmup)
+        _, gemm_ms = timed_graph(torch, stream, [stage(st, 2) for st in sets], args.steps, args.warmup)
         achieved = alg["exec_i8_ops"] / (gemm_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": I8_PEAK_TOPS, "unit": "TOP/s",
                 "frac": round(achieved / I8_PEAK_TOPS, 4), "traffic": traffic,
-                "kernel": "msd_prefill_kernel", "avg_kernel_us": round(gemm_ms * 1e3, 3),
+                "kernel": "msd_gemm_kernel", "avg_kernel_us": round(gemm_ms * 1e3, 3),
                 "algorithmic_ops_per_launch": alg["exec_i8_ops"]}
-        prep_bytes = 2 * M * K + 3 * M * K + 4 * M * (K // gs)
-        extra["prepass"] = {"avg_kernel_us": round(prep_ms * 1e3, 3),
-                            "achieved_GBps": round(prep_bytes / (prep_ms * 1e-3) / 1e9, 1)}
+        prep_bytes = 2 * M * K + K * N // 2 + 3 * M * K + K * N + 4 * M * (K // gs)
+        extra["prep"] = {"kernel": "msd_prep_kernel", "avg_kernel_us": round(prep_ms * 1e3, 3),
+                         "achieved_GBps": round(prep_bytes / (prep_ms * 1e-3) / 1e9, 1)}
     if tinfo is not None and not isinstance(tinfo, str):
         extra["traffic_detail"] = {k: tinfo[k] for k in tinfo if k != "kernel_sources_sha"}
     elif isinstance(tinfo, str):

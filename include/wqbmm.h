@@ -64,7 +64,7 @@ typedef enum wqbmm_status {
 typedef enum wqbmm_path {
   WQBMM_PATH_AUTO = 0,     /* what wqbmm_a16w4_msd picks (wqbmm_select_path)      */
   WQBMM_PATH_DECODE = 1,   /* fused split-K decode kernel; valid for M <= 16     */
-  WQBMM_PATH_PREFILL = 2   /* MSD pre-pass + int8 MFMA GEMM; any M               */
+  WQBMM_PATH_PREFILL = 2   /* operand preparation + MFMA GEMM; any M            */
 } wqbmm_path;
 
 /*
@@ -113,19 +113,24 @@ wqbmm_status wqbmm_a16w4_msd_yint(const void* x, const void* w_packed_int4,
                                   int32_t* y_int, int path, void* stream);
 
 /*
- * Steps 9-11 alone (WQBMM-Exp page §4.1 steps 9-11; the matmul and MergeY
- * stages of §6.1) from a decomposition made by wqbmm_a16w4_msd_prepass, with
- * the prefill kernel.  Lets several weight matrices that multiply the same
- * activation reuse one decomposition.
- *   a_int  int8 [3][M][K], a_max fp32 [M][K/group_size]  (prepass outputs)
- *   w_packed_int4, antiquant_scale, y as for wqbmm_a16w4_msd.
- * Levels outside [-7, 7] in a_int are outside the contract.
+ * Profiling support: run ONE stage of the prefill path (the path for large
+ * M), so that its kernels can be timed separately.
+ *   stage 1: the preparation kernel only (WQBMM-Exp page §6.1 UnfoldA plus the
+ *            weight conversion): x -> the three levels of §4.1 steps 1-8 and
+ *            A_max, w -> MFMA operand tiles, into this stream's workspace;
+ *            y is not written.
+ *   stage 2: the GEMM kernel only (§4.1 steps 9-11) on the operands that the
+ *            most recent prefill-path call on the SAME stream prepared; y is
+ *            written.  Returns WQBMM_ERR_INVALID if that call had a different
+ *            shape or group size (or none happened).  The operands of x and w
+ *            themselves are not re-read in this stage.
+ * Arguments and rules as for wqbmm_a16w4_msd; other stage values give
+ * WQBMM_ERR_INVALID.
  */
-wqbmm_status wqbmm_a16w4_msd_gemm(const int8_t* a_int, const float* a_max,
-                                  const void* w_packed_int4,
-                                  const void* antiquant_scale, int64_t group_size,
-                                  int64_t M, int64_t K, int64_t N, void* y,
-                                  void* stream);
+wqbmm_status wqbmm_a16w4_msd_profile_stage(const void* x, const void* w_packed_int4,
+                                           const void* antiquant_scale, int64_t group_size,
+                                           int64_t M, int64_t K, int64_t N, void* y,
+                                           int stage, void* stream);
 
 /* The path wqbmm_a16w4_msd takes for this shape (WQBMM_PATH_DECODE or
  * WQBMM_PATH_PREFILL).  Pure host function. */

@@ -119,17 +119,18 @@ def test_yint_validation(over, want):
 
 
 @pytest.mark.parametrize("over,want", [
-    (dict(a=0), L.WQBMM_ERR_NULLPTR),
-    (dict(m=0), L.WQBMM_ERR_NULLPTR),
+    (dict(stage=0), L.WQBMM_ERR_INVALID),
+    (dict(stage=3), L.WQBMM_ERR_INVALID),
+    (dict(x=0), L.WQBMM_ERR_NULLPTR),
     (dict(w=0), L.WQBMM_ERR_NULLPTR),
     (dict(N=40), L.WQBMM_ERR_INVALID),
-    (dict(m=MIS), L.WQBMM_ERR_INVALID),
+    (dict(y=MIS), L.WQBMM_ERR_INVALID),
     (dict(gs=96, K=192), L.WQBMM_ERR_UNSUPPORTED),
-    (dict(M=0, a=0, m=0, y=0), L.WQBMM_OK),
+    (dict(M=0, x=0, y=0), L.WQBMM_OK),
 ])
-def test_gemm_validation(over, want):
-    a = dict(a=FAKE, m=FAKE, w=FAKE, s=FAKE, gs=64, M=2, K=256, N=64, y=FAKE)
+def test_profile_stage_validation(over, want):
+    a = dict(x=FAKE, w=FAKE, s=FAKE, gs=64, M=2, K=256, N=64, y=FAKE, stage=1)
     a.update(over)
-    st = L.wqbmm_a16w4_msd_gemm_raw(a["a"], a["m"], a["w"], a["s"], a["gs"], a["M"], a["K"],
-                                    a["N"], a["y"], None)
+    st = L.wqbmm_a16w4_msd_profile_stage_raw(a["x"], a["w"], a["s"], a["gs"], a["M"], a["K"],
+                                             a["N"], a["y"], a["stage"], None)
     assert st == want

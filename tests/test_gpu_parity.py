@@ -282,20 +282,24 @@ def test_side_stream_and_alternating_shapes(torch_dev):
 
 
 @pytest.mark.parametrize("name", ["decode_m16", "prefill_m2048", "outlier_m128"])
-def test_prepass_plus_gemm_equals_prefill_path(torch_dev, name):
-    """The two-stage entry points compose to the same bits as the one-call
-    prefill path (same kernels, same order)."""
+def test_profile_stages_compose_to_prefill_path(torch_dev, name):
+    """Stage 1 (preparation) then stage 2 (GEMM) give the same bits as the
+    one-call prefill path; stage 2 refuses operands prepared for another shape."""
     import weight_only_quantized_msd_amd as W
     torch = torch_dev
     d = workload(name)
     gs = d["group_size"]
     x, w, s = to_dev(torch, d)
-    announce(f"prepass+gemm {name}")
-    a_int, a_max = W.wqbmm_a16w4_msd_prepass(x, gs)
-    y2 = W.wqbmm_a16w4_msd_gemm(a_int, a_max, w, s, gs)
+    announce(f"profile stages {name}")
     y1 = W.wqbmm_a16w4_msd_path(x, w, s, gs, PREFILL)
+    W.wqbmm_a16w4_msd_profile_stage(x, w, s, gs, 1)
+    y2 = W.wqbmm_a16w4_msd_profile_stage(x, w, s, gs, 2)
+    y3 = W.wqbmm_a16w4_msd_profile_stage(x, w, s, gs, 2)   # operands stay prepared
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(y1.view(torch.int16), y3.view(torch.int16))
+    with pytest.raises(W.WqbmmError):
+        W.wqbmm_a16w4_msd_profile_stage(x[: max(1, d["M"] // 2)].contiguous(), w, s, gs, 2)
 
 
 @pytest.mark.parametrize("name,path", [("decode_m16", DECODE), ("ffn_up_m16", DECODE),

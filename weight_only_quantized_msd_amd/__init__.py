@@ -21,7 +21,7 @@ from ._lib import (WQBMM_ERR_ALLOC, WQBMM_ERR_INVALID, WQBMM_ERR_LAUNCH,  # noqa
 
 __all__ = [
     "wqbmm_a16w4_msd", "wqbmm_a16w4_msd_path", "wqbmm_a16w4_msd_prepass",
-    "wqbmm_a16w4_msd_yint", "wqbmm_a16w4_msd_gemm", "wqbmm_select_path", "wqbmm_status_string", "wqbmm_version",
+    "wqbmm_a16w4_msd_yint", "wqbmm_a16w4_msd_profile_stage", "wqbmm_select_path", "wqbmm_status_string", "wqbmm_version",
     "WqbmmError",
 ]
 
@@ -107,22 +107,20 @@ def wqbmm_a16w4_msd_yint(x, w_packed_int4, group_size: int, g_begin: int, g_end:
     return y_int
 
 
-def wqbmm_a16w4_msd_gemm(a_int, a_max, w_packed_int4, antiquant_scale, group_size: int,
-                         y=None, stream=None):
-    """Steps 9-11 from a decomposition made by wqbmm_a16w4_msd_prepass; returns y."""
+def wqbmm_a16w4_msd_profile_stage(x, w_packed_int4, antiquant_scale, group_size: int,
+                                  stage: int, y=None, stream=None):
+    """Run one stage of the prefill path (1: preparation, 2: GEMM on the
+    operands the last prefill call on this stream prepared); returns y."""
     import torch
-    _require(a_int, torch.int8, 3, "a_int")
-    _require(a_max, torch.float32, 2, "a_max")
+    _require(x, torch.float16, 2, "x")
     _require(w_packed_int4, torch.uint8, 2, "w_packed_int4")
     _require(antiquant_scale, torch.float16, 2, "antiquant_scale")
-    _, M, K = a_int.shape
+    M, K = x.shape
     N = w_packed_int4.shape[1] * 2
     if y is None:
-        y = torch.empty((M, N), dtype=torch.float16, device=a_int.device)
-    else:
-        _require(y, torch.float16, 2, "y")
-    st = lib().wqbmm_a16w4_msd_gemm(a_int.data_ptr(), a_max.data_ptr(), w_packed_int4.data_ptr(),
-                                    antiquant_scale.data_ptr(), int(group_size), M, K, N,
-                                    y.data_ptr(), _stream_ptr(stream))
-    check(st, "wqbmm_a16w4_msd_gemm")
+        y = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    st = lib().wqbmm_a16w4_msd_profile_stage(x.data_ptr(), w_packed_int4.data_ptr(),
+                                             antiquant_scale.data_ptr(), int(group_size), M, K, N,
+                                             y.data_ptr(), int(stage), _stream_ptr(stream))
+    check(st, "wqbmm_a16w4_msd_profile_stage")
     return y

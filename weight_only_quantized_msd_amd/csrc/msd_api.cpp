@@ -72,6 +72,8 @@ wqbmm_status check_device(int* dev_out) {
 struct Workspace {
   void* base = nullptr;
   size_t bytes = 0;
+  // shape whose prefill operands the scratch region currently holds
+  int64_t prep_gs = 0, prep_m = -1, prep_k = 0, prep_n = 0;
 };
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
@@ -103,6 +105,7 @@ wqbmm_status get_workspace(int dev, hipStream_t stream, size_t bytes, uint32_t**
     }
     ws.base = p;
     ws.bytes = grow;
+    ws.prep_m = -1;
   }
   *counters = static_cast<uint32_t*>(ws.base);
   *scratch = static_cast<uint8_t*>(ws.base) + prefix;
@@ -115,6 +118,10 @@ int resolve_path(int path, int64_t M, int64_t K, int64_t N, int64_t gs) {
 }
 
 wqbmm_status launch_status(hipError_t e) { return e == hipSuccess ? WQBMM_OK : WQBMM_ERR_LAUNCH; }
+
+wqbmm_status run_prefill(int dev, const void* x, const void* w, const void* scale, int64_t gs,
+                         int64_t M, int64_t K, int64_t N, int64_t g_begin, int64_t g_end, void* y,
+                         int32_t* y_int, int stage, hipStream_t stream);
 
 // Steps 1-11 (or 1-9 with y_int) on one of the two kernel paths.
 wqbmm_status run(const void* x, const void* w, const void* scale, int64_t gs, int64_t M,
@@ -136,19 +143,43 @@ wqbmm_status run(const void* x, const void* w, const void* scale, int64_t gs, in
                                               y_int, reinterpret_cast<float*>(scratch), counters,
                                               plan, stream));
   }
-  // prefill: pre-pass into the workspace, then the MFMA GEMM
-  const int64_t G = K / gs;
-  const size_t aint_bytes = round_up((size_t)(3 * M * K), 256);
-  const size_t amax_bytes = round_up((size_t)(M * G) * sizeof(float), 256);
+  // prefill: operand preparation into the workspace, then the MFMA GEMM
+  return run_prefill(dev, x, w, scale, gs, M, K, N, g_begin, g_end, y, y_int, 0, stream);
+}
+
+// The prefill path.  stage 0: both kernels; 1: preparation only; 2: GEMM only,
+// on the operands a previous stage 0/1 call left in this stream's workspace
+// for the same shape (checked).
+wqbmm_status run_prefill(int dev, const void* x, const void* w, const void* scale, int64_t gs,
+                         int64_t M, int64_t K, int64_t N, int64_t g_begin, int64_t g_end, void* y,
+                         int32_t* y_int, int stage, hipStream_t stream) {
+  const wqbmm::PrefillLayout L = wqbmm::prefill_layout((int)gs, M, K, N);
+  const size_t a_off = 0;
+  const size_t amax_off = round_up(L.a_bytes, 256);
+  const size_t b_off = amax_off + round_up(L.amax_bytes, 256);
+  const size_t total = b_off + round_up(L.b_bytes, 256);
   uint32_t* counters = nullptr;
   uint8_t* scratch = nullptr;
-  st = get_workspace(dev, stream, aint_bytes + amax_bytes, &counters, &scratch);
+  wqbmm_status st = get_workspace(dev, stream, total, &counters, &scratch);
   if (st != WQBMM_OK) return st;
-  int8_t* a_int = reinterpret_cast<int8_t*>(scratch);
-  float* a_max = reinterpret_cast<float*>(scratch + aint_bytes);
-  st = launch_status(wqbmm::launch_prepass(x, (int)gs, M, K, a_int, a_max, stream));
-  if (st != WQBMM_OK) return st;
-  return launch_status(wqbmm::launch_prefill_gemm(a_int, a_max, w, scale, (int)gs, M, K, N,
+  uint8_t* a_t = scratch + a_off;
+  float* amax_t = reinterpret_cast<float*>(scratch + amax_off);
+  uint8_t* b_t = scratch + b_off;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    Workspace& ws = g_ws[std::make_pair(dev, stream)];
+    if (stage == 2) {
+      if (ws.prep_gs != gs || ws.prep_m != M || ws.prep_k != K || ws.prep_n != N)
+        return WQBMM_ERR_INVALID;
+    } else {
+      ws.prep_gs = gs; ws.prep_m = M; ws.prep_k = K; ws.prep_n = N;
+    }
+  }
+  if (stage != 2) {
+    st = launch_status(wqbmm::launch_prefill_prep(x, w, (int)gs, M, K, N, L, a_t, amax_t, b_t, stream));
+    if (st != WQBMM_OK || stage == 1) return st;
+  }
+  return launch_status(wqbmm::launch_prefill_gemm(a_t, amax_t, b_t, scale, (int)gs, M, K, N, L,
                                                   g_begin, g_end, y, y_int, stream));
 }
 
@@ -236,16 +267,16 @@ wqbmm_status wqbmm_a16w4_msd_yint(const void* x, const void* w_packed_int4, int6
              static_cast<hipStream_t>(stream));
 }
 
-wqbmm_status wqbmm_a16w4_msd_gemm(const int8_t* a_int, const float* a_max,
-                                  const void* w_packed_int4, const void* antiquant_scale,
-                                  int64_t group_size, int64_t M, int64_t K, int64_t N, void* y,
-                                  void* stream) {
-  if ((M != 0 && (!a_int || !a_max || !y)) || !w_packed_int4 || !antiquant_scale)
+wqbmm_status wqbmm_a16w4_msd_profile_stage(const void* x, const void* w_packed_int4,
+                                           const void* antiquant_scale, int64_t group_size,
+                                           int64_t M, int64_t K, int64_t N, void* y, int stage,
+                                           void* stream) {
+  if (stage < 1 || stage > 2) return WQBMM_ERR_INVALID;
+  if ((!x && M != 0) || !w_packed_int4 || !antiquant_scale || (!y && M != 0))
     return WQBMM_ERR_NULLPTR;
   wqbmm_status st = check_shape(group_size, M, K, N);
   if (st != WQBMM_OK) return st;
-  if (!aligned16(a_int) || !aligned16(a_max) || !aligned16(w_packed_int4) ||
-      !aligned16(antiquant_scale) || !aligned16(y))
+  if (!aligned16(x) || !aligned16(w_packed_int4) || !aligned16(antiquant_scale) || !aligned16(y))
     return WQBMM_ERR_INVALID;
   st = check_support(group_size);
   if (st != WQBMM_OK) return st;
@@ -253,9 +284,8 @@ wqbmm_status wqbmm_a16w4_msd_gemm(const int8_t* a_int, const float* a_max,
   int dev = -1;
   st = check_device(&dev);
   if (st != WQBMM_OK) return st;
-  return launch_status(wqbmm::launch_prefill_gemm(a_int, a_max, w_packed_int4, antiquant_scale,
-                                                  (int)group_size, M, K, N, 0, K / group_size, y,
-                                                  nullptr, static_cast<hipStream_t>(stream)));
+  return run_prefill(dev, x, w_packed_int4, antiquant_scale, group_size, M, K, N, 0,
+                     K / group_size, y, nullptr, stage, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -12,13 +12,27 @@ namespace wqbmm {
 hipError_t launch_prepass(const void* x, int gs, int64_t M, int64_t K, int8_t* a_int,
                           float* a_max, hipStream_t stream);
 
-// Steps 9-11 on a pre-computed A_int/A_max with the int8 MFMA GEMM.
-// y_int == nullptr: groups [0, G) are combined into y (fp16 [M][N]).
-// y_int != nullptr: groups [g_begin, g_end) are stored as int32 Y_int.
-hipError_t launch_prefill_gemm(const int8_t* a_int, const float* a_max, const void* w,
+// Prefill path (any M): a preparation kernel writes the MFMA operand tiles
+// (the three levels of x and the weights, as fp8 e4m3, plus A_max), then the
+// GEMM contracts them and applies steps 10-11.
+struct PrefillLayout {
+  int64_t mpad;        // rows padded to a multiple of 16
+  size_t a_bytes;      // level tiles of x: 3 * mpad * K
+  size_t amax_bytes;   // A_max, [group][row] fp32
+  size_t b_bytes;      // weight tiles: K * N
+};
+PrefillLayout prefill_layout(int gs, int64_t M, int64_t K, int64_t N);
+
+hipError_t launch_prefill_prep(const void* x, const void* w, int gs, int64_t M, int64_t K,
+                               int64_t N, const PrefillLayout& L, uint8_t* a_t, float* amax_t,
+                               uint8_t* b_t, hipStream_t stream);
+
+// y_int == nullptr: groups [g_begin, g_end) are combined into y (fp16 [M][N]);
+// otherwise they are stored as int32 Y_int.
+hipError_t launch_prefill_gemm(const uint8_t* a_t, const float* amax_t, const uint8_t* b_t,
                                const void* scale, int gs, int64_t M, int64_t K, int64_t N,
-                               int64_t g_begin, int64_t g_end, void* y, int32_t* y_int,
-                               hipStream_t stream);
+                               const PrefillLayout& L, int64_t g_begin, int64_t g_end, void* y,
+                               int32_t* y_int, hipStream_t stream);
 
 // The fused decode kernel (M <= 16): steps 1-11 in one launch, with a
 // deterministic split-K reduction through `partials` and one self-re-arming

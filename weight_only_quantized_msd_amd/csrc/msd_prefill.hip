@@ -1,25 +1,48 @@
-// msd_prefill.hip -- int8 MFMA GEMM of the MSD method for large M.
+// msd_prefill.hip -- the MSD path for large M: an operand-preparation kernel
+// and an MFMA GEMM with a fused per-group epilogue.
 //
 // WQBMM-Exp page (the page "WeightQuantBatchMatmulExperiment 算子深度解析：A16W4
 // PerGroup 伪量化 MatMul 的 MSD 算法与双模板流水设计", lpnh.cn/news/2294145):
-//   §4.1 step 9   Y_int = [Y1; Y2; Y3] = A_int . Weight_group  (integer GEMM,
-//                 the M axis effectively tripled, cf. §8.1 singleCoreM = 3*M)
-//   §4.1 step 10  Y_group = [(Y1/7.49 + Y2/(7.49*14.98) + Y3/(7.49*14.98^2)) * A_max] * scale_group
-//   §4.1 step 11  Y^i = Y_group + Y^(i-1), over groups in order
-//   §6.1          MergeY reads Y_int, A_max and antiquant_scale and writes y
+//   §4.1 steps 1-8   per (row, group) A_max and the three levels A1..A3
+//   §4.1 step 9      Y_int = [Y1; Y2; Y3] = A_int . Weight_group, in integers
+//                    (the M axis effectively tripled, cf. §8.1 singleCoreM = 3*M)
+//   §4.1 step 10     Y_group = [(Y1/7.49 + Y2/(7.49*14.98) + Y3/(7.49*14.98^2)) * A_max] * scale_group
+//   §4.1 step 11     Y^i = Y_group + Y^(i-1), over groups in order
+//   §6.1             UnfoldA (pre-process), matmul, MergeY (post-process)
+//   §6.2             PRELOAD_MSD: the next round's data movement overlaps the
+//                    current round's matmul and merge
 //
-// The page runs these as separate Cube (matmul) and Vector (merge) stages
-// that exchange Y_int through global memory.  Here one workgroup keeps the
-// three int32 accumulators of a group in registers, so the combine and the
-// fp32 accumulation over groups are fused after each group's MFMAs and only
-// the fp16 result is stored.
+// The integer contraction runs on the fp8 MFMA (v_mfma_scale_f32_16x16x128_
+// f8f6f4, unit scales).  Every level value lies in [-7, 7] and every weight in
+// [-8, 7]; both are exact in fp8 e4m3, their products are exact, and a
+// group's sum (|Y_l| <= 7*8*GS = 7168) is exact in the fp32 accumulator, so
+// the MFMA returns the integer Y_l exactly (the Y_int export converts it to
+// int32).  At the same dense rate as int8 this spares the epilogue three
+// int->float conversions per output per group, which otherwise made the
+// fp32 combine (VALU) slower than the contraction (MFMA).
 //
-// Tiling: workgroup tile BM=128 rows x BN=128 columns, 4 waves in a 2x2 grid,
-// wave tile 64x64 = 4x4 MFMA tiles of 16x16, times 3 levels: one W fragment
-// feeds the 12 MFMAs of its column (4 row tiles x 3 levels).  Per group the
-// workgroup stages in LDS: the 3 x 128 x GS bytes of A_int, and the
-// GS x 64 bytes of int4 W unpacked and transposed to [column][k] int8 so each
-// MFMA operand is one 16-byte LDS read.
+// Operand tiles (written by msd_prep_kernel, read by the GEMM):
+//   An MFMA operand covers 16 rows (A) or 16 columns (B) x 128 k, 32 bytes per
+//   lane.  Lane l holds row/column l%16 and, in byte j of its half h (h = 0, 1),
+//   k = 32*(l/16) + 16*h + j of the group.  For GS = 64 only half 0 is stored
+//   (k = 16*(l/16) + j) and half 1 is zero.  A tile (per 16 rows or columns
+//   and group) is stored as [half][lane][16 bytes], GS*16 bytes, so each half is
+//   one conflict-free 1 KB ds_read_b128 per wave.
+//   A_t: [level][row tile][group][tile]   (rows padded to 16 with zeros)
+//   B_t: [column tile][group][tile]
+//   A_max_t: [group][row]  fp32
+//
+// GEMM tiling: workgroup tile BM=128 rows x BN=128 columns, 8 waves in a 4x2
+// grid, wave tile 32x64 = 2x4 MFMA tiles of 16x16, times 3 levels.  LDS holds
+// one group's A (3 x 8 tiles) and B (8 tiles), double-buffered; the next
+// group's global loads are issued before the current group's MFMAs and
+// copied to the other buffer afterwards, one barrier per group.  Within a
+// group a wave walks its 8 output tiles: the tile's 3 MFMAs are issued, then
+// the fp32 combine of the previous tile, so MFMA and VALU overlap in the wave.
+// Tile order: the linear workgroup id is remapped so that each XCD
+// (workgroups are dealt to the 8 XCDs round-robin) gets a contiguous range of
+// row-major tiles, keeping the A rows its tiles share in that XCD's L2.  The
+// mapping affects speed only.
 #include "msd_device.hpp"
 #include "msd_launch.hpp"
 
@@ -27,36 +50,213 @@ namespace wqbmm {
 namespace pf {
 constexpr int BM = 128;
 constexpr int BN = 128;
-constexpr int THREADS = 256;
-constexpr int WM = 64;
+constexpr int THREADS = 512;
+constexpr int WM = 32;
 constexpr int WN = 64;
-constexpr int MT = WM / 16;
-constexpr int NT = WN / 16;
-constexpr int PAD = 16;
+constexpr int MT = WM / 16;   // 2 row tiles per wave
+constexpr int NT = WN / 16;   // 4 column tiles per wave
+constexpr int NXCD = 8;
 }  // namespace pf
 
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// Step-10 level weights for exact integer Y_l (no unpack scaling here).
+constexpr float kE1 = (float)(1.0 / (double)kF1);
+constexpr float kE2 = (float)(1.0 / (double)(kF1 * kF2));
+constexpr float kE3 = (float)(1.0 / (double)(kF1 * kF2 * kF2));
+
+// Byte offset, inside one operand tile, of the 8- or 16-byte run that starts
+// at row/column r (0..15) and group-relative k (a multiple of 8).
+template <int GS>
+__device__ __forceinline__ int tile_offset(int r, int kk) {
+  if constexpr (GS == 128) {
+    const int kb = kk >> 5, h = (kk >> 4) & 1;
+    return (h * 64 + 16 * kb + r) * 16 + (kk & 15);
+  } else {
+    return (16 * (kk >> 4) + r) * 16 + (kk & 15);
+  }
+}
+
+// Signed bit field of v as a float.  The builtin's result type is unsigned, so
+// it is reinterpreted as int32 before the conversion (v_cvt_f32_i32).
+__device__ __forceinline__ float sfield(int32_t v, int off, int width) {
+  return (float)(int32_t)__builtin_amdgcn_sbfe(v, off, width);
+}
+
+// Four integer-valued floats -> four e4m3 bytes (exact), byte i from f_i.
+__device__ __forceinline__ uint32_t pack4_fp8(float f0, float f1, float f2, float f3) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f0, f1, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(f2, f3, lo, true);
+}
+
+// ---------------------------------------------------------------- prep kernel
+// Blocks [0, xblocks): steps 1-8 for 8 consecutive elements of x per thread
+// (rows up to the padded row count; padding rows decompose zeros).
+// Blocks [xblocks, ...): 16 rows x 8 columns of W per thread, int4 -> e4m3.
+template <int GS>
+__global__ __launch_bounds__(256) void msd_prep_kernel(const uint16_t* __restrict__ x,
+                                                       const uint8_t* __restrict__ w, int M,
+                                                       int Mpad, int K, int N, int xblocks,
+                                                       uint8_t* __restrict__ a_t,
+                                                       float* __restrict__ amax_t,
+                                                       uint8_t* __restrict__ b_t) {
+  constexpr int TILE = GS * 16;
+  const int G = K / GS;
+  if ((int)blockIdx.x < xblocks) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t e0 = t * 8;                         // element index in [Mpad][K]
+    const bool live = e0 < (int64_t)Mpad * K;         // groups are all-live or all-dead
+    const int m = live ? (int)(e0 / K) : 0;
+    const int k = live ? (int)(e0 % K) : 0;
+    const bool real = live && m < M;
+    const uint4 v = *reinterpret_cast<const uint4*>(x + (real ? (int64_t)m * K + k : 0));
+    const uint4 xv = real ? v : make_uint4(0u, 0u, 0u, 0u);
+    uint32_t lv[3][2];
+    float amax;
+    msd_decompose8<GS>(xv, lv, amax);
+    if (!live) return;
+    const int g = k / GS, kk = k % GS;
+    const int mt = m >> 4, r = m & 15;
+    const int64_t MTILES = Mpad / 16;
+#pragma unroll
+    for (int l = 0; l < 3; ++l) {
+      // lv holds the levels as int8 bytes; re-encode them as e4m3
+      uint32_t out[2];
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        const int32_t wv = (int32_t)lv[l][d];
+        const float f0 = sfield(wv, 0, 8);
+        const float f1 = sfield(wv, 8, 8);
+        const float f2 = sfield(wv, 16, 8);
+        const float f3 = sfield(wv, 24, 8);
+        out[d] = pack4_fp8(f0, f1, f2, f3);
+      }
+      uint8_t* dst = a_t + ((l * MTILES + mt) * G + g) * (int64_t)TILE + tile_offset<GS>(r, kk);
+      *reinterpret_cast<uint2*>(dst) = make_uint2(out[0], out[1]);
+    }
+    if ((threadIdx.x & (GS / 8 - 1)) == 0) amax_t[(int64_t)g * Mpad + m] = amax;
+    return;
+  }
+  // W: thread -> (16 rows, 8 columns)
+  const int64_t t = (int64_t)(blockIdx.x - xblocks) * 256 + threadIdx.x;
+  const int64_t per_row = N / 8;
+  if (t >= (int64_t)(K / 16) * per_row) return;
+  const int kq = (int)(t / per_row);                  // 16-row block
+  const int n0 = (int)(t % per_row) * 8;
+  const int k0 = kq * 16;
+  uint32_t d[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    d[r] = *reinterpret_cast<const uint32_t*>(w + (int64_t)(k0 + r) * (N / 2) + n0 / 2);
+  const int g = k0 / GS, kk = k0 % GS;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    uint32_t o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      // column c is nibble c of each row's dword: a 4-bit two's-complement value
+      const float f0 = sfield((int32_t)d[4 * q + 0], 4 * c, 4);
+      const float f1 = sfield((int32_t)d[4 * q + 1], 4 * c, 4);
+      const float f2 = sfield((int32_t)d[4 * q + 2], 4 * c, 4);
+      const float f3 = sfield((int32_t)d[4 * q + 3], 4 * c, 4);
+      o[q] = pack4_fp8(f0, f1, f2, f3);
+    }
+    const int n = n0 + c;
+    uint8_t* dst = b_t + ((int64_t)(n >> 4) * G + g) * TILE + tile_offset<GS>(n & 15, kk);
+    *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+// ---------------------------------------------------------------- GEMM kernel
 template <int GS, bool YINT>
-__global__ __launch_bounds__(256, 1) void msd_prefill_kernel(
-    const int8_t* __restrict__ a_int, const float* __restrict__ a_max,
-    const uint8_t* __restrict__ w, const uint16_t* __restrict__ scale, int M, int K, int N,
-    int g_begin, int g_end, uint16_t* __restrict__ y, int32_t* __restrict__ y_int) {
+__global__ __launch_bounds__(512, 1) void msd_gemm_kernel(
+    const uint8_t* __restrict__ a_t, const float* __restrict__ amax_t,
+    const uint8_t* __restrict__ b_t, const uint16_t* __restrict__ scale, int M, int Mpad, int K,
+    int N, int g_begin, int g_end, int mblocks, int nblocks, uint16_t* __restrict__ y,
+    int32_t* __restrict__ y_int) {
   using namespace pf;
-  constexpr int ROW = GS + PAD;  // LDS bytes per staged row (A: per m, B: per column)
-  __shared__ __attribute__((aligned(16))) int8_t sA[3 * BM * ROW];
-  __shared__ __attribute__((aligned(16))) int8_t sB[BN * ROW];
-  __shared__ float sAmax[BM];
-  __shared__ float sScale[BN];
+  constexpr int TILE = GS * 16;                    // bytes per operand tile and group
+  constexpr int A_BYTES = 3 * (BM / 16) * TILE;    // per group
+  constexpr int B_BYTES = (BN / 16) * TILE;
+  constexpr int A_PER_T = A_BYTES / 16 / THREADS;  // 16-byte chunks per thread: 6 or 3
+  constexpr int B_PER_T = B_BYTES / 16 / THREADS;  // 2 or 1
+  static_assert(A_BYTES % (16 * THREADS) == 0 && B_BYTES % (16 * THREADS) == 0, "staging split");
+
+  __shared__ __attribute__((aligned(16))) uint8_t sA[2][A_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t sB[2][B_BYTES];
+  __shared__ float sAmax[2][BM];
+  __shared__ float sScale[2][BN];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
-  const int n0 = blockIdx.x * BN;
-  const int m0 = blockIdx.y * BM;
-  const int64_t MK = (int64_t)M * K;
+  const int wm = wave >> 1;        // 0..3
+  const int wn = wave & 1;         // 0..1
+
+  const int total = mblocks * nblocks;
+  int t = blockIdx.x;
+  if (total % NXCD == 0) t = (blockIdx.x % NXCD) * (total / NXCD) + blockIdx.x / NXCD;
+  const int m0 = (t / nblocks) * BM;
+  const int n0 = (t % nblocks) * BN;
   const int G = K / GS;
-  const int NB2 = N / 2;  // bytes per W row
+  const int64_t MTILES = Mpad / 16;
+
+  // Staging: chunk c of the A stage is (level, row tile, 16-byte chunk of the
+  // tile); tiles of rows beyond the padded row count, and of columns beyond
+  // N, are read from a clamped valid tile: they only feed outputs never stored.
+  uint4 ra[A_PER_T], rb[B_PER_T];
+  float ram, rsc;
+#define WQBMM_PF_LOAD(g_)                                                                         \
+  do {                                                                                            \
+    _Pragma("unroll") for (int i = 0; i < A_PER_T; ++i) {                                         \
+      const int c = tid + i * THREADS;                                                            \
+      const int tl = c / (TILE / 16), off = c % (TILE / 16);                                      \
+      const int l = tl / (BM / 16), mt = min(m0 / 16 + tl % (BM / 16), (int)MTILES - 1);          \
+      ra[i] = *reinterpret_cast<const uint4*>(a_t + ((l * MTILES + mt) * G + (g_)) * (int64_t)TILE + off * 16); \
+    }                                                                                             \
+    _Pragma("unroll") for (int i = 0; i < B_PER_T; ++i) {                                         \
+      const int c = tid + i * THREADS;                                                            \
+      const int tl = c / (TILE / 16), off = c % (TILE / 16);                                      \
+      const int nt = min(n0 / 16 + tl, N / 16 - 1);                                               \
+      rb[i] = *reinterpret_cast<const uint4*>(b_t + ((int64_t)nt * G + (g_)) * TILE + off * 16);  \
+    }                                                                                             \
+    ram = amax_t[(int64_t)(g_) * Mpad + min(m0 + (tid % BM), Mpad - 1)];                         \
+    rsc = YINT ? 0.0f : half_bits_to_float(scale[(int64_t)(g_) * N + min(n0 + (tid % BN), N - 1)]); \
+  } while (0)
+#define WQBMM_PF_STORE(st_)                                                                       \
+  do {                                                                                            \
+    _Pragma("unroll") for (int i = 0; i < A_PER_T; ++i)                                           \
+        *reinterpret_cast<uint4*>(&sA[st_][(tid + i * THREADS) * 16]) = ra[i];                    \
+    _Pragma("unroll") for (int i = 0; i < B_PER_T; ++i)                                           \
+        *reinterpret_cast<uint4*>(&sB[st_][(tid + i * THREADS) * 16]) = rb[i];                    \
+    if (tid < BM) sAmax[st_][tid] = ram;                                                          \
+    else if (tid < BM + BN) sScale[st_][tid - BM] = rsc;                                          \
+  } while (0)
+
+  // Steps 10-11 for one 16x16 output tile (row tile PM_, column tile PN_)
+  // from its three level accumulators ACC_; or the Y_int export.
+#define WQBMM_PF_EPILOGUE(PM_, PN_, ACC_)                                                         \
+  do {                                                                                            \
+    if constexpr (YINT) {                                                                         \
+      const int64_t gi = g - g_begin;                                                             \
+      const int n = n0 + wn * WN + (PN_) * 16 + (lane & 15);                                      \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                             \
+        const int m = m0 + wm * WM + (PM_) * 16 + (lane >> 4) * 4 + i;                            \
+        if (m < M && n < N) {                                                                     \
+          _Pragma("unroll") for (int l = 0; l < 3; ++l)                                           \
+              y_int[((gi * 3 + l) * M + m) * (int64_t)N + n] = (int32_t)(ACC_)[l][i];             \
+        }                                                                                         \
+      }                                                                                           \
+    } else {                                                                                      \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                             \
+        float tt = (ACC_)[0][i] * q[PM_][i][0];                                                   \
+        tt = __builtin_fmaf((ACC_)[1][i], q[PM_][i][1], tt);                                      \
+        tt = __builtin_fmaf((ACC_)[2][i], q[PM_][i][2], tt);                                      \
+        yacc[PM_][PN_][i] = __builtin_fmaf(tt, sc[PN_], yacc[PM_][PN_][i]);                       \
+      }                                                                                           \
+    }                                                                                             \
+  } while (0)
 
   float yacc[MT][NT][4];
 #pragma unroll
@@ -66,115 +266,73 @@ __global__ __launch_bounds__(256, 1) void msd_prefill_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) yacc[mt][nt][i] = 0.0f;
 
+  WQBMM_PF_LOAD(g_begin);
+  WQBMM_PF_STORE(0);
+  __syncthreads();
+
   for (int g = g_begin; g < g_end; ++g) {
-    const int k0 = g * GS;
-    __syncthreads();  // the previous group's LDS reads are complete
+    const int st = (g - g_begin) & 1;
+    const bool more = g + 1 < g_end;
+    WQBMM_PF_LOAD(more ? g + 1 : g);   // unconditional: the last group re-reads itself, unused
 
-    // ---- stage A_int: 3 levels x BM rows x GS bytes, 16-byte chunks
-    constexpr int CPR = GS / 16;
-    constexpr int A_CHUNKS = 3 * BM * CPR;
-    for (int c = tid; c < A_CHUNKS; c += THREADS) {
-      const int row = c / CPR, ch = c % CPR;
-      const int lvl = row / BM, r = row % BM, m = m0 + r;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (m < M) v = *reinterpret_cast<const uint4*>(a_int + lvl * MK + (int64_t)m * K + k0 + ch * 16);
-      *reinterpret_cast<uint4*>(sA + row * ROW + ch * 16) = v;
-    }
-    if (tid < BM) {
-      const int m = m0 + tid;
-      sAmax[tid] = (m < M) ? a_max[(int64_t)m * G + g] : 0.0f;
-    } else if constexpr (!YINT) {
-      const int c = tid - BM, n = n0 + c;
-      sScale[c] = (n < N) ? half_bits_to_float(scale[(int64_t)g * N + n]) : 0.0f;
-    }
-
-    // ---- stage W: units of 8 rows x 8 columns (one dword per row)
-    constexpr int UNITS = (GS / 8) * (BN / 8);
-    for (int u = tid; u < UNITS; u += THREADS) {
-      const int cc = u % (BN / 8), rb = u / (BN / 8);
-      const int ncol = n0 + cc * 8;
-      uint32_t d[8];
+    float q[MT][4][3], sc[NT];
+    if constexpr (!YINT) {
 #pragma unroll
-      for (int r = 0; r < 8; ++r)
-        d[r] = (ncol < N) ? *reinterpret_cast<const uint32_t*>(
-                                w + (int64_t)(k0 + rb * 8 + r) * NB2 + ncol / 2)
-                          : 0u;
-      uint32_t e0[4], e1[4];
-      transpose4x4(d[0], d[1], d[2], d[3], e0[0], e0[1], e0[2], e0[3]);
-      transpose4x4(d[4], d[5], d[6], d[7], e1[0], e1[1], e1[2], e1[3]);
+      for (int nt = 0; nt < NT; ++nt) sc[nt] = sScale[st][wn * WN + nt * 16 + (lane & 15)];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int col = cc * 8 + 2 * b;
-        *reinterpret_cast<uint2*>(sB + col * ROW + rb * 8) = make_uint2(lo16(e0[b]), lo16(e1[b]));
-        *reinterpret_cast<uint2*>(sB + (col + 1) * ROW + rb * 8) = make_uint2(hi16(e0[b]), hi16(e1[b]));
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float am = sAmax[st][wm * WM + mt * 16 + (lane >> 4) * 4 + i];
+          q[mt][i][0] = am * kE1;
+          q[mt][i][1] = am * kE2;
+          q[mt][i][2] = am * kE3;
+        }
+    }
+    // W operands of the wave's 4 column tiles
+    v8i bf[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const uint8_t* base = &sB[st][(wn * NT + nt) * TILE];
+      const v4i lo = *reinterpret_cast<const v4i*>(base + lane * 16);
+      const v4i hi = GS == 128 ? *reinterpret_cast<const v4i*>(base + 1024 + lane * 16) : v4i{0, 0, 0, 0};
+      bf[nt] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+    v4f acc[2][3];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      v8i af[3];
+#pragma unroll
+      for (int l = 0; l < 3; ++l) {
+        const uint8_t* base = &sA[st][(l * (BM / 16) + wm * MT + mt) * TILE];
+        const v4i lo = *reinterpret_cast<const v4i*>(base + lane * 16);
+        const v4i hi = GS == 128 ? *reinterpret_cast<const v4i*>(base + 1024 + lane * 16) : v4i{0, 0, 0, 0};
+        af[l] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int j = mt * NT + nt, cur = j & 1;
+#pragma unroll
+        for (int l = 0; l < 3; ++l)
+          acc[cur][l] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              af[l], bf[nt], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+        if (j > 0) {
+          const int pm = (j - 1) / NT, pn = (j - 1) % NT;
+          WQBMM_PF_EPILOGUE(pm, pn, acc[cur ^ 1]);
+        }
       }
     }
+    {
+      constexpr int jl = MT * NT - 1;
+      WQBMM_PF_EPILOGUE(jl / NT, jl % NT, acc[jl & 1]);
+    }
+
+    if (more) WQBMM_PF_STORE(st ^ 1);
     __syncthreads();
-
-    // ---- step 9: three integer GEMMs sharing each W fragment
-    v4i acc[3][MT][NT];
-#pragma unroll
-    for (int l = 0; l < 3; ++l)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[l][mt][nt] = v4i{0, 0, 0, 0};
-
-    const int kofs = (lane >> 4) * 16;
-#pragma unroll
-    for (int ks = 0; ks < GS / 64; ++ks) {
-      v4i bf[NT];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        bf[nt] = *reinterpret_cast<const v4i*>(sB + (wn * WN + nt * 16 + (lane & 15)) * ROW + ks * 64 + kofs);
-#pragma unroll
-      for (int l = 0; l < 3; ++l)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const v4i af = *reinterpret_cast<const v4i*>(
-              sA + (l * BM + wm * WM + mt * 16 + (lane & 15)) * ROW + ks * 64 + kofs);
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) acc[l][mt][nt] = mfma_i8(af, bf[nt], acc[l][mt][nt]);
-        }
-    }
-
-    if constexpr (YINT) {
-      // Y_int export: undo the 16*w scaling exactly (arithmetic shift)
-      const int64_t gi = g - g_begin;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int m = m0 + wm * WM + mt * 16 + (lane >> 4) * 4 + i;
-          if (m >= M) continue;
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            const int n = n0 + wn * WN + nt * 16 + (lane & 15);
-            if (n >= N) continue;
-#pragma unroll
-            for (int l = 0; l < 3; ++l)
-              y_int[((gi * 3 + l) * M + m) * (int64_t)N + n] = acc[l][mt][nt][i] >> 4;
-          }
-        }
-    } else {
-      // ---- steps 10-11: combine the levels, scale, accumulate in fp32
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float am = sAmax[wm * WM + mt * 16 + (lane >> 4) * 4 + i];
-          const float q1 = am * kC1, q2 = am * kC2, q3 = am * kC3;
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            const float sc = sScale[wn * WN + nt * 16 + (lane & 15)];
-            float t = (float)acc[0][mt][nt][i] * q1;
-            t = __builtin_fmaf((float)acc[1][mt][nt][i], q2, t);
-            t = __builtin_fmaf((float)acc[2][mt][nt][i], q3, t);
-            yacc[mt][nt][i] = __builtin_fmaf(t, sc, yacc[mt][nt][i]);
-          }
-        }
-    }
   }
+#undef WQBMM_PF_LOAD
+#undef WQBMM_PF_STORE
+#undef WQBMM_PF_EPILOGUE
 
   if constexpr (!YINT) {
 #pragma unroll
@@ -190,29 +348,58 @@ __global__ __launch_bounds__(256, 1) void msd_prefill_kernel(
         }
       }
   }
-  (void)G;
 }
 
-hipError_t launch_prefill_gemm(const int8_t* a_int, const float* a_max, const void* w,
-                               const void* scale, int gs, int64_t M, int64_t K, int64_t N,
-                               int64_t g_begin, int64_t g_end, void* y, int32_t* y_int,
-                               hipStream_t stream) {
-  const dim3 grid((unsigned)((N + pf::BN - 1) / pf::BN), (unsigned)((M + pf::BM - 1) / pf::BM));
+// ---------------------------------------------------------------- launchers
+
+PrefillLayout prefill_layout(int gs, int64_t M, int64_t K, int64_t N) {
+  PrefillLayout L;
+  L.mpad = (M + 15) / 16 * 16;
+  const int64_t G = K / gs;
+  L.a_bytes = (size_t)(3 * L.mpad * K);
+  L.amax_bytes = (size_t)(G * L.mpad) * sizeof(float);
+  L.b_bytes = (size_t)(K * N);
+  return L;
+}
+
+hipError_t launch_prefill_prep(const void* x, const void* w, int gs, int64_t M, int64_t K,
+                               int64_t N, const PrefillLayout& L, uint8_t* a_t, float* amax_t,
+                               uint8_t* b_t, hipStream_t stream) {
+  const int64_t xthreads = L.mpad * K / 8;
+  const int xblocks = (int)((xthreads + 255) / 256);
+  const int64_t wthreads = (K / 16) * (N / 8);
+  const int wblocks = (int)((wthreads + 255) / 256);
+  const uint16_t* xp = static_cast<const uint16_t*>(x);
   const uint8_t* wp = static_cast<const uint8_t*>(w);
+  const int m = (int)M, mp = (int)L.mpad, k = (int)K, n = (int)N;
+  if (gs == 64)
+    hipLaunchKernelGGL(msd_prep_kernel<64>, dim3(xblocks + wblocks), dim3(256), 0, stream, xp, wp, m,
+                       mp, k, n, xblocks, a_t, amax_t, b_t);
+  else
+    hipLaunchKernelGGL(msd_prep_kernel<128>, dim3(xblocks + wblocks), dim3(256), 0, stream, xp, wp, m,
+                       mp, k, n, xblocks, a_t, amax_t, b_t);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_gemm(const uint8_t* a_t, const float* amax_t, const uint8_t* b_t,
+                               const void* scale, int gs, int64_t M, int64_t K, int64_t N,
+                               const PrefillLayout& L, int64_t g_begin, int64_t g_end, void* y,
+                               int32_t* y_int, hipStream_t stream) {
+  const int mblocks = (int)((M + pf::BM - 1) / pf::BM);
+  const int nblocks = (int)((N + pf::BN - 1) / pf::BN);
+  const dim3 grid((unsigned)(mblocks * nblocks));
   const uint16_t* sp = static_cast<const uint16_t*>(scale);
   uint16_t* yp = static_cast<uint16_t*>(y);
-  const int m = (int)M, k = (int)K, n = (int)N, gb = (int)g_begin, ge = (int)g_end;
+  const int m = (int)M, mp = (int)L.mpad, k = (int)K, n = (int)N, gb = (int)g_begin, ge = (int)g_end;
+#define WQBMM_GEMM_LAUNCH(GS_, Y_)                                                                 \
+  hipLaunchKernelGGL((msd_gemm_kernel<GS_, Y_>), grid, dim3(pf::THREADS), 0, stream, a_t, amax_t, \
+                     b_t, sp, m, mp, k, n, gb, ge, mblocks, nblocks, yp, y_int)
   if (y_int) {
-    if (gs == 64)
-      hipLaunchKernelGGL((msd_prefill_kernel<64, true>), grid, dim3(pf::THREADS), 0, stream, a_int, a_max, wp, sp, m, k, n, gb, ge, yp, y_int);
-    else
-      hipLaunchKernelGGL((msd_prefill_kernel<128, true>), grid, dim3(pf::THREADS), 0, stream, a_int, a_max, wp, sp, m, k, n, gb, ge, yp, y_int);
+    if (gs == 64) WQBMM_GEMM_LAUNCH(64, true); else WQBMM_GEMM_LAUNCH(128, true);
   } else {
-    if (gs == 64)
-      hipLaunchKernelGGL((msd_prefill_kernel<64, false>), grid, dim3(pf::THREADS), 0, stream, a_int, a_max, wp, sp, m, k, n, gb, ge, yp, y_int);
-    else
-      hipLaunchKernelGGL((msd_prefill_kernel<128, false>), grid, dim3(pf::THREADS), 0, stream, a_int, a_max, wp, sp, m, k, n, gb, ge, yp, y_int);
+    if (gs == 64) WQBMM_GEMM_LAUNCH(64, false); else WQBMM_GEMM_LAUNCH(128, false);
   }
+#undef WQBMM_GEMM_LAUNCH
   return hipGetLastError();
 }
 
