@@ -1,9 +1,10 @@
 #!/usr/bin/env python3
 """Throughput of the A16W4 per-group MSD matmul on one MI355X.
 
-One step = one call of the whole operator (MSD pre-pass, int8 MFMA
-contraction, fp32 combine/accumulate, fp16 store) on one synthetic batch that
-is already resident in HBM.  Steps cycle through enough distinct buffer sets
+One step = one call of the whole operator (steps 1-11: decomposition of x,
+integer contraction on MFMA, fp32 combine/accumulate, fp16 store) on one
+synthetic batch that is already resident in HBM, with weights already in the
+library's tiled layout (converted once per weight, outside the timed region).  Steps cycle through enough distinct buffer sets
 (x, w, scale, y) that their footprint exceeds 512 MiB, twice the 256 MiB
 MALL, so every step streams its weights from HBM.  The K timed steps are
 captured once into a HIP graph and replayed, so the GPU runs them back to
@@ -51,10 +52,12 @@ def algorithmic(M, K, N, gs):
     return dict(w_bytes=w_bytes, bytes=bytes_total, eff_ops=2 * M * N * K, exec_i8_ops=6 * M * N * K)
 
 
-def make_sets(torch, M, K, N, gs, nsets, seed, dist):
+def make_sets(torch, W, M, K, N, gs, nsets, seed, dist):
     """Seeded synthetic buffer sets with the workload's distributions, drawn on
     the GPU: x ~ N(0,1) (or U[-3,3]) fp16, int4 weights uniform over their
-    range packed two per byte, per-group scales uniform / lognormal fp16."""
+    range packed two per byte and then converted once into the library's
+    tiled layout (outside any timed region, as a deployment converts its
+    static weights at load time), per-group scales uniform / lognormal fp16."""
     gen = torch.Generator(device="cuda")
     sets = []
     G = K // gs
@@ -71,7 +74,9 @@ def make_sets(torch, M, K, N, gs, nsets, seed, dist):
         lo, hi = dist["w"]
         wv = torch.randint(lo, hi + 1, (K, N), generator=gen, device="cuda", dtype=torch.int16)
         wu = wv & 0xF
-        w = (wu[:, 0::2] | (wu[:, 1::2] << 4)).to(torch.uint8).contiguous()
+        w_nd = (wu[:, 0::2] | (wu[:, 1::2] << 4)).to(torch.uint8).contiguous()
+        w = W.wqbmm_a16w4_tile_weights(w_nd)
+        del w_nd
         kind, p0, p1 = dist["scale"]
         if kind == "uniform":
             s = torch.rand((G, N), generator=gen, device="cuda") * (p1 - p0) + p0
@@ -184,7 +189,7 @@ def main():
     set_bytes = alg["bytes"]
     nsets = max(2, min(256, math.ceil(MALL_COLD_BYTES / set_bytes)))
     torch.cuda.init()
-    sets = make_sets(torch, M, K, N, gs, nsets, wl.seed, dist)
+    sets = make_sets(torch, W, M, K, N, gs, nsets, wl.seed, dist)
     stream = torch.cuda.Stream()
     lib = W.lib()
     sptr = int(stream.cuda_stream)

@@ -16,13 +16,27 @@
  *     accumulated over groups.
  *   - §4.3: int4 weights are stored two per byte.
  *
+ * Weights are static, so they are converted ONCE, on the device, from the
+ * page's ND layout into the tiled layout every kernel reads
+ * (wqbmm_a16w4_tiled_weight_bytes + wqbmm_a16w4_tile_weights), the way the
+ * call example (section 调用示例) of the page "CANN ops-math：
+ * aclnnCalculateMatmulWeightSizeV2 接口详解" (zskr.cn/news/2299903) queries the
+ * converted size, converts the ND weight once and then passes the converted
+ * weight to the quantized matmul.  The matmul entry points take w_tiled.
+ *
  * Conventions for every entry point:
  *   - Array pointers are DEVICE pointers (HIP device memory of the current
  *     device) owned by the caller; the library never retains or frees them.
  *     Row-major ("ND") layouts, no padding between rows.
  *   - fp16 arrays hold IEEE binary16 values.
- *   - w_packed_int4 is uint8 [K][N/2]: byte (k, j) holds column 2j in bits 0-3
- *     and column 2j+1 in bits 4-7, each a 4-bit two's-complement value in [-8, 7].
+ *   - w_nd (the ND weight) is uint8 [K][N/2]: byte (k, j) holds column 2j in
+ *     bits 0-3 and column 2j+1 in bits 4-7, each a 4-bit two's-complement value
+ *     in [-8, 7].
+ *   - w_tiled is the output of wqbmm_a16w4_tile_weights for the same K and N,
+ *     wqbmm_a16w4_tiled_weight_bytes(K, N) bytes.  Its layout is internal to the
+ *     library (int4, 16-column x 128-row tiles of 1 KB shaped after the MFMA
+ *     operands; rows are padded to a multiple of 128 with zeros) and is only
+ *     produced and consumed by it.
  *   - stream is a hipStream_t (NULL = the legacy default stream).  All work is
  *     enqueued asynchronously on it; nothing synchronizes the host.  Faults in
  *     device code surface at the caller's next synchronization, as with any
@@ -68,21 +82,39 @@ typedef enum wqbmm_path {
 } wqbmm_path;
 
 /*
+ * Size in bytes of the tiled weights for K x N (K*N/2 when K % 128 == 0), or
+ * -1 if K or N breaks the shape rules (K in [1, 2^20], N in [32, 2^20],
+ * N % 32 == 0).  Pure host function.
+ */
+int64_t wqbmm_a16w4_tiled_weight_bytes(int64_t K, int64_t N);
+
+/*
+ * One-time conversion of the ND int4 weights into the tiled layout.
+ *   w_nd     uint8 [K][N/2]   (format above)
+ *   w_tiled  wqbmm_a16w4_tiled_weight_bytes(K, N) bytes, caller-allocated,
+ *            written completely (padding rows included)
+ * Shape rules as for wqbmm_a16w4_tiled_weight_bytes; both pointers 16-byte
+ * aligned; w_nd and w_tiled must not overlap.
+ */
+wqbmm_status wqbmm_a16w4_tile_weights(const void* w_nd, int64_t K, int64_t N, void* w_tiled,
+                                      void* stream);
+
+/*
  * The operator (WQBMM-Exp page §4.1 steps 1-11, §4.2).
  *   x               fp16  [M][K]
- *   w_packed_int4   uint8 [K][N/2]            (format above)
+ *   w_tiled         int4 weights K x N, tiled (wqbmm_a16w4_tile_weights)
  *   antiquant_scale fp16  [K/group_size][N]   (per group of K, per column)
  *   y               fp16  [M][N]              (write-only, fully overwritten)
  * y[m][n] is the round-to-nearest-even fp16 of the fp32 sum over groups.
  */
-wqbmm_status wqbmm_a16w4_msd(const void* x, const void* w_packed_int4,
+wqbmm_status wqbmm_a16w4_msd(const void* x, const void* w_tiled,
                              const void* antiquant_scale, int64_t group_size,
                              int64_t M, int64_t K, int64_t N, void* y,
                              void* stream);
 
 /* Same operation with an explicit kernel path (WQBMM_PATH_*).  The decode
  * path with M > 16 returns WQBMM_ERR_INVALID. */
-wqbmm_status wqbmm_a16w4_msd_path(const void* x, const void* w_packed_int4,
+wqbmm_status wqbmm_a16w4_msd_path(const void* x, const void* w_tiled,
                                   const void* antiquant_scale, int64_t group_size,
                                   int64_t M, int64_t K, int64_t N, void* y,
                                   int path, void* stream);
@@ -107,7 +139,7 @@ wqbmm_status wqbmm_a16w4_msd_prepass(const void* x, int64_t group_size,
  *          y_int[g-g_begin][l][m][n] = sum over k in group g of A_l[m][k]*w[k][n]
  * Requires 0 <= g_begin < g_end <= K/group_size (else WQBMM_ERR_INVALID).
  */
-wqbmm_status wqbmm_a16w4_msd_yint(const void* x, const void* w_packed_int4,
+wqbmm_status wqbmm_a16w4_msd_yint(const void* x, const void* w_tiled,
                                   int64_t group_size, int64_t M, int64_t K,
                                   int64_t N, int64_t g_begin, int64_t g_end,
                                   int32_t* y_int, int path, void* stream);
@@ -127,7 +159,7 @@ wqbmm_status wqbmm_a16w4_msd_yint(const void* x, const void* w_packed_int4,
  * Arguments and rules as for wqbmm_a16w4_msd; other stage values give
  * WQBMM_ERR_INVALID.
  */
-wqbmm_status wqbmm_a16w4_msd_profile_stage(const void* x, const void* w_packed_int4,
+wqbmm_status wqbmm_a16w4_msd_profile_stage(const void* x, const void* w_tiled,
                                            const void* antiquant_scale, int64_t group_size,
                                            int64_t M, int64_t K, int64_t N, void* y,
                                            int stage, void* stream);

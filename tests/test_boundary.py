@@ -134,3 +134,33 @@ def test_profile_stage_validation(over, want):
     st = L.wqbmm_a16w4_msd_profile_stage_raw(a["x"], a["w"], a["s"], a["gs"], a["M"], a["K"],
                                              a["N"], a["y"], a["stage"], None)
     assert st == want
+
+
+@pytest.mark.parametrize("K,N,want", [
+    (4096, 4096, 4096 * 4096 // 2),            # K % 128 == 0: exactly K*N/2
+    (8192, 28672, 8192 * 28672 // 2),
+    (192, 64, (64 // 16) * 2 * 1024),          # rows padded to 256
+    (64, 32, 2 * 1024),
+    (1, 32, 2 * 1024),
+    (0, 64, -1), (64, 0, -1), (64, 48, -1),    # shape rules
+    ((1 << 20) + 1, 64, -1), (64, (1 << 20) + 32, -1),
+])
+def test_tiled_weight_bytes(K, N, want):
+    assert L.wqbmm_a16w4_tiled_weight_bytes(K, N) == want
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(w=0), L.WQBMM_ERR_NULLPTR),
+    (dict(t=0), L.WQBMM_ERR_NULLPTR),
+    (dict(w=0, K=0), L.WQBMM_ERR_NULLPTR),       # null pointer checked first
+    (dict(K=0), L.WQBMM_ERR_INVALID),
+    (dict(N=48), L.WQBMM_ERR_INVALID),
+    (dict(N=-32), L.WQBMM_ERR_INVALID),
+    (dict(w=MIS), L.WQBMM_ERR_INVALID),
+    (dict(t=MIS), L.WQBMM_ERR_INVALID),
+])
+def test_tile_weights_validation(over, want):
+    a = dict(w=FAKE, K=256, N=64, t=FAKE)
+    a.update(over)
+    st = L.wqbmm_a16w4_tile_weights_raw(a["w"], a["K"], a["N"], a["t"], None)
+    assert st == want

@@ -50,8 +50,27 @@ def workload(name, M=None):
 
 
 def to_dev(torch, d):
-    return (torch.from_numpy(d["x"]).cuda(), torch.from_numpy(d["w_packed"]).cuda(),
-            torch.from_numpy(d["scale"]).cuda())
+    """x, the TILED weights (converted on the device), scale."""
+    import weight_only_quantized_msd_amd as W
+    w_tiled = W.wqbmm_a16w4_tile_weights(torch.from_numpy(d["w_packed"]).cuda())
+    return (torch.from_numpy(d["x"]).cuda(), w_tiled, torch.from_numpy(d["scale"]).cuda())
+
+
+def tiled_reference(w, K, N):
+    """The tiled weight layout as documented with the C ABI, restated with
+    numpy from the unpacked int4 matrix w [K][N]: chunk (nt, kb, lane) holds
+    column 16nt + lane%16 at rows 128kb + 64s + 16(lane/16) + 8d + j (low
+    nibble of byte 4d + j of step s) and that row + 4 (high nibble); rows
+    beyond K are zero."""
+    KB = (K + 127) // 128
+    wp = np.zeros((KB * 128, N), np.int64)
+    wp[:K] = w
+    nt, kb, lane, s, d, j = np.meshgrid(np.arange(N // 16), np.arange(KB), np.arange(64),
+                                        np.arange(2), np.arange(2), np.arange(4), indexing="ij")
+    n = 16 * nt + lane % 16
+    k = 128 * kb + 64 * s + 16 * (lane // 16) + 8 * d + j
+    byte = (wp[k, n] & 0xF) | ((wp[k + 4, n] & 0xF) << 4)
+    return byte.astype(np.uint8).reshape(N // 16, KB * 1024)
 
 
 def check_y(y, y32, what):
@@ -77,6 +96,19 @@ def sample_rows(M, n, seed):
 
 ALL = ["tiny", "decode_m1", "decode_m16", "ffn_up_m16", "prefill_m2048", "outlier_m128",
        "pages_sample_m1"]
+
+
+# ------------------------------------------------------------------ weight tiling
+
+@pytest.mark.parametrize("K,N", [(256, 256), (192, 96), (64, 32), (4096, 4096), (8192, 28672 // 8)])
+def test_tiled_weights_match_documented_layout(torch_dev, K, N):
+    import weight_only_quantized_msd_amd as W
+    torch = torch_dev
+    d = datagen.random_case(1, K, N, 64, seed=K + N)
+    announce(f"tile weights K={K} N={N}")
+    got = W.wqbmm_a16w4_tile_weights(torch.from_numpy(d["w_packed"]).cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), tiled_reference(d["w"].astype(np.int64), K, N))
 
 
 # ------------------------------------------------------------------ steps 1-8
@@ -230,7 +262,7 @@ def test_zero_weights_give_exact_zero(torch_dev):
     torch = torch_dev
     d = datagen.random_case(16, 1024, 256, 128, seed=3)
     x = torch.from_numpy(d["x"]).cuda()
-    w = torch.zeros((1024, 128), dtype=torch.uint8, device="cuda")
+    w = W.wqbmm_a16w4_tile_weights(torch.zeros((1024, 128), dtype=torch.uint8, device="cuda"))
     s = torch.from_numpy(d["scale"]).cuda()
     for p in (DECODE, PREFILL):
         announce(f"zero weights path={p}")
@@ -358,7 +390,7 @@ def test_empty_batch_is_noop(torch_dev):
     import weight_only_quantized_msd_amd as W
     torch = torch_dev
     x = torch.empty((0, 256), dtype=torch.float16, device="cuda")
-    w = torch.zeros((256, 64), dtype=torch.uint8, device="cuda")
+    w = W.wqbmm_a16w4_tile_weights(torch.zeros((256, 64), dtype=torch.uint8, device="cuda"))
     s = torch.ones((4, 128), dtype=torch.float16, device="cuda")
     y = W.wqbmm_a16w4_msd(x, w, s, 64)
     torch.cuda.synchronize()

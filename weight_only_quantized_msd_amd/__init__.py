@@ -1,9 +1,12 @@
 """A16W4 per-group MSD weight-quantized matmul for AMD MI355X (gfx950).
 
-    y = wqbmm_a16w4_msd(x, w_packed_int4, antiquant_scale, group_size)
+    w_tiled = wqbmm_a16w4_tile_weights(w_nd)          # once per weight
+    y = wqbmm_a16w4_msd(x, w_tiled, antiquant_scale, group_size)
 
-x: fp16 [M][K]; w_packed_int4: uint8 [K][N/2] (two int4 per byte, column 2j in
-the low nibble); antiquant_scale: fp16 [K/group_size][N]; y: fp16 [M][N].
+x: fp16 [M][K]; w_nd: uint8 [K][N/2] (two int4 per byte, column 2j in the low
+nibble), converted once on the device into the library's tiled layout
+(uint8 [N/16][ceil(K/128)*1024]); antiquant_scale: fp16 [K/group_size][N];
+y: fp16 [M][N].
 
 The method is the multi-step decomposition (MSD) of the page
 "WeightQuantBatchMatmulExperiment 算子深度解析：A16W4 PerGroup 伪量化 MatMul 的
@@ -20,7 +23,7 @@ from ._lib import (WQBMM_ERR_ALLOC, WQBMM_ERR_INVALID, WQBMM_ERR_LAUNCH,  # noqa
                    status_string, wqbmm_select_path, wqbmm_version)
 
 __all__ = [
-    "wqbmm_a16w4_msd", "wqbmm_a16w4_msd_path", "wqbmm_a16w4_msd_prepass",
+    "wqbmm_a16w4_tile_weights", "wqbmm_a16w4_msd", "wqbmm_a16w4_msd_path", "wqbmm_a16w4_msd_prepass",
     "wqbmm_a16w4_msd_yint", "wqbmm_a16w4_msd_profile_stage", "wqbmm_select_path", "wqbmm_status_string", "wqbmm_version",
     "WqbmmError",
 ]
@@ -48,33 +51,62 @@ def _require(t, dtype, ndim, name):
         raise ValueError(f"{name} must be a contiguous {ndim}-D tensor")
 
 
-def wqbmm_a16w4_msd_path(x, w_packed_int4, antiquant_scale, group_size: int, path: int,
+def _tiled_shape(K: int, N: int):
+    return (N // 16, (K + 127) // 128 * 1024)
+
+
+def wqbmm_a16w4_tile_weights(w_nd, stream=None):
+    """One-time conversion of the ND int4 weights (uint8 [K][N/2]) into the
+    tiled layout the kernels read; returns uint8 [N/16][ceil(K/128)*1024]."""
+    import torch
+    _require(w_nd, torch.uint8, 2, "w_nd")
+    K, N = w_nd.shape[0], w_nd.shape[1] * 2
+    nbytes = lib().wqbmm_a16w4_tiled_weight_bytes(K, N)
+    if nbytes < 0:
+        check(WQBMM_ERR_INVALID, "wqbmm_a16w4_tiled_weight_bytes")
+    w_tiled = torch.empty(_tiled_shape(K, N), dtype=torch.uint8, device=w_nd.device)
+    assert w_tiled.numel() == nbytes
+    st = lib().wqbmm_a16w4_tile_weights(w_nd.data_ptr(), K, N, w_tiled.data_ptr(),
+                                        _stream_ptr(stream))
+    check(st, "wqbmm_a16w4_tile_weights")
+    return w_tiled
+
+
+def _weight_n(w_tiled, K):
+    import torch
+    _require(w_tiled, torch.uint8, 2, "w_tiled")
+    N = w_tiled.shape[0] * 16
+    if tuple(w_tiled.shape) != _tiled_shape(K, N):
+        raise ValueError("w_tiled must be the wqbmm_a16w4_tile_weights output for this K")
+    return N
+
+
+def wqbmm_a16w4_msd_path(x, w_tiled, antiquant_scale, group_size: int, path: int,
                          y=None, stream=None):
     import torch
     _require(x, torch.float16, 2, "x")
-    _require(w_packed_int4, torch.uint8, 2, "w_packed_int4")
     _require(antiquant_scale, torch.float16, 2, "antiquant_scale")
     M, K = x.shape
-    N = w_packed_int4.shape[1] * 2
-    if w_packed_int4.shape[0] != K or antiquant_scale.shape[1] != N or (
+    N = _weight_n(w_tiled, K)
+    if antiquant_scale.shape[1] != N or (
             group_size > 0 and antiquant_scale.shape[0] * group_size != K):
-        raise ValueError("inconsistent shapes: x [M][K], w [K][N/2], scale [K/gs][N]")
+        raise ValueError("inconsistent shapes: x [M][K], tiled w for K x N, scale [K/gs][N]")
     if y is None:
         y = torch.empty((M, N), dtype=torch.float16, device=x.device)
     else:
         _require(y, torch.float16, 2, "y")
         if tuple(y.shape) != (M, N):
             raise ValueError("y must be [M][N]")
-    st = lib().wqbmm_a16w4_msd_path(x.data_ptr(), w_packed_int4.data_ptr(),
+    st = lib().wqbmm_a16w4_msd_path(x.data_ptr(), w_tiled.data_ptr(),
                                     antiquant_scale.data_ptr(), int(group_size), M, K, N,
                                     y.data_ptr(), int(path), _stream_ptr(stream))
     check(st, "wqbmm_a16w4_msd")
     return y
 
 
-def wqbmm_a16w4_msd(x, w_packed_int4, antiquant_scale, group_size: int, y=None, stream=None):
+def wqbmm_a16w4_msd(x, w_tiled, antiquant_scale, group_size: int, y=None, stream=None):
     """The operator; returns y (fp16 [M][N]).  Asynchronous on the current stream."""
-    return wqbmm_a16w4_msd_path(x, w_packed_int4, antiquant_scale, group_size,
+    return wqbmm_a16w4_msd_path(x, w_tiled, antiquant_scale, group_size,
                                 WQBMM_PATH_AUTO, y=y, stream=stream)
 
 
@@ -91,35 +123,33 @@ def wqbmm_a16w4_msd_prepass(x, group_size: int, stream=None):
     return a_int, a_max
 
 
-def wqbmm_a16w4_msd_yint(x, w_packed_int4, group_size: int, g_begin: int, g_end: int,
+def wqbmm_a16w4_msd_yint(x, w_tiled, group_size: int, g_begin: int, g_end: int,
                          path: int = WQBMM_PATH_AUTO, stream=None):
     """Steps 1-9 for groups [g_begin, g_end): int32 [g_end-g_begin][3][M][N]."""
     import torch
     _require(x, torch.float16, 2, "x")
-    _require(w_packed_int4, torch.uint8, 2, "w_packed_int4")
     M, K = x.shape
-    N = w_packed_int4.shape[1] * 2
+    N = _weight_n(w_tiled, K)
     y_int = torch.empty((max(g_end - g_begin, 0), 3, M, N), dtype=torch.int32, device=x.device)
-    st = lib().wqbmm_a16w4_msd_yint(x.data_ptr(), w_packed_int4.data_ptr(), int(group_size),
+    st = lib().wqbmm_a16w4_msd_yint(x.data_ptr(), w_tiled.data_ptr(), int(group_size),
                                     M, K, N, int(g_begin), int(g_end), y_int.data_ptr(),
                                     int(path), _stream_ptr(stream))
     check(st, "wqbmm_a16w4_msd_yint")
     return y_int
 
 
-def wqbmm_a16w4_msd_profile_stage(x, w_packed_int4, antiquant_scale, group_size: int,
+def wqbmm_a16w4_msd_profile_stage(x, w_tiled, antiquant_scale, group_size: int,
                                   stage: int, y=None, stream=None):
     """Run one stage of the prefill path (1: preparation, 2: GEMM on the
     operands the last prefill call on this stream prepared); returns y."""
     import torch
     _require(x, torch.float16, 2, "x")
-    _require(w_packed_int4, torch.uint8, 2, "w_packed_int4")
     _require(antiquant_scale, torch.float16, 2, "antiquant_scale")
     M, K = x.shape
-    N = w_packed_int4.shape[1] * 2
+    N = _weight_n(w_tiled, K)
     if y is None:
         y = torch.empty((M, N), dtype=torch.float16, device=x.device)
-    st = lib().wqbmm_a16w4_msd_profile_stage(x.data_ptr(), w_packed_int4.data_ptr(),
+    st = lib().wqbmm_a16w4_msd_profile_stage(x.data_ptr(), w_tiled.data_ptr(),
                                              antiquant_scale.data_ptr(), int(group_size), M, K, N,
                                              y.data_ptr(), int(stage), _stream_ptr(stream))
     check(st, "wqbmm_a16w4_msd_profile_stage")

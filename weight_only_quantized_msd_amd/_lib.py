@@ -31,6 +31,8 @@ _p = ctypes.c_void_p
 
 # name -> (restype, argtypes); mirrors include/wqbmm.h
 SIGNATURES = {
+    "wqbmm_a16w4_tiled_weight_bytes": (_i64, [_i64, _i64]),
+    "wqbmm_a16w4_tile_weights": (_int, [_p, _i64, _i64, _p, _p]),
     "wqbmm_a16w4_msd": (_int, [_p, _p, _p, _i64, _i64, _i64, _i64, _p, _p]),
     "wqbmm_a16w4_msd_path": (_int, [_p, _p, _p, _i64, _i64, _i64, _i64, _p, _int, _p]),
     "wqbmm_a16w4_msd_prepass": (_int, [_p, _i64, _i64, _i64, _p, _p, _p]),
@@ -83,6 +85,14 @@ def check(status: int, where: str) -> None:
 
 
 # ---- raw C entry points (pointers as ints) ------------------------------------
+
+def wqbmm_a16w4_tiled_weight_bytes(K, N) -> int:
+    return lib().wqbmm_a16w4_tiled_weight_bytes(K, N)
+
+
+def wqbmm_a16w4_tile_weights_raw(w_nd, K, N, w_tiled, stream) -> int:
+    return lib().wqbmm_a16w4_tile_weights(w_nd, K, N, w_tiled, stream)
+
 
 def wqbmm_a16w4_msd_raw(x, w, scale, group_size, M, K, N, y, stream) -> int:
     return lib().wqbmm_a16w4_msd(x, w, scale, group_size, M, K, N, y, stream)

@@ -30,8 +30,9 @@ constexpr int64_t kMaxK = int64_t(1) << 20;
 constexpr int64_t kMaxN = int64_t(1) << 20;
 constexpr int kDecodeMaxM = 16;
 // Split-K counters of the decode kernel live in a fixed prefix of the
-// workspace that no other kernel writes: one word per 128-column block.
-constexpr int64_t kCounterWords = kMaxN / 128;
+// workspace that no other kernel writes: one word per decode column block.
+constexpr int64_t kCounterWords = wqbmm::kDecodeCounterWords;
+static_assert(kCounterWords * wqbmm::kDecodeCols >= kMaxN, "a counter per column block");
 constexpr size_t kCounterBytes = size_t(kCounterWords) * sizeof(uint32_t);
 
 // NULL counts as aligned: it is only accepted where the array is empty (M == 0).
@@ -204,17 +205,33 @@ const char* wqbmm_status_string(int status) {
   }
 }
 
-int wqbmm_version(void) { return 1 * 10000 + 0 * 100 + 0; }
+int wqbmm_version(void) { return 1 * 10000 + 1 * 100 + 0; }
 
-wqbmm_status wqbmm_a16w4_msd_path(const void* x, const void* w_packed_int4,
+int64_t wqbmm_a16w4_tiled_weight_bytes(int64_t K, int64_t N) {
+  if (K <= 0 || N <= 0 || K > kMaxK || N > kMaxN || N % 32 != 0) return -1;
+  return (int64_t)wqbmm::tiled_weight_bytes(K, N);
+}
+
+wqbmm_status wqbmm_a16w4_tile_weights(const void* w_nd, int64_t K, int64_t N, void* w_tiled,
+                                      void* stream) {
+  if (!w_nd || !w_tiled) return WQBMM_ERR_NULLPTR;
+  if (K <= 0 || N <= 0 || K > kMaxK || N > kMaxN || N % 32 != 0) return WQBMM_ERR_INVALID;
+  if (!aligned16(w_nd) || !aligned16(w_tiled)) return WQBMM_ERR_INVALID;
+  int dev = -1;
+  wqbmm_status st = check_device(&dev);
+  if (st != WQBMM_OK) return st;
+  return launch_status(wqbmm::launch_prepack(w_nd, K, N, w_tiled, static_cast<hipStream_t>(stream)));
+}
+
+wqbmm_status wqbmm_a16w4_msd_path(const void* x, const void* w_tiled,
                                   const void* antiquant_scale, int64_t group_size, int64_t M,
                                   int64_t K, int64_t N, void* y, int path, void* stream) {
   // x and y have no elements when M == 0 and may then be NULL
-  if ((!x && M != 0) || !w_packed_int4 || !antiquant_scale || (!y && M != 0))
+  if ((!x && M != 0) || !w_tiled || !antiquant_scale || (!y && M != 0))
     return WQBMM_ERR_NULLPTR;
   wqbmm_status st = check_shape(group_size, M, K, N);
   if (st != WQBMM_OK) return st;
-  if (!aligned16(x) || !aligned16(w_packed_int4) || !aligned16(antiquant_scale) || !aligned16(y))
+  if (!aligned16(x) || !aligned16(w_tiled) || !aligned16(antiquant_scale) || !aligned16(y))
     return WQBMM_ERR_INVALID;
   if (path < WQBMM_PATH_AUTO || path > WQBMM_PATH_PREFILL) return WQBMM_ERR_INVALID;
   const int p = resolve_path(path, M, K, N, group_size);
@@ -222,14 +239,14 @@ wqbmm_status wqbmm_a16w4_msd_path(const void* x, const void* w_packed_int4,
   st = check_support(group_size);
   if (st != WQBMM_OK) return st;
   if (M == 0) return WQBMM_OK;
-  return run(x, w_packed_int4, antiquant_scale, group_size, M, K, N, 0, K / group_size, y,
+  return run(x, w_tiled, antiquant_scale, group_size, M, K, N, 0, K / group_size, y,
              nullptr, p, static_cast<hipStream_t>(stream));
 }
 
-wqbmm_status wqbmm_a16w4_msd(const void* x, const void* w_packed_int4,
+wqbmm_status wqbmm_a16w4_msd(const void* x, const void* w_tiled,
                              const void* antiquant_scale, int64_t group_size, int64_t M,
                              int64_t K, int64_t N, void* y, void* stream) {
-  return wqbmm_a16w4_msd_path(x, w_packed_int4, antiquant_scale, group_size, M, K, N, y,
+  return wqbmm_a16w4_msd_path(x, w_tiled, antiquant_scale, group_size, M, K, N, y,
                               WQBMM_PATH_AUTO, stream);
 }
 
@@ -249,13 +266,13 @@ wqbmm_status wqbmm_a16w4_msd_prepass(const void* x, int64_t group_size, int64_t 
                                              static_cast<hipStream_t>(stream)));
 }
 
-wqbmm_status wqbmm_a16w4_msd_yint(const void* x, const void* w_packed_int4, int64_t group_size,
+wqbmm_status wqbmm_a16w4_msd_yint(const void* x, const void* w_tiled, int64_t group_size,
                                   int64_t M, int64_t K, int64_t N, int64_t g_begin,
                                   int64_t g_end, int32_t* y_int, int path, void* stream) {
-  if ((!x && M != 0) || !w_packed_int4 || (!y_int && M != 0)) return WQBMM_ERR_NULLPTR;
+  if ((!x && M != 0) || !w_tiled || (!y_int && M != 0)) return WQBMM_ERR_NULLPTR;
   wqbmm_status st = check_shape(group_size, M, K, N);
   if (st != WQBMM_OK) return st;
-  if (!aligned16(x) || !aligned16(w_packed_int4) || !aligned16(y_int)) return WQBMM_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(w_tiled) || !aligned16(y_int)) return WQBMM_ERR_INVALID;
   if (g_begin < 0 || g_end > K / group_size || g_begin >= g_end) return WQBMM_ERR_INVALID;
   if (path < WQBMM_PATH_AUTO || path > WQBMM_PATH_PREFILL) return WQBMM_ERR_INVALID;
   const int p = resolve_path(path, M, K, N, group_size);
@@ -263,20 +280,20 @@ wqbmm_status wqbmm_a16w4_msd_yint(const void* x, const void* w_packed_int4, int6
   st = check_support(group_size);
   if (st != WQBMM_OK) return st;
   if (M == 0) return WQBMM_OK;
-  return run(x, w_packed_int4, nullptr, group_size, M, K, N, g_begin, g_end, nullptr, y_int, p,
+  return run(x, w_tiled, nullptr, group_size, M, K, N, g_begin, g_end, nullptr, y_int, p,
              static_cast<hipStream_t>(stream));
 }
 
-wqbmm_status wqbmm_a16w4_msd_profile_stage(const void* x, const void* w_packed_int4,
+wqbmm_status wqbmm_a16w4_msd_profile_stage(const void* x, const void* w_tiled,
                                            const void* antiquant_scale, int64_t group_size,
                                            int64_t M, int64_t K, int64_t N, void* y, int stage,
                                            void* stream) {
   if (stage < 1 || stage > 2) return WQBMM_ERR_INVALID;
-  if ((!x && M != 0) || !w_packed_int4 || !antiquant_scale || (!y && M != 0))
+  if ((!x && M != 0) || !w_tiled || !antiquant_scale || (!y && M != 0))
     return WQBMM_ERR_NULLPTR;
   wqbmm_status st = check_shape(group_size, M, K, N);
   if (st != WQBMM_OK) return st;
-  if (!aligned16(x) || !aligned16(w_packed_int4) || !aligned16(antiquant_scale) || !aligned16(y))
+  if (!aligned16(x) || !aligned16(w_tiled) || !aligned16(antiquant_scale) || !aligned16(y))
     return WQBMM_ERR_INVALID;
   st = check_support(group_size);
   if (st != WQBMM_OK) return st;
@@ -284,7 +301,7 @@ wqbmm_status wqbmm_a16w4_msd_profile_stage(const void* x, const void* w_packed_i
   int dev = -1;
   st = check_device(&dev);
   if (st != WQBMM_OK) return st;
-  return run_prefill(dev, x, w_packed_int4, antiquant_scale, group_size, M, K, N, 0,
+  return run_prefill(dev, x, w_tiled, antiquant_scale, group_size, M, K, N, 0,
                      K / group_size, y, nullptr, stage, static_cast<hipStream_t>(stream));
 }
 

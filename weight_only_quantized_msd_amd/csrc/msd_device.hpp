@@ -40,33 +40,39 @@ __device__ __forceinline__ uint16_t float_to_half_bits(float f) {
 // A3 = round(tmp3).  Every operation is one IEEE fp32 rounding in this order
 // (no contraction; '/' is the correctly rounded divide), round is
 // half-to-even (v_rndne_f32).  |A_l| <= 7 follows from 7.49 < 7.5 and
-// |residual| <= 0.5.
-__device__ __forceinline__ void msd_expand(float a, float amax, int& A1, int& A2, int& A3) {
+// |residual| <= 0.5.  msd_expand_f returns the levels as (integral) floats,
+// msd_expand as ints.
+__device__ __forceinline__ void msd_expand_f(float a, float amax, float& r1, float& r2, float& r3) {
 #pragma clang fp contract(off)
   const float t1 = (kF1 * a) / amax;
-  const float r1 = __builtin_rintf(t1);
+  r1 = __builtin_rintf(t1);
   const float t2 = (t1 - r1) * kF2;
-  const float r2 = __builtin_rintf(t2);
+  r2 = __builtin_rintf(t2);
   const float t3 = (t2 - r2) * kF2;
-  const float r3 = __builtin_rintf(t3);
+  r3 = __builtin_rintf(t3);
+}
+
+__device__ __forceinline__ void msd_expand(float a, float amax, int& A1, int& A2, int& A3) {
+  float r1, r2, r3;
+  msd_expand_f(a, amax, r1, r2, r3);
   A1 = (int)r1;
   A2 = (int)r2;
   A3 = (int)r3;
 }
 
-// Maximum over WIDTH (8 or 16) consecutive, aligned lanes, with DPP lane
+// Maximum over WIDTH (4, 8 or 16) consecutive, aligned lanes, with DPP lane
 // permutations (no LDS traffic): exchange within quads (xor 1, xor 2), then
 // mirror within each half-row of 8 lanes, then within each row of 16.  max is
 // exact, so the order does not matter.  Every lane of the wave must call it.
 template <int WIDTH>
 __device__ __forceinline__ float group_max(float v) {
-  static_assert(WIDTH == 8 || WIDTH == 16, "group of 8 or 16 lanes");
+  static_assert(WIDTH == 4 || WIDTH == 8 || WIDTH == 16, "group of 4, 8 or 16 lanes");
   auto dpp = [](float x, auto ctrl) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), decltype(ctrl)::value, 0xf, 0xf, false));
   };
   v = fmaxf(v, dpp(v, std::integral_constant<int, 0xB1>{}));   // quad_perm [1,0,3,2]: lane ^ 1
   v = fmaxf(v, dpp(v, std::integral_constant<int, 0x4E>{}));   // quad_perm [2,3,0,1]: lane ^ 2
-  v = fmaxf(v, dpp(v, std::integral_constant<int, 0x141>{}));  // row_half_mirror: 8 lanes
+  if constexpr (WIDTH >= 8) v = fmaxf(v, dpp(v, std::integral_constant<int, 0x141>{}));  // row_half_mirror
   if constexpr (WIDTH == 16) v = fmaxf(v, dpp(v, std::integral_constant<int, 0x140>{}));  // row_mirror
   return v;
 }
@@ -104,31 +110,15 @@ __device__ __forceinline__ void msd_decompose8(const uint4 xv, uint32_t (&lv)[3]
   }
 }
 
-// ---- int4 weights -> int8 MFMA operands --------------------------------------
+// ---- tiled int4 weights -> int8 MFMA operands ---------------------------------
 //
-// A dword read from row k of the [K][N/2] storage holds 8 columns (bytes b=0..3,
-// column 2b in the low nibble, 2b+1 in the high nibble).  The MFMA B operand
-// wants 4 consecutive k of ONE column per dword.  transpose4x4 turns the dwords
-// of rows k..k+3 into e[b] = (byte b of row k, of row k+1, of row k+2, of row
-// k+3): column pair b, four rows.  lo16/hi16 then isolate one nibble per byte
-// in the high half, i.e. the int8 value 16*w (exact; the 1/16 is folded into
-// the step-10 weights kC1..kC3).
+// In the tiled weight format, byte j of a dword holds rows j (low nibble) and
+// j+4 (high nibble) of one column.  lo16/hi16 isolate one nibble per byte in
+// the byte's high half, i.e. the int8 value 16*w (exact; the 1/16 is folded
+// into the step-10 weights kC1..kC3): lo16 gives rows 0..3, hi16 rows 4..7.
 
-__device__ __forceinline__ void transpose4x4(uint32_t d0, uint32_t d1, uint32_t d2, uint32_t d3,
-                                             uint32_t& e0, uint32_t& e1, uint32_t& e2, uint32_t& e3) {
-  // v_perm_b32(s0, s1, sel): selector byte 0-3 picks s1's bytes, 4-7 s0's.
-  const uint32_t t01l = __builtin_amdgcn_perm(d1, d0, 0x05010400u);  // d0.b0 d1.b0 d0.b1 d1.b1
-  const uint32_t t01h = __builtin_amdgcn_perm(d1, d0, 0x07030602u);  // d0.b2 d1.b2 d0.b3 d1.b3
-  const uint32_t t23l = __builtin_amdgcn_perm(d3, d2, 0x05010400u);
-  const uint32_t t23h = __builtin_amdgcn_perm(d3, d2, 0x07030602u);
-  e0 = __builtin_amdgcn_perm(t23l, t01l, 0x05040100u);               // d0.b0 d1.b0 d2.b0 d3.b0
-  e1 = __builtin_amdgcn_perm(t23l, t01l, 0x07060302u);               // d0.b1 d1.b1 d2.b1 d3.b1
-  e2 = __builtin_amdgcn_perm(t23h, t01h, 0x05040100u);
-  e3 = __builtin_amdgcn_perm(t23h, t01h, 0x07060302u);
-}
-
-__device__ __forceinline__ uint32_t lo16(uint32_t e) { return (e << 4) & 0xF0F0F0F0u; }  // even column, 16*w
-__device__ __forceinline__ uint32_t hi16(uint32_t e) { return e & 0xF0F0F0F0u; }         // odd column, 16*w
+__device__ __forceinline__ uint32_t lo16(uint32_t e) { return (e << 4) & 0xF0F0F0F0u; }  // rows j, 16*w
+__device__ __forceinline__ uint32_t hi16(uint32_t e) { return e & 0xF0F0F0F0u; }         // rows j+4, 16*w
 
 // v_mfma_i32_16x16x64_i8: D[16][16] += A[16][64] . B[64][16] in int32.
 // Lane l supplies row (l%16) of A and column (l%16) of B, 16 bytes each, for

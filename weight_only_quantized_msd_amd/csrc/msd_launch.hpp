@@ -7,14 +7,30 @@
 
 namespace wqbmm {
 
+// ---- tiled int4 weights (the kernels' weight format) ------------------------
+// Chunk (column tile nt of 16 columns, k-block kb of 128 rows, lane l) is 16
+// bytes at ((nt * KB + kb) * 64 + l) * 16, KB = ceil(K / 128).  It holds column
+// n = 16*nt + l%16 at k = 128*kb + 64*s + 16*(l/16) + i (i = 0..15) for the two
+// 64-row steps s = 0, 1 (bytes 8s .. 8s+7).  In dword d (0, 1) of a step, byte
+// j carries k-offset 8d + j in its low nibble and 8d + 4 + j in its high
+// nibble (4-bit two's complement).  Rows k >= K hold 0.
+constexpr int kTileCols = 16;
+constexpr int kTileRows = 128;
+inline int64_t tiled_kblocks(int64_t K) { return (K + kTileRows - 1) / kTileRows; }
+inline size_t tiled_weight_bytes(int64_t K, int64_t N) {
+  return (size_t)(N / kTileCols) * (size_t)tiled_kblocks(K) * 1024u;
+}
+// Row-major w [K][N/2] (column 2j in the low nibble of byte j) -> tiled.
+hipError_t launch_prepack(const void* w_nd, int64_t K, int64_t N, void* w_tiled, hipStream_t stream);
+
 // Steps 1-8 (WQBMM-Exp page §4.1): x fp16 [M][K] -> a_int int8 [3][M][K],
 // a_max fp32 [M][K/gs].
 hipError_t launch_prepass(const void* x, int gs, int64_t M, int64_t K, int8_t* a_int,
                           float* a_max, hipStream_t stream);
 
 // Prefill path (any M): a preparation kernel writes the MFMA operand tiles
-// (the three levels of x and the weights, as fp8 e4m3, plus A_max), then the
-// GEMM contracts them and applies steps 10-11.
+// (the three levels of x and the tiled weights, as fp8 e4m3, plus A_max), then
+// the GEMM contracts them and applies steps 10-11.
 struct PrefillLayout {
   int64_t mpad;        // rows padded to a multiple of 16
   size_t a_bytes;      // level tiles of x: 3 * mpad * K
@@ -38,11 +54,13 @@ hipError_t launch_prefill_gemm(const uint8_t* a_t, const float* amax_t, const ui
 // deterministic split-K reduction through `partials` and one self-re-arming
 // counter per column block (`counters` must be zero before the first launch).
 struct DecodePlan {
-  int64_t col_blocks;   // blocks of columns per launch
+  int64_t col_blocks;   // blocks of kDecodeCols columns
   int64_t splits;       // K-slices per column block
-  int64_t cols;         // columns per block
-  int wn, wk;           // waves per workgroup along N and along K
+  int64_t kb_begin;     // first 128-row block of the group range
+  int kbw;              // 128-row blocks per wave (1 or 2)
 };
+constexpr int kDecodeCols = 64;   // columns per decode workgroup
+constexpr int64_t kDecodeCounterWords = (int64_t(1) << 20) / kDecodeCols;
 DecodePlan decode_plan(int gs, int64_t M, int64_t K, int64_t N, int64_t g_begin, int64_t g_end);
 size_t decode_partials_bytes(const DecodePlan& p, int64_t M, int64_t N);
 

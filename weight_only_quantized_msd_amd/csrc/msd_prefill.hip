@@ -24,10 +24,13 @@
 // Operand tiles (written by msd_prep_kernel, read by the GEMM):
 //   An MFMA operand covers 16 rows (A) or 16 columns (B) x 128 k, 32 bytes per
 //   lane.  Lane l holds row/column l%16 and, in byte j of its half h (h = 0, 1),
-//   k = 32*(l/16) + 16*h + j of the group.  For GS = 64 only half 0 is stored
-//   (k = 16*(l/16) + j) and half 1 is zero.  A tile (per 16 rows or columns
-//   and group) is stored as [half][lane][16 bytes], GS*16 bytes, so each half is
-//   one conflict-free 1 KB ds_read_b128 per wave.
+//   k = 64*h + 16*(l/16) + j of the group: the half is a 64-row step of the
+//   tiled weight format, so a tiled-weight chunk converts into one lane's two
+//   halves in place.  For GS = 64 only half 0 is stored and half 1 is zero.
+//   The contraction is the same for any byte -> k assignment that A and B
+//   share.  A tile (per 16 rows or columns and group) is stored as
+//   [half][lane][16 bytes], GS*16 bytes, so each half is one conflict-free
+//   1 KB ds_read_b128 per wave.
 //   A_t: [level][row tile][group][tile]   (rows padded to 16 with zeros)
 //   B_t: [column tile][group][tile]
 //   A_max_t: [group][row]  fp32
@@ -66,18 +69,6 @@ constexpr float kE1 = (float)(1.0 / (double)kF1);
 constexpr float kE2 = (float)(1.0 / (double)(kF1 * kF2));
 constexpr float kE3 = (float)(1.0 / (double)(kF1 * kF2 * kF2));
 
-// Byte offset, inside one operand tile, of the 8- or 16-byte run that starts
-// at row/column r (0..15) and group-relative k (a multiple of 8).
-template <int GS>
-__device__ __forceinline__ int tile_offset(int r, int kk) {
-  if constexpr (GS == 128) {
-    const int kb = kk >> 5, h = (kk >> 4) & 1;
-    return (h * 64 + 16 * kb + r) * 16 + (kk & 15);
-  } else {
-    return (16 * (kk >> 4) + r) * 16 + (kk & 15);
-  }
-}
-
 // Signed bit field of v as a float.  The builtin's result type is unsigned, so
 // it is reinterpreted as int32 before the conversion (v_cvt_f32_i32).
 __device__ __forceinline__ float sfield(int32_t v, int off, int width) {
@@ -91,79 +82,102 @@ __device__ __forceinline__ uint32_t pack4_fp8(float f0, float f1, float f2, floa
 }
 
 // ---------------------------------------------------------------- prep kernel
-// Blocks [0, xblocks): steps 1-8 for 8 consecutive elements of x per thread
-// (rows up to the padded row count; padding rows decompose zeros).
-// Blocks [xblocks, ...): 16 rows x 8 columns of W per thread, int4 -> e4m3.
+// Waves [0, xwaves): one (16-row tile, group) each, steps 1-8 for its 16 x GS
+// elements.  Lane l takes row l/4 and the GS/4 consecutive elements at
+// (l%4)*GS/4 of the group, so a group's maximum is a 4-lane reduction and
+// every 16-byte chunk it writes is one operand slot (slot 16*kb + row of half
+// h, for k = 64h + 16kb + j): each store of a wave fills whole 256-byte runs.
+// Waves [xwaves, ...): one 16-byte tiled-weight chunk per thread, whose two
+// 64-row steps become the lane's two 16-byte fp8 operand halves.
 template <int GS>
 __global__ __launch_bounds__(256) void msd_prep_kernel(const uint16_t* __restrict__ x,
-                                                       const uint8_t* __restrict__ w, int M,
-                                                       int Mpad, int K, int N, int xblocks,
+                                                       const uint8_t* __restrict__ wt, int M,
+                                                       int Mpad, int K, int N, int64_t xwaves,
                                                        uint8_t* __restrict__ a_t,
                                                        float* __restrict__ amax_t,
                                                        uint8_t* __restrict__ b_t) {
   constexpr int TILE = GS * 16;
+  constexpr int EPL = GS / 4;                        // elements per lane: 32 or 16
   const int G = K / GS;
-  if ((int)blockIdx.x < xblocks) {
-    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t e0 = t * 8;                         // element index in [Mpad][K]
-    const bool live = e0 < (int64_t)Mpad * K;         // groups are all-live or all-dead
-    const int m = live ? (int)(e0 / K) : 0;
-    const int k = live ? (int)(e0 % K) : 0;
-    const bool real = live && m < M;
-    const uint4 v = *reinterpret_cast<const uint4*>(x + (real ? (int64_t)m * K + k : 0));
-    const uint4 xv = real ? v : make_uint4(0u, 0u, 0u, 0u);
-    uint32_t lv[3][2];
-    float amax;
-    msd_decompose8<GS>(xv, lv, amax);
-    if (!live) return;
-    const int g = k / GS, kk = k % GS;
-    const int mt = m >> 4, r = m & 15;
+  const int lane = threadIdx.x & 63;
+  const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wid < xwaves) {
+    const int mt = (int)(wid / G), g = (int)(wid % G);
+    const int r = lane >> 2, q = lane & 3;
+    const int m = mt * 16 + r;
+    const bool real = m < M;                         // padding rows decompose zeros
+    const uint16_t* src = x + (real ? (int64_t)m * K + (int64_t)g * GS + q * EPL : 0);
+    float a[EPL];
+    float mx = 0.0f;
+#pragma unroll
+    for (int c = 0; c < EPL / 8; ++c) {
+      const uint4 v = *reinterpret_cast<const uint4*>(src + 8 * c);
+      const uint32_t vw[4] = {real ? v.x : 0u, real ? v.y : 0u, real ? v.z : 0u, real ? v.w : 0u};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[8 * c + 2 * i] = half_bits_to_float(vw[i] & 0xffffu);
+        a[8 * c + 2 * i + 1] = half_bits_to_float(vw[i] >> 16);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) mx = fmaxf(mx, fabsf(a[e]));
+    const float amax = group_max<4>(mx);
+    uint32_t out[3][EPL / 4];
+#pragma unroll
+    for (int l = 0; l < 3; ++l)
+#pragma unroll
+      for (int d = 0; d < EPL / 4; ++d) out[l][d] = 0u;
+    if (amax > 0.0f) {
+#pragma unroll
+      for (int d = 0; d < EPL / 4; ++d) {
+        float r3[3][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) msd_expand_f(a[4 * d + i], amax, r3[0][i], r3[1][i], r3[2][i]);
+#pragma unroll
+        for (int l = 0; l < 3; ++l) out[l][d] = pack4_fp8(r3[l][0], r3[l][1], r3[l][2], r3[l][3]);
+      }
+    }
     const int64_t MTILES = Mpad / 16;
 #pragma unroll
-    for (int l = 0; l < 3; ++l) {
-      // lv holds the levels as int8 bytes; re-encode them as e4m3
-      uint32_t out[2];
+    for (int c = 0; c < EPL / 16; ++c) {
+      const int kk = q * EPL + 16 * c;               // group-relative k of this chunk
+      const int slot = (kk >> 6) * 64 + 16 * ((kk >> 4) & 3) + r;
 #pragma unroll
-      for (int d = 0; d < 2; ++d) {
-        const int32_t wv = (int32_t)lv[l][d];
-        const float f0 = sfield(wv, 0, 8);
-        const float f1 = sfield(wv, 8, 8);
-        const float f2 = sfield(wv, 16, 8);
-        const float f3 = sfield(wv, 24, 8);
-        out[d] = pack4_fp8(f0, f1, f2, f3);
+      for (int l = 0; l < 3; ++l) {
+        uint8_t* dst = a_t + ((l * MTILES + mt) * G + g) * (int64_t)TILE + slot * 16;
+        *reinterpret_cast<uint4*>(dst) =
+            make_uint4(out[l][4 * c], out[l][4 * c + 1], out[l][4 * c + 2], out[l][4 * c + 3]);
       }
-      uint8_t* dst = a_t + ((l * MTILES + mt) * G + g) * (int64_t)TILE + tile_offset<GS>(r, kk);
-      *reinterpret_cast<uint2*>(dst) = make_uint2(out[0], out[1]);
     }
-    if ((threadIdx.x & (GS / 8 - 1)) == 0) amax_t[(int64_t)g * Mpad + m] = amax;
+    if (q == 0) amax_t[(int64_t)g * Mpad + m] = amax;
     return;
   }
-  // W: thread -> (16 rows, 8 columns)
-  const int64_t t = (int64_t)(blockIdx.x - xblocks) * 256 + threadIdx.x;
-  const int64_t per_row = N / 8;
-  if (t >= (int64_t)(K / 16) * per_row) return;
-  const int kq = (int)(t / per_row);                  // 16-row block
-  const int n0 = (int)(t % per_row) * 8;
-  const int k0 = kq * 16;
-  uint32_t d[16];
+  // tiled weights: chunk t = (nt * KB + kb) * 64 + lane
+  const int KB = (K + kTileRows - 1) / kTileRows;
+  const int64_t t = (wid - xwaves) * 64 + lane;
+  if (t >= (int64_t)(N / kTileCols) * KB * 64) return;
+  const int kb = (int)((t >> 6) % KB);
+  const int64_t nt = (t >> 6) / KB;
+  const uint4 v = *reinterpret_cast<const uint4*>(wt + t * 16);
+  const uint32_t dw[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-  for (int r = 0; r < 16; ++r)
-    d[r] = *reinterpret_cast<const uint32_t*>(w + (int64_t)(k0 + r) * (N / 2) + n0 / 2);
-  const int g = k0 / GS, kk = k0 % GS;
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
+  for (int st = 0; st < 2; ++st) {
+    // step st: dwords 2st, 2st+1; rows j in the low nibbles, j+4 in the high
     uint32_t o[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      // column c is nibble c of each row's dword: a 4-bit two's-complement value
-      const float f0 = sfield((int32_t)d[4 * q + 0], 4 * c, 4);
-      const float f1 = sfield((int32_t)d[4 * q + 1], 4 * c, 4);
-      const float f2 = sfield((int32_t)d[4 * q + 2], 4 * c, 4);
-      const float f3 = sfield((int32_t)d[4 * q + 3], 4 * c, 4);
-      o[q] = pack4_fp8(f0, f1, f2, f3);
+    for (int d = 0; d < 2; ++d) {
+      const int32_t e = (int32_t)dw[2 * st + d];
+      o[2 * d] = pack4_fp8(sfield(e, 0, 4), sfield(e, 8, 4), sfield(e, 16, 4), sfield(e, 24, 4));
+      o[2 * d + 1] = pack4_fp8(sfield(e, 4, 4), sfield(e, 12, 4), sfield(e, 20, 4), sfield(e, 28, 4));
     }
-    const int n = n0 + c;
-    uint8_t* dst = b_t + ((int64_t)(n >> 4) * G + g) * TILE + tile_offset<GS>(n & 15, kk);
+    uint8_t* dst;
+    if constexpr (GS == 128) {
+      dst = b_t + ((nt * G + kb) * 2 + st) * 1024 + lane * 16;
+    } else {
+      const int g = 2 * kb + st;
+      if (g >= G) continue;                           // padding rows of the last block
+      dst = b_t + (nt * G + g) * 1024 + lane * 16;
+    }
     *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
   }
 }
@@ -365,19 +379,18 @@ PrefillLayout prefill_layout(int gs, int64_t M, int64_t K, int64_t N) {
 hipError_t launch_prefill_prep(const void* x, const void* w, int gs, int64_t M, int64_t K,
                                int64_t N, const PrefillLayout& L, uint8_t* a_t, float* amax_t,
                                uint8_t* b_t, hipStream_t stream) {
-  const int64_t xthreads = L.mpad * K / 8;
-  const int xblocks = (int)((xthreads + 255) / 256);
-  const int64_t wthreads = (K / 16) * (N / 8);
-  const int wblocks = (int)((wthreads + 255) / 256);
+  const int64_t xwaves = (L.mpad / 16) * (K / gs);             // (row tile, group) tasks
+  const int64_t wwaves = (N / kTileCols) * tiled_kblocks(K);   // 64 weight chunks each
+  const unsigned blocks = (unsigned)((xwaves + wwaves + 3) / 4);
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   const uint8_t* wp = static_cast<const uint8_t*>(w);
   const int m = (int)M, mp = (int)L.mpad, k = (int)K, n = (int)N;
   if (gs == 64)
-    hipLaunchKernelGGL(msd_prep_kernel<64>, dim3(xblocks + wblocks), dim3(256), 0, stream, xp, wp, m,
-                       mp, k, n, xblocks, a_t, amax_t, b_t);
+    hipLaunchKernelGGL(msd_prep_kernel<64>, dim3(blocks), dim3(256), 0, stream, xp, wp, m, mp, k, n,
+                       xwaves, a_t, amax_t, b_t);
   else
-    hipLaunchKernelGGL(msd_prep_kernel<128>, dim3(xblocks + wblocks), dim3(256), 0, stream, xp, wp, m,
-                       mp, k, n, xblocks, a_t, amax_t, b_t);
+    hipLaunchKernelGGL(msd_prep_kernel<128>, dim3(blocks), dim3(256), 0, stream, xp, wp, m, mp, k, n,
+                       xwaves, a_t, amax_t, b_t);
   return hipGetLastError();
 }
 
