@@ -32,7 +32,7 @@ constexpr int kDecodeMaxM = 16;
 // Split-K counters of the decode kernel live in a fixed prefix of the
 // workspace that no other kernel writes: one word per decode column block.
 constexpr int64_t kCounterWords = wqbmm::kDecodeCounterWords;
-static_assert(kCounterWords * wqbmm::kDecodeCols >= kMaxN, "a counter per column block");
+static_assert(kCounterWords * wqbmm::kTileCols >= kMaxN, "a counter per column block");
 constexpr size_t kCounterBytes = size_t(kCounterWords) * sizeof(uint32_t);
 
 // NULL counts as aligned: it is only accepted where the array is empty (M == 0).

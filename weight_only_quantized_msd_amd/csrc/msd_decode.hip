@@ -14,9 +14,16 @@
 // nGmOffset = baseN * blockIdx, plus a split of K):
 //   wave      = one 16-column tile x KBW 128-row blocks of the tiled weights
 //               (KBW contiguous 1 KB runs, one 16-byte load per lane each);
-//   workgroup = WC = 4 column tiles (64 columns) x WK = 4 waves along K, all
-//               sharing one decomposed slice of x in LDS;
-//   grid      = (N / 64 column blocks) x (K-splits).
+//   workgroup = WC column tiles x WK waves along K, all sharing one decomposed
+//               slice of x (R = WK*KBW*128 rows) in LDS;
+//   grid      = (column blocks) x (K-splits).
+// The decomposition is recomputed by every column block, M*R elements per
+// workgroup, and is VALU-bound; the split-K hand-off costs three dependent
+// device-memory round trips.  Two shapes balance them:
+//   M <= 4:  1 column tile x 16 waves x 2 blocks: R = 4096, so K <= 4096 needs
+//            no split and no hand-off (cheap to decompose at small M);
+//   M <= 16: 8 column tiles x 1 wave x 4 blocks: 128 columns share a 512-row
+//            decomposition; K-splits of 512 rows are handed off.
 // The tiled layout makes each 16-byte chunk exactly a lane's B operand of
 // v_mfma_i32_16x16x64_i8 for two 64-row steps (16*w per byte after masking the
 // nibbles), so the weights need no transposition.
@@ -38,8 +45,6 @@
 
 namespace wqbmm {
 namespace dc {
-constexpr int WC = kDecodeCols / kTileCols;   // column tiles per workgroup
-constexpr int WK = 4;                         // waves along K per column tile
 constexpr int PAD = 16;                       // LDS row padding (bank spread)
 }  // namespace dc
 
@@ -85,15 +90,18 @@ __global__ __launch_bounds__(64 * WC * WK) void msd_decode_kernel(
   //         wave.  Loads are unconditional (out-of-range ones read a valid
   //         address and are zeroed afterwards): a load under a branch makes the
   //         compiler wait for every outstanding load at the join.
-  constexpr int ITEMS = MT * (R / 8);
-  constexpr int ROUNDS = (ITEMS + THREADS - 1) / THREADS;
+  // Only the M real rows are decomposed.  The LDS rows (and A_max entries) of
+  // rows m >= M are left as they are: they only feed accumulator rows that
+  // are never stored, and integer MFMAs cannot trap.
+  constexpr int ROUNDS = (MT * (R / 8) + THREADS - 1) / THREADS;
+  const int items = (M < MT ? M : MT) * (R / 8);
   uint4 xv[ROUNDS];
 #pragma unroll
   for (int rd = 0; rd < ROUNDS; ++rd) {
     const int it = rd * THREADS + tid;
     const int m = it / (R / 8);
     const int k = kbase + (it % (R / 8)) * 8;
-    const bool ok = it < ITEMS && m < M && k < K;
+    const bool ok = it < items && k < K;
     const uint4 v = *reinterpret_cast<const uint4*>(x + (ok ? (int64_t)m * K + k : 0));
     xv[rd] = ok ? v : make_uint4(0u, 0u, 0u, 0u);
   }
@@ -129,19 +137,19 @@ __global__ __launch_bounds__(64 * WC * WK) void msd_decode_kernel(
   // dropped.
 #pragma unroll
   for (int rd = 0; rd < ROUNDS; ++rd) {
+    if (rd * THREADS >= items) break;              // workgroup-uniform
     const int it = rd * THREADS + tid;
     const int m = it / (R / 8);
     const int ch = it % (R / 8);
     uint32_t lv[3][2];
     float amax;
     msd_decompose8<GS>(xv[rd], lv, amax);
-    if (it < ITEMS) {
+    if (it < items) {
 #pragma unroll
       for (int l = 0; l < 3; ++l) {
         const int slot = LAYOUT == 0 ? (4 * m + l) : (l * 16 + m);
         *reinterpret_cast<uint2*>(sA + slot * ROWA + ch * 8) = make_uint2(lv[l][0], lv[l][1]);
       }
-      if (LAYOUT == 0) *reinterpret_cast<uint2*>(sA + (4 * m + 3) * ROWA + ch * 8) = make_uint2(0u, 0u);
       if ((ch & (GS / 8 - 1)) == 0) sAmax[m][(ch * 8) / GS] = amax;
     }
   }
@@ -303,19 +311,24 @@ hipError_t launch_zero_counters(uint32_t* counters, int64_t n, hipStream_t strea
   return hipGetLastError();
 }
 
-// Launch shape: 64-column blocks; two 128-row blocks per wave (a workgroup
-// then covers 1024 rows) unless that leaves fewer than 256 workgroups, in
-// which case one.
+// The two workgroup shapes (see the top of this file).
+namespace dc {
+constexpr int S0_WC = 1, S0_WK = 16, S0_KBW = 2;   // M <= 4
+constexpr int S1_WC = 8, S1_WK = 1, S1_KBW = 4;    // M <= 16
+}  // namespace dc
+
 DecodePlan decode_plan(int gs, int64_t M, int64_t K, int64_t N, int64_t g_begin, int64_t g_end) {
-  (void)M; (void)K;
+  (void)K;
   DecodePlan p;
-  p.col_blocks = (N + kDecodeCols - 1) / kDecodeCols;
+  p.shape = M <= 4 ? 0 : 1;
+  const int wc = p.shape == 0 ? dc::S0_WC : dc::S1_WC;
+  const int rows = (p.shape == 0 ? dc::S0_WK * dc::S0_KBW : dc::S1_WK * dc::S1_KBW) * kTileRows;
+  p.cols = wc * kTileCols;
+  p.col_blocks = (N + p.cols - 1) / p.cols;
   p.kb_begin = g_begin * gs / kTileRows;
   const int64_t kb_end = (g_end * gs + kTileRows - 1) / kTileRows;
   const int64_t nkb = kb_end - p.kb_begin;
-  const int64_t per2 = dc::WK * 2;
-  p.kbw = p.col_blocks * ((nkb + per2 - 1) / per2) >= 256 ? 2 : 1;
-  const int64_t per = dc::WK * p.kbw;
+  const int64_t per = rows / kTileRows;
   p.splits = (nkb + per - 1) / per;
   return p;
 }
@@ -323,7 +336,7 @@ DecodePlan decode_plan(int gs, int64_t M, int64_t K, int64_t N, int64_t g_begin,
 size_t decode_partials_bytes(const DecodePlan& p, int64_t M, int64_t N) {
   (void)N;
   if (p.splits <= 1) return 0;
-  return (size_t)p.splits * (size_t)M * (size_t)(p.col_blocks * kDecodeCols) * sizeof(float);
+  return (size_t)p.splits * (size_t)M * (size_t)(p.col_blocks * p.cols) * sizeof(float);
 }
 
 hipError_t launch_decode(const void* x, const void* w, const void* scale, int gs, int64_t M,
@@ -337,30 +350,22 @@ hipError_t launch_decode(const void* x, const void* w, const void* scale, int gs
   uint16_t* yp = static_cast<uint16_t*>(y);
   const int m = (int)M, k = (int)K, n = (int)N, gb = (int)g_begin, ge = (int)g_end;
   const int kb0 = (int)plan.kb_begin, S = (int)plan.splits;
-  if (plan.kbw != 1 && plan.kbw != 2) return hipErrorInvalidValue;
+  if ((plan.shape == 0) != (M <= 4) || M > 16) return hipErrorInvalidValue;
   if (S > 1 && !y_int && (!partials || !counters)) return hipErrorInvalidValue;
-#define WQBMM_DECODE_LAUNCH(GS_, L_, KBW_, Y_)                                                 \
-  hipLaunchKernelGGL((msd_decode_kernel<GS_, L_, dc::WC, dc::WK, KBW_, Y_>), grid,               \
-                     dim3(64 * dc::WC * dc::WK), 0, stream, xp, wp, sp, m, k, n, gb, ge, kb0, S, yp, \
-                     y_int, partials, counters)
-#define WQBMM_DECODE_KBW(GS_, L_, Y_)                                \
-  do {                                                               \
-    if (plan.kbw == 2) WQBMM_DECODE_LAUNCH(GS_, L_, 2, Y_);          \
-    else WQBMM_DECODE_LAUNCH(GS_, L_, 1, Y_);                        \
+#define WQBMM_DECODE_LAUNCH(GS_, L_, WC_, WK_, KBW_, Y_)                                         \
+  hipLaunchKernelGGL((msd_decode_kernel<GS_, L_, WC_, WK_, KBW_, Y_>), grid, dim3(64 * (WC_) * (WK_)), \
+                     0, stream, xp, wp, sp, m, k, n, gb, ge, kb0, S, yp, y_int, partials, counters)
+#define WQBMM_DECODE_SHAPE(GS_, Y_)                                                              \
+  do {                                                                                           \
+    if (plan.shape == 0) WQBMM_DECODE_LAUNCH(GS_, 0, dc::S0_WC, dc::S0_WK, dc::S0_KBW, Y_);       \
+    else WQBMM_DECODE_LAUNCH(GS_, 1, dc::S1_WC, dc::S1_WK, dc::S1_KBW, Y_);                       \
   } while (0)
-#define WQBMM_DECODE_Y(GS_, L_)                                      \
-  do {                                                               \
-    if (y_int) WQBMM_DECODE_KBW(GS_, L_, true);                      \
-    else WQBMM_DECODE_KBW(GS_, L_, false);                           \
-  } while (0)
-  const int layout = M <= 4 ? 0 : 1;
   if (gs == 64) {
-    if (layout == 0) WQBMM_DECODE_Y(64, 0); else WQBMM_DECODE_Y(64, 1);
+    if (y_int) WQBMM_DECODE_SHAPE(64, true); else WQBMM_DECODE_SHAPE(64, false);
   } else {
-    if (layout == 0) WQBMM_DECODE_Y(128, 0); else WQBMM_DECODE_Y(128, 1);
+    if (y_int) WQBMM_DECODE_SHAPE(128, true); else WQBMM_DECODE_SHAPE(128, false);
   }
-#undef WQBMM_DECODE_Y
-#undef WQBMM_DECODE_KBW
+#undef WQBMM_DECODE_SHAPE
 #undef WQBMM_DECODE_LAUNCH
   return hipGetLastError();
 }

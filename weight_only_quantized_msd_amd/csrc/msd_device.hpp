@@ -34,17 +34,37 @@ __device__ __forceinline__ uint16_t float_to_half_bits(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));  // RNE
 }
 
+// Division by a group's A_max.  Step 2 divides tmp = 7.49*a by A_max with a
+// correctly rounded fp32 divide.  Every element of a group shares the divisor,
+// so its reciprocal is formed once: y = rcp(d) refined by one Newton step,
+// y' = y + y*(1 - d*y).  Each quotient is then q0 = t*y', corrected once with
+// the exact remainder: q = q0 + y'*(t - d*q0) (Markstein's final step; both
+// corrections are single fused multiply-adds).  For the operands that occur
+// here (d a positive fp16 value, t = rn(7.49*a) with |a| <= d an fp16 value)
+// the result equals the correctly rounded t/d for every pair; a GPU test
+// checks that exhaustively against the CPU oracle's division.
+__device__ __forceinline__ float msd_recip(float d) {
+  const float y = __builtin_amdgcn_rcpf(d);
+  return __builtin_fmaf(__builtin_fmaf(-d, y, 1.0f), y, y);
+}
+
+__device__ __forceinline__ float msd_div(float t, float d, float y) {
+  const float q0 = t * y;
+  return __builtin_fmaf(__builtin_fmaf(-q0, d, t), y, q0);
+}
+
 // WQBMM-Exp page §4.1 steps 2-7 for one element of a group whose maximum
-// |x| is amax > 0: tmp1 = 7.49*a/A_max, A1 = round(tmp1),
-// tmp2 = (tmp1-A1)*14.98, A2 = round(tmp2), tmp3 = (tmp2-A2)*14.98,
-// A3 = round(tmp3).  Every operation is one IEEE fp32 rounding in this order
-// (no contraction; '/' is the correctly rounded divide), round is
-// half-to-even (v_rndne_f32).  |A_l| <= 7 follows from 7.49 < 7.5 and
-// |residual| <= 0.5.  msd_expand_f returns the levels as (integral) floats,
-// msd_expand as ints.
-__device__ __forceinline__ void msd_expand_f(float a, float amax, float& r1, float& r2, float& r3) {
+// |x| is amax > 0 (rcp = msd_recip(amax)): tmp1 = 7.49*a/A_max, A1 =
+// round(tmp1), tmp2 = (tmp1-A1)*14.98, A2 = round(tmp2), tmp3 =
+// (tmp2-A2)*14.98, A3 = round(tmp3).  Every operation is one IEEE fp32
+// rounding in this order (no contraction; the division is correctly
+// rounded, see msd_div), round is half-to-even (v_rndne_f32).  |A_l| <= 7
+// follows from 7.49 < 7.5 and |residual| <= 0.5.  msd_expand_f returns the
+// levels as (integral) floats, msd_expand as ints.
+__device__ __forceinline__ void msd_expand_f(float a, float amax, float rcp, float& r1, float& r2,
+                                             float& r3) {
 #pragma clang fp contract(off)
-  const float t1 = (kF1 * a) / amax;
+  const float t1 = msd_div(kF1 * a, amax, rcp);
   r1 = __builtin_rintf(t1);
   const float t2 = (t1 - r1) * kF2;
   r2 = __builtin_rintf(t2);
@@ -52,9 +72,9 @@ __device__ __forceinline__ void msd_expand_f(float a, float amax, float& r1, flo
   r3 = __builtin_rintf(t3);
 }
 
-__device__ __forceinline__ void msd_expand(float a, float amax, int& A1, int& A2, int& A3) {
+__device__ __forceinline__ void msd_expand(float a, float amax, float rcp, int& A1, int& A2, int& A3) {
   float r1, r2, r3;
-  msd_expand_f(a, amax, r1, r2, r3);
+  msd_expand_f(a, amax, rcp, r1, r2, r3);
   A1 = (int)r1;
   A2 = (int)r2;
   A3 = (int)r3;
@@ -98,10 +118,11 @@ __device__ __forceinline__ void msd_decompose8(const uint4 xv, uint32_t (&lv)[3]
 #pragma unroll
   for (int l = 0; l < 3; ++l) lv[l][0] = lv[l][1] = 0u;
   if (amax > 0.0f) {
+    const float rcp = msd_recip(amax);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       int A1, A2, A3;
-      msd_expand(a[i], amax, A1, A2, A3);
+      msd_expand(a[i], amax, rcp, A1, A2, A3);
       const int sh = 8 * (i & 3);
       lv[0][i >> 2] |= (uint32_t)(A1 & 0xff) << sh;
       lv[1][i >> 2] |= (uint32_t)(A2 & 0xff) << sh;

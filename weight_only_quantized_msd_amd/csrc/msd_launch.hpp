@@ -54,13 +54,14 @@ hipError_t launch_prefill_gemm(const uint8_t* a_t, const float* amax_t, const ui
 // deterministic split-K reduction through `partials` and one self-re-arming
 // counter per column block (`counters` must be zero before the first launch).
 struct DecodePlan {
-  int64_t col_blocks;   // blocks of kDecodeCols columns
+  int shape;            // workgroup shape: 0 for M <= 4, 1 for M <= 16
+  int64_t cols;         // columns per workgroup
+  int64_t col_blocks;   // column blocks
   int64_t splits;       // K-slices per column block
   int64_t kb_begin;     // first 128-row block of the group range
-  int kbw;              // 128-row blocks per wave (1 or 2)
 };
-constexpr int kDecodeCols = 64;   // columns per decode workgroup
-constexpr int64_t kDecodeCounterWords = (int64_t(1) << 20) / kDecodeCols;
+// one split-K counter per column block; column blocks are >= 16 columns
+constexpr int64_t kDecodeCounterWords = (int64_t(1) << 20) / kTileCols;
 DecodePlan decode_plan(int gs, int64_t M, int64_t K, int64_t N, int64_t g_begin, int64_t g_end);
 size_t decode_partials_bytes(const DecodePlan& p, int64_t M, int64_t N);
 

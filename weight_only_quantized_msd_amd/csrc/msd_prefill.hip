@@ -128,11 +128,12 @@ __global__ __launch_bounds__(256) void msd_prep_kernel(const uint16_t* __restric
 #pragma unroll
       for (int d = 0; d < EPL / 4; ++d) out[l][d] = 0u;
     if (amax > 0.0f) {
+      const float rcp = msd_recip(amax);
 #pragma unroll
       for (int d = 0; d < EPL / 4; ++d) {
         float r3[3][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) msd_expand_f(a[4 * d + i], amax, r3[0][i], r3[1][i], r3[2][i]);
+        for (int i = 0; i < 4; ++i) msd_expand_f(a[4 * d + i], amax, rcp, r3[0][i], r3[1][i], r3[2][i]);
 #pragma unroll
         for (int l = 0; l < 3; ++l) out[l][d] = pack4_fp8(r3[l][0], r3[l][1], r3[l][2], r3[l][3]);
       }
