@@ -12,6 +12,7 @@
 // section 返回值说明.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstring>
 #include <map>
@@ -29,11 +30,6 @@ constexpr int64_t kMaxM = int64_t(1) << 24;
 constexpr int64_t kMaxK = int64_t(1) << 20;
 constexpr int64_t kMaxN = int64_t(1) << 20;
 constexpr int kDecodeMaxM = 16;
-// Split-K counters of the decode kernel live in a fixed prefix of the
-// workspace that no other kernel writes: one word per decode column block.
-constexpr int64_t kCounterWords = wqbmm::kDecodeCounterWords;
-static_assert(kCounterWords * wqbmm::kTileCols >= kMaxN, "a counter per column block");
-constexpr size_t kCounterBytes = size_t(kCounterWords) * sizeof(uint32_t);
 
 // NULL counts as aligned: it is only accepted where the array is empty (M == 0).
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -70,9 +66,14 @@ wqbmm_status check_device(int* dev_out) {
 }
 
 // ---- per-(device, stream) workspace, grown on demand
+// Layout: [decode accumulators][scratch].  The decode accumulators must be
+// zero before a decode launch; the kernel re-arms every element it uses, and
+// no other kernel writes that region, so it is zeroed only when allocated.
+// The scratch region holds the prefill operand tiles.
 struct Workspace {
   void* base = nullptr;
-  size_t bytes = 0;
+  size_t acc_bytes = 0;
+  size_t scratch_bytes = 0;
   // shape whose prefill operands the scratch region currently holds
   int64_t prep_gs = 0, prep_m = -1, prep_k = 0, prep_n = 0;
 };
@@ -80,36 +81,41 @@ std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Returns the counter prefix and a scratch region of at least `bytes` for
-// launches on `stream`.  Growth synchronizes `stream` so that no launch still
-// using the old buffer is pending before it is freed; a new buffer gets its
-// counters zeroed by a kernel enqueued on `stream`.
-wqbmm_status get_workspace(int dev, hipStream_t stream, size_t bytes, uint32_t** counters,
-                           uint8_t** scratch) {
-  const size_t prefix = round_up(kCounterBytes, 256);
-  const size_t need = prefix + round_up(bytes, 256);
+// Returns an accumulator region of at least `acc` bytes (zeroed) and a
+// scratch region of at least `scratch` bytes for launches on `stream`.
+// Growth synchronizes `stream` so that no launch still using the old buffer
+// is pending before it is freed; a new buffer gets its accumulator region
+// zeroed by a kernel enqueued on `stream`.
+wqbmm_status get_workspace(int dev, hipStream_t stream, size_t acc, size_t scratch,
+                           uint64_t** acc_out, uint8_t** scratch_out) {
   std::lock_guard<std::mutex> lk(g_mu);
   Workspace& ws = g_ws[std::make_pair(dev, stream)];
-  if (ws.bytes < need) {
+  acc = round_up(acc, 256);
+  scratch = round_up(scratch, 256);
+  if (ws.acc_bytes < acc || ws.scratch_bytes < scratch || !ws.base) {
+    const size_t new_acc = std::max(ws.acc_bytes, acc + acc / 4);
+    const size_t new_scratch = std::max(ws.scratch_bytes, scratch + scratch / 4);
     if (ws.base) {
       if (hipStreamSynchronize(stream) != hipSuccess) return WQBMM_ERR_LAUNCH;
       (void)hipFree(ws.base);
       ws.base = nullptr;
-      ws.bytes = 0;
+      ws.acc_bytes = ws.scratch_bytes = 0;
     }
-    const size_t grow = need + need / 4;
     void* p = nullptr;
-    if (hipMalloc(&p, grow) != hipSuccess) return WQBMM_ERR_ALLOC;
-    if (wqbmm::launch_zero_counters(static_cast<uint32_t*>(p), kCounterWords, stream) != hipSuccess) {
+    const size_t total = round_up(new_acc, 256) + round_up(new_scratch, 256) + 256;
+    if (hipMalloc(&p, total) != hipSuccess) return WQBMM_ERR_ALLOC;
+    if (wqbmm::launch_zero_words(static_cast<uint32_t*>(p), (int64_t)(round_up(new_acc, 256) / 4),
+                                 stream) != hipSuccess) {
       (void)hipFree(p);
       return WQBMM_ERR_LAUNCH;
     }
     ws.base = p;
-    ws.bytes = grow;
+    ws.acc_bytes = round_up(new_acc, 256);
+    ws.scratch_bytes = round_up(new_scratch, 256);
     ws.prep_m = -1;
   }
-  *counters = static_cast<uint32_t*>(ws.base);
-  *scratch = static_cast<uint8_t*>(ws.base) + prefix;
+  *acc_out = static_cast<uint64_t*>(ws.base);
+  *scratch_out = static_cast<uint8_t*>(ws.base) + ws.acc_bytes;
   return WQBMM_OK;
 }
 
@@ -133,16 +139,15 @@ wqbmm_status run(const void* x, const void* w, const void* scale, int64_t gs, in
   if (st != WQBMM_OK) return st;
   if (path == WQBMM_PATH_DECODE) {
     const DecodePlan plan = wqbmm::decode_plan((int)gs, M, K, N, g_begin, g_end);
-    uint32_t* counters = nullptr;
+    uint64_t* accum = nullptr;
     uint8_t* scratch = nullptr;
-    const size_t pbytes = y_int ? 0 : wqbmm::decode_partials_bytes(plan, M, N);
-    if (pbytes) {
-      st = get_workspace(dev, stream, pbytes, &counters, &scratch);
+    const size_t abytes = y_int ? 0 : wqbmm::decode_accum_bytes(plan, M, N);
+    if (abytes) {
+      st = get_workspace(dev, stream, abytes, 0, &accum, &scratch);
       if (st != WQBMM_OK) return st;
     }
     return launch_status(wqbmm::launch_decode(x, w, scale, (int)gs, M, K, N, g_begin, g_end, y,
-                                              y_int, reinterpret_cast<float*>(scratch), counters,
-                                              plan, stream));
+                                              y_int, accum, plan, stream));
   }
   // prefill: operand preparation into the workspace, then the MFMA GEMM
   return run_prefill(dev, x, w, scale, gs, M, K, N, g_begin, g_end, y, y_int, 0, stream);
@@ -159,9 +164,9 @@ wqbmm_status run_prefill(int dev, const void* x, const void* w, const void* scal
   const size_t amax_off = round_up(L.a_bytes, 256);
   const size_t b_off = amax_off + round_up(L.amax_bytes, 256);
   const size_t total = b_off + round_up(L.b_bytes, 256);
-  uint32_t* counters = nullptr;
+  uint64_t* accum = nullptr;
   uint8_t* scratch = nullptr;
-  wqbmm_status st = get_workspace(dev, stream, total, &counters, &scratch);
+  wqbmm_status st = get_workspace(dev, stream, 0, total, &accum, &scratch);
   if (st != WQBMM_OK) return st;
   uint8_t* a_t = scratch + a_off;
   float* amax_t = reinterpret_cast<float*>(scratch + amax_off);

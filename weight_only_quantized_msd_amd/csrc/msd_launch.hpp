@@ -50,27 +50,25 @@ hipError_t launch_prefill_gemm(const uint8_t* a_t, const float* amax_t, const ui
                                const PrefillLayout& L, int64_t g_begin, int64_t g_end, void* y,
                                int32_t* y_int, hipStream_t stream);
 
-// The fused decode kernel (M <= 16): steps 1-11 in one launch, with a
-// deterministic split-K reduction through `partials` and one self-re-arming
-// counter per column block (`counters` must be zero before the first launch).
+// The fused decode kernel (M <= 16): steps 1-11 in one launch.  A K-split
+// hands its partials off through `accum` (int64 per output; zero before the
+// first launch, re-armed by the kernel).
 struct DecodePlan {
   int shape;            // workgroup shape: 0 for M <= 4, 1 for M <= 16
   int64_t cols;         // columns per workgroup
   int64_t col_blocks;   // column blocks
-  int64_t splits;       // K-slices per column block
+  int64_t splits;       // K-slices per column block (<= 32)
+  int64_t nch;          // row chunks per K-slice
   int64_t kb_begin;     // first 128-row block of the group range
 };
-// one split-K counter per column block; column blocks are >= 16 columns
-constexpr int64_t kDecodeCounterWords = (int64_t(1) << 20) / kTileCols;
 DecodePlan decode_plan(int gs, int64_t M, int64_t K, int64_t N, int64_t g_begin, int64_t g_end);
-size_t decode_partials_bytes(const DecodePlan& p, int64_t M, int64_t N);
+size_t decode_accum_bytes(const DecodePlan& p, int64_t M, int64_t N);
 
 hipError_t launch_decode(const void* x, const void* w, const void* scale, int gs, int64_t M,
                          int64_t K, int64_t N, int64_t g_begin, int64_t g_end, void* y,
-                         int32_t* y_int, float* partials, uint32_t* counters,
-                         const DecodePlan& plan, hipStream_t stream);
+                         int32_t* y_int, uint64_t* accum, const DecodePlan& plan, hipStream_t stream);
 
-// Zero n counter words (a kernel, not a memset).
-hipError_t launch_zero_counters(uint32_t* counters, int64_t n, hipStream_t stream);
+// Zero n 32-bit words (a kernel, not a memset).
+hipError_t launch_zero_words(uint32_t* p, int64_t n, hipStream_t stream);
 
 }  // namespace wqbmm
