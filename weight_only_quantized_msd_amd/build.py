@@ -19,6 +19,9 @@ SOURCES = ["msd_api.cpp", "msd_prepack.hip", "msd_prepass.hip", "msd_prefill.hip
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CFLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs: the fused epilogues read every accumulator, and
+    # the AGPR form costs one v_accvgpr_read per value
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
           "-Wall", "-Wno-unused-function"]
 
 

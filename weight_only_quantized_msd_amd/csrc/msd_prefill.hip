@@ -35,13 +35,16 @@
 //   B_t: [column tile][group][tile]
 //   A_max_t: [group][row]  fp32
 //
-// GEMM tiling: workgroup tile BM=128 rows x BN=128 columns, 8 waves in a 4x2
-// grid, wave tile 32x64 = 2x4 MFMA tiles of 16x16, times 3 levels.  LDS holds
-// one group's A (3 x 8 tiles) and B (8 tiles), double-buffered; the next
-// group's global loads are issued before the current group's MFMAs and
-// copied to the other buffer afterwards, one barrier per group.  Within a
-// group a wave walks its 8 output tiles: the tile's 3 MFMAs are issued, then
-// the fp32 combine of the previous tile, so MFMA and VALU overlap in the wave.
+// GEMM tiling: workgroup tile BM=128 rows x BN=128 columns, 4 waves, wave
+// tile 32 rows x 128 columns = 2x8 MFMA tiles of 16x16, times 3 levels: each
+// wave reuses its three A operands across all 8 column tiles, which keeps
+// the LDS reads per MFMA low (the A operand is three times the bytes of an
+// ordinary GEMM's).  LDS holds one group's A (3 x 8 tiles) and B (8 tiles),
+// double-buffered; the next group is copied global -> LDS directly
+// (global_load_lds, 16 bytes per lane, no staging registers) while the
+// current group is computed, one barrier per group.  Within a group a wave
+// walks its 16 output tiles: the tile's 3 MFMAs are issued, then the fp32
+// combine of the previous tile, so MFMA and VALU overlap in the wave.
 // Tile order: the linear workgroup id is remapped so that each XCD
 // (workgroups are dealt to the 8 XCDs round-robin) gets a contiguous range of
 // row-major tiles, keeping the A rows its tiles share in that XCD's L2.  The
@@ -53,11 +56,14 @@ namespace wqbmm {
 namespace pf {
 constexpr int BM = 128;
 constexpr int BN = 128;
-constexpr int THREADS = 512;
-constexpr int WM = 32;
-constexpr int WN = 64;
-constexpr int MT = WM / 16;   // 2 row tiles per wave
-constexpr int NT = WN / 16;   // 4 column tiles per wave
+constexpr int WAVES_N = 2;     // waves along N
+constexpr int WAVES_M = 4;     // waves along M
+constexpr int WAVES = WAVES_M * WAVES_N;
+constexpr int THREADS = 64 * WAVES;
+constexpr int WM = BM / WAVES_M;   // 32 rows per wave
+constexpr int WN = BN / WAVES_N;   // 64 columns per wave
+constexpr int MT = WM / 16;    // 2 row tiles per wave
+constexpr int NT = WN / 16;    // 4 column tiles per wave
 constexpr int NXCD = 8;
 }  // namespace pf
 
@@ -185,29 +191,35 @@ __global__ __launch_bounds__(256) void msd_prep_kernel(const uint16_t* __restric
 
 // ---------------------------------------------------------------- GEMM kernel
 template <int GS, bool YINT>
-__global__ __launch_bounds__(512, 1) void msd_gemm_kernel(
+__global__ __launch_bounds__(pf::THREADS, 1) void msd_gemm_kernel(
     const uint8_t* __restrict__ a_t, const float* __restrict__ amax_t,
     const uint8_t* __restrict__ b_t, const uint16_t* __restrict__ scale, int M, int Mpad, int K,
     int N, int g_begin, int g_end, int mblocks, int nblocks, uint16_t* __restrict__ y,
     int32_t* __restrict__ y_int) {
   using namespace pf;
-  constexpr int TILE = GS * 16;                    // bytes per operand tile and group
-  constexpr int A_BYTES = 3 * (BM / 16) * TILE;    // per group
-  constexpr int B_BYTES = (BN / 16) * TILE;
-  constexpr int A_PER_T = A_BYTES / 16 / THREADS;  // 16-byte chunks per thread: 6 or 3
-  constexpr int B_PER_T = B_BYTES / 16 / THREADS;  // 2 or 1
-  static_assert(A_BYTES % (16 * THREADS) == 0 && B_BYTES % (16 * THREADS) == 0, "staging split");
+  constexpr int TILE = GS * 16;                        // bytes per operand tile and group
+  constexpr int HALVES = GS / 64;                      // 1 KB chunks per tile
+  constexpr int A_CHUNKS = 3 * (BM / 16) * HALVES;     // per group: 48 or 24
+  constexpr int B_CHUNKS = (BN / 16) * HALVES;         // per group: 16 or 8
+  constexpr int CPW = (A_CHUNKS + B_CHUNKS) / WAVES;   // chunks copied per wave
+  static_assert((A_CHUNKS + B_CHUNKS) % WAVES == 0 && A_CHUNKS % CPW == 0, "chunk split");
 
-  __shared__ __attribute__((aligned(16))) uint8_t sA[2][A_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t sB[2][B_BYTES];
-  __shared__ float sAmax[2][BM];
-  __shared__ float sScale[2][BN];
+  // Two named buffers (not one array indexed by the parity of the group) so
+  // that the copies into one and the reads of the other are visibly disjoint.
+  __shared__ __attribute__((aligned(16))) uint8_t sA0[A_CHUNKS * 1024];
+  __shared__ __attribute__((aligned(16))) uint8_t sA1[A_CHUNKS * 1024];
+  __shared__ __attribute__((aligned(16))) uint8_t sB0[B_CHUNKS * 1024];
+  __shared__ __attribute__((aligned(16))) uint8_t sB1[B_CHUNKS * 1024];
+  __shared__ __attribute__((aligned(16))) float sAm0[BM];
+  __shared__ __attribute__((aligned(16))) float sAm1[BM];
+  __shared__ __attribute__((aligned(16))) uint16_t sSc0[BN];
+  __shared__ __attribute__((aligned(16))) uint16_t sSc1[BN];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1;        // 0..3
-  const int wn = wave & 1;         // 0..1
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WAVES_N;   // rows WM*wm of the tile
+  const int wn = wave % WAVES_N;   // columns WN*wn of the tile
 
   const int total = mblocks * nblocks;
   int t = blockIdx.x;
@@ -217,60 +229,123 @@ __global__ __launch_bounds__(512, 1) void msd_gemm_kernel(
   const int G = K / GS;
   const int64_t MTILES = Mpad / 16;
 
-  // Staging: chunk c of the A stage is (level, row tile, 16-byte chunk of the
-  // tile); tiles of rows beyond the padded row count, and of columns beyond
-  // N, are read from a clamped valid tile: they only feed outputs never stored.
-  uint4 ra[A_PER_T], rb[B_PER_T];
-  float ram, rsc;
-#define WQBMM_PF_LOAD(g_)                                                                         \
-  do {                                                                                            \
-    _Pragma("unroll") for (int i = 0; i < A_PER_T; ++i) {                                         \
-      const int c = tid + i * THREADS;                                                            \
-      const int tl = c / (TILE / 16), off = c % (TILE / 16);                                      \
-      const int l = tl / (BM / 16), mt = min(m0 / 16 + tl % (BM / 16), (int)MTILES - 1);          \
-      ra[i] = *reinterpret_cast<const uint4*>(a_t + ((l * MTILES + mt) * G + (g_)) * (int64_t)TILE + off * 16); \
-    }                                                                                             \
-    _Pragma("unroll") for (int i = 0; i < B_PER_T; ++i) {                                         \
-      const int c = tid + i * THREADS;                                                            \
-      const int tl = c / (TILE / 16), off = c % (TILE / 16);                                      \
-      const int nt = min(n0 / 16 + tl, N / 16 - 1);                                               \
-      rb[i] = *reinterpret_cast<const uint4*>(b_t + ((int64_t)nt * G + (g_)) * TILE + off * 16);  \
-    }                                                                                             \
-    ram = amax_t[(int64_t)(g_) * Mpad + min(m0 + (tid % BM), Mpad - 1)];                         \
-    rsc = YINT ? 0.0f : half_bits_to_float(scale[(int64_t)(g_) * N + min(n0 + (tid % BN), N - 1)]); \
-  } while (0)
-#define WQBMM_PF_STORE(st_)                                                                       \
-  do {                                                                                            \
-    _Pragma("unroll") for (int i = 0; i < A_PER_T; ++i)                                           \
-        *reinterpret_cast<uint4*>(&sA[st_][(tid + i * THREADS) * 16]) = ra[i];                    \
-    _Pragma("unroll") for (int i = 0; i < B_PER_T; ++i)                                           \
-        *reinterpret_cast<uint4*>(&sB[st_][(tid + i * THREADS) * 16]) = rb[i];                    \
-    if (tid < BM) sAmax[st_][tid] = ram;                                                          \
-    else if (tid < BM + BN) sScale[st_][tid - BM] = rsc;                                          \
+  // This wave's share of a group's operand chunks: chunk q = tile * HALVES +
+  // half, A tiles (level, row tile) first, then B tiles; a wave's chunks are
+  // all A or all B.  csrc[c] is the chunk's byte offset at group 0 (uniform).
+  // Tiles of rows beyond the padded row count, and of columns beyond N, are
+  // read from a clamped valid tile: they only feed outputs never stored.
+  const bool a_wave = wave * CPW < A_CHUNKS;
+  int64_t csrc[CPW];
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) {
+    const int q = wave * CPW + c;
+    if (q < A_CHUNKS) {
+      const int tile = q / HALVES, h = q % HALVES;
+      const int l = tile / (BM / 16), mt = min(m0 / 16 + tile % (BM / 16), (int)MTILES - 1);
+      csrc[c] = (l * MTILES + mt) * G * (int64_t)TILE + h * 1024;
+    } else {
+      const int tile = (q - A_CHUNKS) / HALVES, h = (q - A_CHUNKS) % HALVES;
+      const int nt = min(n0 / 16 + tile, N / 16 - 1);
+      csrc[c] = (int64_t)nt * G * TILE + h * 1024;
+    }
+  }
+  const int am_row0 = min(m0 + lane, Mpad - 1), am_row1 = min(m0 + 64 + lane, Mpad - 1);
+  const int sc_col = min(n0 + 2 * lane, N - 2);
+
+  // Group g_'s operands -> LDS, by DMA (global_load_lds, 16 bytes per lane:
+  // lane i's bytes land at the destination + 16*i, i.e. a [lane][16] chunk).
+  // A_max (fp32) and the scales (fp16 pairs) go 4 bytes per lane.  (The
+  // 4-byte copies take byte pointers: typed float pointers made the
+  // compiler crash in its SGPR-copy pass.)
+#define WQBMM_DMA(g_, SA_, SB_, SAM_, SSC_)                                                        \
+  do {                                                                                             \
+    const int64_t goff_ = (int64_t)(g_) * TILE;                                                    \
+    _Pragma("unroll") for (int c = 0; c < CPW; ++c) {                                              \
+      const int q = wave * CPW + c;                                                                \
+      const uint8_t* src_ = (a_wave ? a_t : b_t) + (csrc[c] + goff_) + lane * 16;                  \
+      uint8_t* dst_ = a_wave ? (SA_) + q * 1024 : (SB_) + (q - A_CHUNKS) * 1024;                   \
+      __builtin_amdgcn_global_load_lds(src_, dst_, 16, 0, 0);                                      \
+    }                                                                                              \
+    if (wave == WAVES - 1) {                                                                       \
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(amax_t) + ((int64_t)(g_) * Mpad + am_row0) * 4, reinterpret_cast<uint8_t*>(SAM_), 4, 0, 0);  \
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(amax_t) + ((int64_t)(g_) * Mpad + am_row1) * 4, reinterpret_cast<uint8_t*>(SAM_) + 256, 4, 0, 0); \
+      if constexpr (!YINT)                                                                         \
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(scale) + ((int64_t)(g_) * N + sc_col) * 2, reinterpret_cast<uint8_t*>(SSC_), 4, 0, 0);     \
+    }                                                                                              \
   } while (0)
 
   // Steps 10-11 for one 16x16 output tile (row tile PM_, column tile PN_)
   // from its three level accumulators ACC_; or the Y_int export.
-#define WQBMM_PF_EPILOGUE(PM_, PN_, ACC_)                                                         \
-  do {                                                                                            \
-    if constexpr (YINT) {                                                                         \
-      const int64_t gi = g - g_begin;                                                             \
-      const int n = n0 + wn * WN + (PN_) * 16 + (lane & 15);                                      \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                             \
-        const int m = m0 + wm * WM + (PM_) * 16 + (lane >> 4) * 4 + i;                            \
-        if (m < M && n < N) {                                                                     \
-          _Pragma("unroll") for (int l = 0; l < 3; ++l)                                           \
-              y_int[((gi * 3 + l) * M + m) * (int64_t)N + n] = (int32_t)(ACC_)[l][i];             \
-        }                                                                                         \
-      }                                                                                           \
-    } else {                                                                                      \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                             \
-        float tt = (ACC_)[0][i] * q[PM_][i][0];                                                   \
-        tt = __builtin_fmaf((ACC_)[1][i], q[PM_][i][1], tt);                                      \
-        tt = __builtin_fmaf((ACC_)[2][i], q[PM_][i][2], tt);                                      \
-        yacc[PM_][PN_][i] = __builtin_fmaf(tt, sc[PN_], yacc[PM_][PN_][i]);                       \
-      }                                                                                           \
-    }                                                                                             \
+#define WQBMM_PF_EPILOGUE(PM_, PN_, ACC_, G_)                                                      \
+  do {                                                                                             \
+    if constexpr (YINT) {                                                                          \
+      const int64_t gi = (G_) - g_begin;                                                           \
+      const int n = n0 + wn * WN + (PN_) * 16 + (lane & 15);                                                 \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                              \
+        const int m = m0 + wm * WM + (PM_) * 16 + (lane >> 4) * 4 + i;                           \
+        if (m < M && n < N) {                                                                      \
+          _Pragma("unroll") for (int l = 0; l < 3; ++l)                                            \
+              y_int[((gi * 3 + l) * M + m) * (int64_t)N + n] = (int32_t)(ACC_)[l][i];              \
+        }                                                                                          \
+      }                                                                                            \
+    } else {                                                                                       \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                              \
+        float tt = (ACC_)[0][i] * q[PM_][i][0];                                                    \
+        tt = __builtin_fmaf((ACC_)[1][i], q[PM_][i][1], tt);                                       \
+        tt = __builtin_fmaf((ACC_)[2][i], q[PM_][i][2], tt);                                       \
+        yacc[PM_][PN_][i] = __builtin_fmaf(tt, sc[PN_], yacc[PM_][PN_][i]);                        \
+      }                                                                                            \
+    }                                                                                              \
+  } while (0)
+
+  // One group from one buffer: the wave's 2 x 3 A operands stay in registers;
+  // per column tile, its B operand and 2 x 3 MFMAs, the combine of each
+  // output tile interleaved with the next tile's MFMAs.
+#define WQBMM_COMPUTE(SA_, SB_, SAM_, SSC_, G_)                                                    \
+  do {                                                                                             \
+    float q[MT][4][3], sc[NT];                                                                     \
+    if constexpr (!YINT) {                                                                         \
+      _Pragma("unroll") for (int nt = 0; nt < NT; ++nt)                                            \
+          sc[nt] = half_bits_to_float((SSC_)[wn * WN + nt * 16 + (lane & 15)]);                              \
+      _Pragma("unroll") for (int mt = 0; mt < MT; ++mt) {                                          \
+        const float4 a4 = *reinterpret_cast<const float4*>(&(SAM_)[wm * WM + mt * 16 + (lane >> 4) * 4]); \
+        const float am[4] = {a4.x, a4.y, a4.z, a4.w};                                              \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                            \
+          q[mt][i][0] = am[i] * kE1;                                                               \
+          q[mt][i][1] = am[i] * kE2;                                                               \
+          q[mt][i][2] = am[i] * kE3;                                                               \
+        }                                                                                          \
+      }                                                                                            \
+    }                                                                                              \
+    v8i af[MT][3];                                                                                 \
+    _Pragma("unroll") for (int mt = 0; mt < MT; ++mt)                                              \
+      _Pragma("unroll") for (int l = 0; l < 3; ++l) {                                              \
+        const uint8_t* base = (SA_) + (l * (BM / 16) + wm * MT + mt) * TILE;                     \
+        const v4i lo = *reinterpret_cast<const v4i*>(base + lane * 16);                            \
+        const v4i hi = HALVES == 2 ? *reinterpret_cast<const v4i*>(base + 1024 + lane * 16) : v4i{0, 0, 0, 0}; \
+        af[mt][l] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};                   \
+      }                                                                                            \
+    v4f acc[2][3];                                                                                 \
+    _Pragma("unroll") for (int nt = 0; nt < NT; ++nt) {                                            \
+      const uint8_t* bb = (SB_) + (wn * NT + nt) * TILE;                                                       \
+      const v4i blo = *reinterpret_cast<const v4i*>(bb + lane * 16);                               \
+      const v4i bhi = HALVES == 2 ? *reinterpret_cast<const v4i*>(bb + 1024 + lane * 16) : v4i{0, 0, 0, 0}; \
+      const v8i bf = v8i{blo[0], blo[1], blo[2], blo[3], bhi[0], bhi[1], bhi[2], bhi[3]};          \
+      _Pragma("unroll") for (int mt = 0; mt < MT; ++mt) {                                          \
+        const int j = nt * MT + mt, cur = j & 1;                                                   \
+        _Pragma("unroll") for (int l = 0; l < 3; ++l)                                              \
+            acc[cur][l] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(                        \
+                af[mt][l], bf, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);                     \
+        if (j > 0) {                                                                               \
+          const int pm = (j - 1) % MT, pn = (j - 1) / MT;                                          \
+          WQBMM_PF_EPILOGUE(pm, pn, acc[cur ^ 1], G_);                                             \
+        }                                                                                          \
+      }                                                                                            \
+    }                                                                                              \
+    {                                                                                              \
+      constexpr int jl = MT * NT - 1;                                                              \
+      WQBMM_PF_EPILOGUE(jl % MT, jl / MT, acc[jl & 1], G_);                                        \
+    }                                                                                              \
   } while (0)
 
   float yacc[MT][NT][4];
@@ -281,73 +356,27 @@ __global__ __launch_bounds__(512, 1) void msd_gemm_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) yacc[mt][nt][i] = 0.0f;
 
-  WQBMM_PF_LOAD(g_begin);
-  WQBMM_PF_STORE(0);
+  // Buffer 0 holds the even-indexed groups of the range, buffer 1 the odd
+  // ones.  While a group is computed from one buffer, the next group is
+  // copied into the other; each wave waits for its own copies, and the
+  // barrier then publishes all of them and frees the buffer just read.
+  WQBMM_DMA(g_begin, sA0, sB0, sAm0, sSc0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-
-  for (int g = g_begin; g < g_end; ++g) {
-    const int st = (g - g_begin) & 1;
-    const bool more = g + 1 < g_end;
-    WQBMM_PF_LOAD(more ? g + 1 : g);   // unconditional: the last group re-reads itself, unused
-
-    float q[MT][4][3], sc[NT];
-    if constexpr (!YINT) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) sc[nt] = sScale[st][wn * WN + nt * 16 + (lane & 15)];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float am = sAmax[st][wm * WM + mt * 16 + (lane >> 4) * 4 + i];
-          q[mt][i][0] = am * kE1;
-          q[mt][i][1] = am * kE2;
-          q[mt][i][2] = am * kE3;
-        }
-    }
-    // W operands of the wave's 4 column tiles
-    v8i bf[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const uint8_t* base = &sB[st][(wn * NT + nt) * TILE];
-      const v4i lo = *reinterpret_cast<const v4i*>(base + lane * 16);
-      const v4i hi = GS == 128 ? *reinterpret_cast<const v4i*>(base + 1024 + lane * 16) : v4i{0, 0, 0, 0};
-      bf[nt] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    }
-    v4f acc[2][3];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      v8i af[3];
-#pragma unroll
-      for (int l = 0; l < 3; ++l) {
-        const uint8_t* base = &sA[st][(l * (BM / 16) + wm * MT + mt) * TILE];
-        const v4i lo = *reinterpret_cast<const v4i*>(base + lane * 16);
-        const v4i hi = GS == 128 ? *reinterpret_cast<const v4i*>(base + 1024 + lane * 16) : v4i{0, 0, 0, 0};
-        af[l] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      }
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const int j = mt * NT + nt, cur = j & 1;
-#pragma unroll
-        for (int l = 0; l < 3; ++l)
-          acc[cur][l] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              af[l], bf[nt], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
-        if (j > 0) {
-          const int pm = (j - 1) / NT, pn = (j - 1) % NT;
-          WQBMM_PF_EPILOGUE(pm, pn, acc[cur ^ 1]);
-        }
-      }
-    }
-    {
-      constexpr int jl = MT * NT - 1;
-      WQBMM_PF_EPILOGUE(jl / NT, jl % NT, acc[jl & 1]);
-    }
-
-    if (more) WQBMM_PF_STORE(st ^ 1);
+  for (int g = g_begin; g < g_end; g += 2) {
+    if (g + 1 < g_end) WQBMM_DMA(g + 1, sA1, sB1, sAm1, sSc1);
+    WQBMM_COMPUTE(sA0, sB0, sAm0, sSc0, g);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (g + 1 >= g_end) break;
+    if (g + 2 < g_end) WQBMM_DMA(g + 2, sA0, sB0, sAm0, sSc0);
+    WQBMM_COMPUTE(sA1, sB1, sAm1, sSc1, g + 1);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
-#undef WQBMM_PF_LOAD
-#undef WQBMM_PF_STORE
+#undef WQBMM_COMPUTE
 #undef WQBMM_PF_EPILOGUE
+#undef WQBMM_DMA
 
   if constexpr (!YINT) {
 #pragma unroll
