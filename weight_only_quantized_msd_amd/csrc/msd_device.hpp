@@ -97,11 +97,27 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
+// Round half to even of |t| < 2^22 with the 1.5*2^23 trick: u = t + kMagic
+// lands where the float spacing is 1, so the (round-to-nearest-even) sum
+// holds rint(t) in its low mantissa bits -- its low byte is rint(t) as a
+// two's-complement int8 -- and u - kMagic is rint(t) exactly (kMagic is even,
+// so ties go to the even integer as with rintf).
+constexpr float kMagic = 12582912.0f;
+
+// Low bytes of four dwords -> one dword (byte j from x_j): three v_perm_b32
+// (selector 0x0c gives a zero byte).
+__device__ __forceinline__ uint32_t pack_low_bytes(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3) {
+  const uint32_t p01 = __builtin_amdgcn_perm(x1, x0, 0x0c0c0400u);   // x0.b0 x1.b0 0 0
+  const uint32_t p23 = __builtin_amdgcn_perm(x3, x2, 0x0c0c0400u);   // x2.b0 x3.b0 0 0
+  return __builtin_amdgcn_perm(p23, p01, 0x05040100u);               // x0.b0 x1.b0 x2.b0 x3.b0
+}
+
 // Steps 1-8 for 8 consecutive elements of one row (one 16-byte fp16 chunk).
 // The group's GS elements are held by GS/8 consecutive, aligned lanes; every
 // lane of the wave must call this (the max is a cross-lane reduction).
 // Out: the 8 levels of each of A1..A3 packed as int8 bytes in two dwords each,
-// and the group's A_max (step 1: rowMax(|A_group|), exact in fp32).
+// and the group's A_max (step 1: rowMax(|A_group|), exact in fp32).  The
+// arithmetic is msd_expand_f's, with each rint done by the kMagic sum.
 template <int GS>
 __device__ __forceinline__ void msd_decompose8(const uint4 xv, uint32_t (&lv)[3][2], float& amax) {
   const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
@@ -119,14 +135,24 @@ __device__ __forceinline__ void msd_decompose8(const uint4 xv, uint32_t (&lv)[3]
   for (int l = 0; l < 3; ++l) lv[l][0] = lv[l][1] = 0u;
   if (amax > 0.0f) {
     const float rcp = msd_recip(amax);
+    uint32_t u[3][8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      int A1, A2, A3;
-      msd_expand(a[i], amax, rcp, A1, A2, A3);
-      const int sh = 8 * (i & 3);
-      lv[0][i >> 2] |= (uint32_t)(A1 & 0xff) << sh;
-      lv[1][i >> 2] |= (uint32_t)(A2 & 0xff) << sh;
-      lv[2][i >> 2] |= (uint32_t)(A3 & 0xff) << sh;
+#pragma clang fp contract(off)
+      const float t1 = msd_div(kF1 * a[i], amax, rcp);
+      const float u1 = t1 + kMagic;
+      const float t2 = (t1 - (u1 - kMagic)) * kF2;
+      const float u2 = t2 + kMagic;
+      const float t3 = (t2 - (u2 - kMagic)) * kF2;
+      const float u3 = t3 + kMagic;
+      u[0][i] = __float_as_uint(u1);
+      u[1][i] = __float_as_uint(u2);
+      u[2][i] = __float_as_uint(u3);
+    }
+#pragma unroll
+    for (int l = 0; l < 3; ++l) {
+      lv[l][0] = pack_low_bytes(u[l][0], u[l][1], u[l][2], u[l][3]);
+      lv[l][1] = pack_low_bytes(u[l][4], u[l][5], u[l][6], u[l][7]);
     }
   }
 }

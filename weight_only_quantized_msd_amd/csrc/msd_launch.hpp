@@ -29,13 +29,14 @@ hipError_t launch_prepass(const void* x, int gs, int64_t M, int64_t K, int8_t* a
                           float* a_max, hipStream_t stream);
 
 // Prefill path (any M): a preparation kernel writes the MFMA operand tiles
-// (the three levels of x and the tiled weights, as fp8 e4m3, plus A_max), then
-// the GEMM contracts them and applies steps 10-11.
+// (the three levels of x and the tiled weights, as FP6 e2m3, plus A_max),
+// then the GEMM contracts them and applies steps 10-11.
 struct PrefillLayout {
-  int64_t mpad;        // rows padded to a multiple of 16
-  size_t a_bytes;      // level tiles of x: 3 * mpad * K
+  int64_t mpad;        // rows padded to a multiple of 128
+  int64_t npad;        // columns padded to a multiple of 128
+  size_t a_bytes;      // level tiles of x: 3 * (mpad/16) * G tiles of 1536 bytes
   size_t amax_bytes;   // A_max, [group][row] fp32
-  size_t b_bytes;      // weight tiles: K * N
+  size_t b_bytes;      // weight tiles: (npad/16) * G tiles of 1536 bytes
 };
 PrefillLayout prefill_layout(int gs, int64_t M, int64_t K, int64_t N);
 
