@@ -112,48 +112,67 @@ __device__ __forceinline__ uint32_t pack_low_bytes(uint32_t x0, uint32_t x1, uin
   return __builtin_amdgcn_perm(p23, p01, 0x05040100u);               // x0.b0 x1.b0 x2.b0 x3.b0
 }
 
+// Maximum over WIDTH (8 or 16) consecutive, aligned lanes of non-negative
+// float bit patterns, as unsigned integers (for non-negative finite floats the
+// order of the bit patterns is the order of the values, and an integer max
+// needs no NaN canonicalisation): DPP exchanges as in group_max.
+template <int WIDTH>
+__device__ __forceinline__ uint32_t group_max_bits(uint32_t v) {
+  static_assert(WIDTH == 8 || WIDTH == 16, "group of 8 or 16 lanes");
+  auto dpp = [](uint32_t x, auto ctrl) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, decltype(ctrl)::value, 0xf, 0xf, false);
+  };
+  v = max(v, dpp(v, std::integral_constant<int, 0xB1>{}));    // lane ^ 1
+  v = max(v, dpp(v, std::integral_constant<int, 0x4E>{}));    // lane ^ 2
+  v = max(v, dpp(v, std::integral_constant<int, 0x141>{}));   // row_half_mirror
+  if constexpr (WIDTH == 16) v = max(v, dpp(v, std::integral_constant<int, 0x140>{}));  // row_mirror
+  return v;
+}
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
 // Steps 1-8 for 8 consecutive elements of one row (one 16-byte fp16 chunk).
 // The group's GS elements are held by GS/8 consecutive, aligned lanes; every
 // lane of the wave must call this (the max is a cross-lane reduction).
 // Out: the 8 levels of each of A1..A3 packed as int8 bytes in two dwords each,
-// and the group's A_max (step 1: rowMax(|A_group|), exact in fp32).  The
-// arithmetic is msd_expand_f's, with each rint done by the kMagic sum.
+// and the group's A_max (step 1: rowMax(|A_group|), exact: the maximum is
+// taken over the fp16 magnitudes' bit patterns and widened once).  The
+// arithmetic is msd_expand_f's, with each rint done by the kMagic sum;
+// tmp = 7.49*a is one fused multiply-add with a zero addend straight from
+// the fp16 value (v_fma_mix_f32: exact widening, one rounding of the
+// product).  A zero group (A_max = 0, so every a is +-0) takes a zero
+// reciprocal, which makes every quotient 0 and every level 0, as the guard
+// of the definition requires.
 template <int GS>
 __device__ __forceinline__ void msd_decompose8(const uint4 xv, uint32_t (&lv)[3][2], float& amax) {
   const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
-  float a[8];
+  const u16x2 m01 = __builtin_elementwise_max(__builtin_bit_cast(u16x2, xw[0] & 0x7fff7fffu),
+                                              __builtin_bit_cast(u16x2, xw[1] & 0x7fff7fffu));
+  const u16x2 m23 = __builtin_elementwise_max(__builtin_bit_cast(u16x2, xw[2] & 0x7fff7fffu),
+                                              __builtin_bit_cast(u16x2, xw[3] & 0x7fff7fffu));
+  const u16x2 mh = __builtin_elementwise_max(m01, m23);
+  const uint32_t mb = group_max_bits<GS / 8>(max((uint32_t)mh.x, (uint32_t)mh.y));
+  amax = half_bits_to_float(mb);
+  const float rcp = amax > 0.0f ? msd_recip(amax) : 0.0f;
+  uint32_t u[3][8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    a[2 * i] = half_bits_to_float(xw[i] & 0xffffu);
-    a[2 * i + 1] = half_bits_to_float(xw[i] >> 16);
-  }
-  float m = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(a[i]));
-  amax = group_max<GS / 8>(m);
-#pragma unroll
-  for (int l = 0; l < 3; ++l) lv[l][0] = lv[l][1] = 0u;
-  if (amax > 0.0f) {
-    const float rcp = msd_recip(amax);
-    uint32_t u[3][8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 8; ++i) {
 #pragma clang fp contract(off)
-      const float t1 = msd_div(kF1 * a[i], amax, rcp);
-      const float u1 = t1 + kMagic;
-      const float t2 = (t1 - (u1 - kMagic)) * kF2;
-      const float u2 = t2 + kMagic;
-      const float t3 = (t2 - (u2 - kMagic)) * kF2;
-      const float u3 = t3 + kMagic;
-      u[0][i] = __float_as_uint(u1);
-      u[1][i] = __float_as_uint(u2);
-      u[2][i] = __float_as_uint(u3);
-    }
+    const _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)(i & 1 ? xw[i >> 1] >> 16 : xw[i >> 1] & 0xffffu));
+    const float t1 = msd_div(__builtin_fmaf((float)h, kF1, 0.0f), amax, rcp);
+    const float u1 = t1 + kMagic;
+    const float t2 = (t1 - (u1 - kMagic)) * kF2;
+    const float u2 = t2 + kMagic;
+    const float t3 = (t2 - (u2 - kMagic)) * kF2;
+    const float u3 = t3 + kMagic;
+    u[0][i] = __float_as_uint(u1);
+    u[1][i] = __float_as_uint(u2);
+    u[2][i] = __float_as_uint(u3);
+  }
 #pragma unroll
-    for (int l = 0; l < 3; ++l) {
-      lv[l][0] = pack_low_bytes(u[l][0], u[l][1], u[l][2], u[l][3]);
-      lv[l][1] = pack_low_bytes(u[l][4], u[l][5], u[l][6], u[l][7]);
-    }
+  for (int l = 0; l < 3; ++l) {
+    lv[l][0] = pack_low_bytes(u[l][0], u[l][1], u[l][2], u[l][3]);
+    lv[l][1] = pack_low_bytes(u[l][4], u[l][5], u[l][6], u[l][7]);
   }
 }
 
