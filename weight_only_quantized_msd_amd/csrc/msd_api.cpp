@@ -161,15 +161,15 @@ wqbmm_status run_prefill(int dev, const void* x, const void* w, const void* scal
                          int32_t* y_int, int stage, hipStream_t stream) {
   const wqbmm::PrefillLayout L = wqbmm::prefill_layout((int)gs, M, K, N);
   const size_t a_off = 0;
-  const size_t amax_off = round_up(L.a_bytes, 256);
-  const size_t b_off = amax_off + round_up(L.amax_bytes, 256);
+  const size_t q_off = round_up(L.a_bytes, 256);
+  const size_t b_off = q_off + round_up(L.q_bytes, 256);
   const size_t total = b_off + round_up(L.b_bytes, 256);
   uint64_t* accum = nullptr;
   uint8_t* scratch = nullptr;
   wqbmm_status st = get_workspace(dev, stream, 0, total, &accum, &scratch);
   if (st != WQBMM_OK) return st;
   uint8_t* a_t = scratch + a_off;
-  float* amax_t = reinterpret_cast<float*>(scratch + amax_off);
+  float* q_t = reinterpret_cast<float*>(scratch + q_off);
   uint8_t* b_t = scratch + b_off;
   {
     std::lock_guard<std::mutex> lk(g_mu);
@@ -182,10 +182,10 @@ wqbmm_status run_prefill(int dev, const void* x, const void* w, const void* scal
     }
   }
   if (stage != 2) {
-    st = launch_status(wqbmm::launch_prefill_prep(x, w, (int)gs, M, K, N, L, a_t, amax_t, b_t, stream));
+    st = launch_status(wqbmm::launch_prefill_prep(x, w, (int)gs, M, K, N, L, a_t, q_t, b_t, stream));
     if (st != WQBMM_OK || stage == 1) return st;
   }
-  return launch_status(wqbmm::launch_prefill_gemm(a_t, amax_t, b_t, scale, (int)gs, M, K, N, L,
+  return launch_status(wqbmm::launch_prefill_gemm(a_t, q_t, b_t, scale, (int)gs, M, K, N, L,
                                                   g_begin, g_end, y, y_int, stream));
 }
 

@@ -29,24 +29,26 @@ hipError_t launch_prepass(const void* x, int gs, int64_t M, int64_t K, int8_t* a
                           float* a_max, hipStream_t stream);
 
 // Prefill path (any M): a preparation kernel writes the MFMA operand tiles
-// (the three levels of x and the tiled weights, as FP6 e2m3, plus A_max),
-// then the GEMM contracts them and applies steps 10-11.
+// (the three levels of x and the tiled weights, as FP6 e2m3) and the rows'
+// step-10 level weights (A_max * w_l, fp32), then the GEMM contracts them and
+// applies steps 10-11.
 struct PrefillLayout {
   int64_t mpad;        // rows padded to a multiple of 128
-  int64_t npad;        // columns padded to a multiple of 128
+  int64_t bn;          // columns per GEMM workgroup tile: 128 or 256
+  int64_t npad;        // columns padded to a multiple of bn
   size_t a_bytes;      // level tiles of x: 3 * (mpad/16) * G tiles of 1536 bytes
-  size_t amax_bytes;   // A_max, [group][row] fp32
+  size_t q_bytes;      // level weights, [group][row block][level][128] fp32
   size_t b_bytes;      // weight tiles: (npad/16) * G tiles of 1536 bytes
 };
 PrefillLayout prefill_layout(int gs, int64_t M, int64_t K, int64_t N);
 
 hipError_t launch_prefill_prep(const void* x, const void* w, int gs, int64_t M, int64_t K,
-                               int64_t N, const PrefillLayout& L, uint8_t* a_t, float* amax_t,
+                               int64_t N, const PrefillLayout& L, uint8_t* a_t, float* q_t,
                                uint8_t* b_t, hipStream_t stream);
 
 // y_int == nullptr: groups [g_begin, g_end) are combined into y (fp16 [M][N]);
 // otherwise they are stored as int32 Y_int.
-hipError_t launch_prefill_gemm(const uint8_t* a_t, const float* amax_t, const uint8_t* b_t,
+hipError_t launch_prefill_gemm(const uint8_t* a_t, const float* q_t, const uint8_t* b_t,
                                const void* scale, int gs, int64_t M, int64_t K, int64_t N,
                                const PrefillLayout& L, int64_t g_begin, int64_t g_end, void* y,
                                int32_t* y_int, hipStream_t stream);

@@ -38,53 +38,51 @@
 //   [lane][dwords 0-3] (1 KB) then [lane][dwords 4-5] (512 bytes), 1536
 //   bytes, read by one conflict-free ds_read_b128 and one ds_read_b64.
 //   A_t: [row block of 128][group][level][row tile 0..7][tile]
-//   B_t: [column block of 128][group][column tile 0..7][tile]
+//   B_t: [column block of BN][group][column tile 0..BN/16-1][tile]
+//   Q_t: [group][row block][level][128 rows] fp32: A_max * w_l, the row's
+//        step-10 weight of level l (w_l = 1/7.49, 1/(7.49*14.98),
+//        1/(7.49*14.98^2)), formed once per (row, group)
 //   Rows beyond M and columns beyond N hold zeros (written by the prep
 //   kernel), so the operands of one group of a workgroup tile are two
-//   contiguous runs: 36 KB of A and 12 KB of B.
-//   A_max_t: [group][row]  fp32, rows padded to 128.
+//   contiguous runs: 36 KB of A and BN/16 * 1.5 KB of B.
 //
-// GEMM tiling: workgroup tile BM=128 rows x BN=128 columns, 8 waves as 4
-// (along M) x 2 (along N), wave tile 32 rows x 64 columns = 2x4 MFMA tiles of
-// 16x16, times 3 levels: each wave reuses its three A operands across its 4
-// column tiles, which keeps the LDS reads per MFMA low (the A operand is
-// three times the bytes of an ordinary GEMM's).  LDS holds one group's A
-// (3 x 8 tiles) and B (8 tiles), double-buffered; the next group is copied
-// global -> LDS directly (global_load_lds, 16 bytes per lane, no staging
-// registers; each wave copies an equal share of the chunks, the last wave
-// also the group's A_max and scale slices) while the current group is
-// computed, one barrier per group.  Within a group a wave walks its 8 output
-// tiles: a tile's 3 MFMAs are issued, then the fp32 combine of the previous
-// tile, so the combine never waits for the MFMA it follows.  The combine
-// (4 VALU per output per group) does not run concurrently with MFMA on the
-// same SIMD -- it is issued between MFMAs -- so it adds to the MFMA time;
-// two waves per SIMD hide part of it.  The MFMA results stay in VGPRs.
-// Tile order: the linear workgroup id is remapped so that each XCD
-// (workgroups are dealt to the 8 XCDs round-robin) gets a contiguous range of
-// row-major tiles, keeping the A rows its tiles share in that XCD's L2.  The
-// mapping affects speed only.
+// GEMM tiling: workgroup tile BM = 128 rows x BN = 256 (or 128) columns, 8
+// waves as 2 (along M) x 4 (along N), wave tile 64 rows x BN/4 columns =
+// 4 x NT MFMA tiles of 16x16, times 3 levels.  A wave holds its NT B
+// operands for the group and walks its row tiles: per row tile the 3 level
+// operands and the rows' weights, then per column tile 3 MFMAs, with the
+// fp32 combine of the previous output tile interleaved (4 VALU per output
+// and group: three for the levels, one for the scale and the running sum).
+// Per group a workgroup reads 36 KB + BN/16 * 1.5 KB of operands; LDS holds
+// one group's operands, weights and scales, double-buffered: the next group
+// is copied global -> LDS directly (global_load_lds, no staging registers;
+// each wave copies an equal share of 1 KB pieces, and the weights and
+// scales in 4-byte lanes) while the current group is computed, one barrier
+// per group.  The MFMA results stay in VGPRs.
+// Tile order: workgroups are dealt to the 8 XCDs round-robin; the linear
+// id is remapped so that each XCD gets a contiguous range of tiles, taken in
+// bands of 4 row blocks (column-major within a band), so that the tiles an
+// XCD runs together share 4 A runs and few B runs in its L2.  The mapping
+// affects speed only.
 #include "msd_device.hpp"
 #include "msd_launch.hpp"
 
 namespace wqbmm {
 namespace pf {
 constexpr int BM = 128;
-constexpr int BN = 128;
-constexpr int WAVES_N = 2;     // waves along N
-constexpr int WAVES_M = 4;     // waves along M
+constexpr int WAVES_M = 2;     // waves along M
+constexpr int WAVES_N = 4;     // waves along N
 constexpr int WAVES = WAVES_M * WAVES_N;
 constexpr int THREADS = 64 * WAVES;
-constexpr int WM = BM / WAVES_M;   // 32 rows per wave
-constexpr int WN = BN / WAVES_N;   // 64 columns per wave
-constexpr int MT = WM / 16;    // 2 row tiles per wave
-constexpr int NT = WN / 16;    // 4 column tiles per wave
+constexpr int WM = BM / WAVES_M;   // 64 rows per wave
+constexpr int MT = WM / 16;    // 4 row tiles per wave
 constexpr int RT = BM / 16;    // 8 row tiles per block
-constexpr int CT = BN / 16;    // 8 column tiles per block
 constexpr int TILE = 1536;     // bytes of one operand tile (16 x 128 k, e2m3)
 constexpr int TILE_LO = 1024;  // its [lane][dwords 0-3] part
 constexpr int A_GROUP = 3 * RT * TILE;   // one group of a row block: 36 KB
-constexpr int B_GROUP = CT * TILE;       // one group of a column block: 12 KB
+constexpr int Q_GROUP = 3 * BM * 4;      // level weights of a row block: 1.5 KB
 constexpr int NXCD = 8;
+constexpr int BAND = 4;        // row blocks per band of the tile order
 }  // namespace pf
 
 typedef int v2i __attribute__((ext_vector_type(2)));
@@ -110,8 +108,14 @@ __device__ __forceinline__ float sfield(int32_t v, int off, int width) {
 }
 
 // 32 exactly representable values -> six dwords of e2m3 (value / div).
+// The instruction writes its six result dwords while it still reads its two
+// 16-dword sources, so the result must not overlap them: the compiler's
+// builtin can be given a destination inside a source (which corrupts the
+// packed values), so it is emitted here with an early-clobber destination.
 __device__ __forceinline__ v6i pack_e2m3(const v16f& u, const v16f& v, float div) {
-  return __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(u, v, div);
+  v6i r;
+  asm volatile("v_cvt_scalef32_2xpk16_fp6_f32 %0, %1, %2, %3" : "=&v"(r) : "v"(u), "v"(v), "v"(div));
+  return r;
 }
 
 // One packed operand lane -> its tile slot: dwords 0-3 at 16*slot, dwords 4-5
@@ -126,19 +130,18 @@ __device__ __forceinline__ void store_operand(uint8_t* tile, int slot, const v6i
 // elements.  Lane l takes row l/4 and, with kq = l%4, the elements of operand
 // lane 16*kq + row (u: k = 16*kq + j, v: k = 64 + 16*kq + j), so a group's
 // maximum is a 4-lane reduction and the wave's stores fill one whole tile per
-// level.
+// level; the rows' level weights A_max * w_l go to Q_t.
 // Waves [xwaves, ...): one 16-byte tiled-weight chunk per thread (column
 // tiles up to the padded width; those beyond N become zeros), converted in
-// place into operand lane l of its column tile.
+// place into operand lane l of its column tile (column blocks of BN).
 template <int GS>
 __global__ __launch_bounds__(256) void msd_prep_kernel(const uint16_t* __restrict__ x,
                                                        const uint8_t* __restrict__ wt, int M,
-                                                       int Mpad, int K, int N, int Npad,
+                                                       int Mpad, int K, int N, int Npad, int BN,
                                                        int64_t xwaves, uint8_t* __restrict__ a_t,
-                                                       float* __restrict__ amax_t,
+                                                       float* __restrict__ q_t,
                                                        uint8_t* __restrict__ b_t) {
   using namespace pf;
-  constexpr int EPL = GS / 4;                        // real elements per lane: 32 or 16
   const int G = K / GS;
   const int lane = threadIdx.x & 63;
   const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -188,7 +191,10 @@ __global__ __launch_bounds__(256) void msd_prep_kernel(const uint16_t* __restric
       uint8_t* tile = a_t + ((((int64_t)rb * G + g) * 3 + l) * RT + rt) * TILE;
       store_operand(tile, 16 * kq + r, pack_e2m3(lv[l][0], lv[l][1], 1.0f));
     }
-    if (kq == 0) amax_t[(int64_t)g * Mpad + m] = amax;
+    if (kq < 3) {                                    // lanes kq = 0, 1, 2: level weight kq of row m
+      const float w = kq == 0 ? kE1 : (kq == 1 ? kE2 : kE3);
+      q_t[(((int64_t)g * (Mpad / BM) + rb) * 3 + kq) * BM + (m % BM)] = amax * w;
+    }
     return;
   }
   // tiled weights: chunk t = (nt * KB + kb) * 64 + lane
@@ -210,6 +216,7 @@ __global__ __launch_bounds__(256) void msd_prep_kernel(const uint16_t* __restric
       const int j = i % 8;
       w[st][i] = sfield(dw[2 * st + i / 8], j < 4 ? 8 * j : 8 * (j - 4) + 4, 4);
     }
+  const int CT = BN / 16;
   const int cb = nt / CT, ct = nt % CT;
   if constexpr (GS == 128) {
     uint8_t* tile = b_t + (((int64_t)cb * G + kb) * CT + ct) * TILE;
@@ -229,17 +236,32 @@ __global__ __launch_bounds__(256) void msd_prep_kernel(const uint16_t* __restric
 }
 
 // ---------------------------------------------------------------- GEMM kernel
-template <int GS, bool YINT>
+// One operand (six dwords) of lane `lane` from an LDS tile, as the MFMA's
+// eight-dword argument (the last two are unused by the FP6 form).
+__device__ __forceinline__ v8i lds_operand(const uint8_t* tile, int lane) {
+  const v4i lo = *reinterpret_cast<const v4i*>(tile + lane * 16);
+  const v2i hi = *reinterpret_cast<const v2i*>(tile + pf::TILE_LO + lane * 8);
+  return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], 0, 0};
+}
+
+template <int GS, int BN, bool YINT>
 __global__ __launch_bounds__(pf::THREADS, 1) void msd_gemm_kernel(
-    const uint8_t* __restrict__ a_t, const float* __restrict__ amax_t,
+    const uint8_t* __restrict__ a_t, const float* __restrict__ q_t,
     const uint8_t* __restrict__ b_t, const uint16_t* __restrict__ scale, int M, int Mpad, int K,
     int N, int g_begin, int g_end, int mblocks, int nblocks, uint16_t* __restrict__ y,
     int32_t* __restrict__ y_int) {
   using namespace pf;
-  constexpr int A_KB = A_GROUP / 1024;                 // 1 KB copies per group: 36
-  constexpr int B_KB = B_GROUP / 1024;                 // 12
-  constexpr int CPW = (A_KB + B_KB) / WAVES;           // copies per wave: 6
-  static_assert((A_KB + B_KB) % WAVES == 0 && A_KB % CPW == 0, "copy split");
+  constexpr int CT = BN / 16;                          // column tiles per block
+  constexpr int NT = CT / WAVES_N;                     // column tiles per wave: 4 or 2
+  constexpr int WN = NT * 16;                          // columns per wave
+  constexpr int B_GROUP = CT * TILE;                   // one group of a column block
+  constexpr int A_KB = A_GROUP / 1024;                 // 36 pieces of 1 KB
+  constexpr int PIECES = A_KB + B_GROUP / 1024;        // 60 or 48
+  constexpr int CPW = (PIECES + WAVES - 1) / WAVES;    // pieces per wave: 8 or 6
+  constexpr int QW = Q_GROUP / 256;                    // 256-byte copies of the weights: 6
+  constexpr int SW = BN * 2 / 256;                     // 256-byte copies of the scales: 2 or 1
+  static_assert(QW + SW <= WAVES, "one small copy per wave");
+  static_assert(B_GROUP % 1024 == 0, "whole pieces");
 
   // Two named buffers (not one array indexed by the parity of the group) so
   // that the copies into one and the reads of the other are visibly disjoint.
@@ -247,10 +269,10 @@ __global__ __launch_bounds__(pf::THREADS, 1) void msd_gemm_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t sA1[A_GROUP];
   __shared__ __attribute__((aligned(16))) uint8_t sB0[B_GROUP];
   __shared__ __attribute__((aligned(16))) uint8_t sB1[B_GROUP];
-  __shared__ __attribute__((aligned(16))) float sAm0[BM];
-  __shared__ __attribute__((aligned(16))) float sAm1[BM];
-  __shared__ __attribute__((aligned(16))) uint16_t sSc0[BN];
-  __shared__ __attribute__((aligned(16))) uint16_t sSc1[BN];
+  __shared__ __attribute__((aligned(16))) float sQ0[3 * BM];
+  __shared__ __attribute__((aligned(16))) float sQ1[3 * BM];
+  __shared__ __attribute__((aligned(16))) uint16_t sS0[BN];
+  __shared__ __attribute__((aligned(16))) uint16_t sS1[BN];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -258,160 +280,166 @@ __global__ __launch_bounds__(pf::THREADS, 1) void msd_gemm_kernel(
   const int wm = wave / WAVES_N;   // rows WM*wm of the tile
   const int wn = wave % WAVES_N;   // columns WN*wn of the tile
 
+  // Tile order: XCD x (= id % 8) runs the contiguous range of tiles
+  // [x * total/8, (x+1) * total/8); tiles are numbered in bands of BAND row
+  // blocks, column-major within a band.
   const int total = mblocks * nblocks;
   int t = blockIdx.x;
   if (total % NXCD == 0) t = (blockIdx.x % NXCD) * (total / NXCD) + blockIdx.x / NXCD;
-  const int rb = t / nblocks, cb = t % nblocks;
+  const int band_tiles = BAND * nblocks;
+  const int band = t / band_tiles;
+  const int in_band = t % band_tiles;
+  const int band_rows = min(BAND, mblocks - band * BAND);
+  const int rb = band * BAND + in_band % band_rows;
+  const int cb = in_band / band_rows;
   const int m0 = rb * BM;
   const int n0 = cb * BN;
   const int G = K / GS;
+  const int RB = Mpad / BM;
 
-  // This wave's share of a group's copies: waves [0, A_KB/CPW) copy 1 KB
-  // pieces of the block's A run, the others pieces of its B run.
-  const bool a_wave = wave * CPW < A_KB;
-  const int piece = a_wave ? wave * CPW : wave * CPW - A_KB;
-  const uint8_t* dma_src = (a_wave ? a_t + (int64_t)rb * G * A_GROUP : b_t + (int64_t)cb * G * B_GROUP) +
-                           piece * 1024 + lane * 16;
-  const int64_t dma_stride = a_wave ? A_GROUP : B_GROUP;
-  const int am_row0 = m0 + lane, am_row1 = m0 + 64 + lane;   // < Mpad (a multiple of BM)
-  const int sc_col = min(n0 + 2 * lane, N - 2);
-
-  // Group g_'s operands -> LDS, by DMA (global_load_lds, 16 bytes per lane:
+  // Group g_'s operands -> LDS by DMA (global_load_lds, 16 bytes per lane:
   // lane i's bytes land at the destination + 16*i, so a 1 KB piece keeps its
-  // layout).  A_max (fp32) and the scales (fp16 pairs) go 4 bytes per lane.
-  // (The 4-byte copies take byte pointers: typed float pointers made the
-  // compiler crash in its SGPR-copy pass.)
-#define WQBMM_DMA(g_, SA_, SB_, SAM_, SSC_)                                                        \
-  do {                                                                                             \
-    const uint8_t* src_ = dma_src + (int64_t)(g_) * dma_stride;                                    \
-    uint8_t* dst_ = (a_wave ? (SA_) : (SB_)) + piece * 1024;                                       \
-    _Pragma("unroll") for (int c = 0; c < CPW; ++c)                                                \
-      __builtin_amdgcn_global_load_lds(src_ + c * 1024, dst_ + c * 1024, 16, 0, 0);                \
-    if (wave == WAVES - 1) {                                                                       \
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(amax_t) + ((int64_t)(g_) * Mpad + am_row0) * 4, reinterpret_cast<uint8_t*>(SAM_), 4, 0, 0);  \
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(amax_t) + ((int64_t)(g_) * Mpad + am_row1) * 4, reinterpret_cast<uint8_t*>(SAM_) + 256, 4, 0, 0); \
-      if constexpr (!YINT)                                                                         \
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(scale) + ((int64_t)(g_) * N + sc_col) * 2, reinterpret_cast<uint8_t*>(SSC_), 4, 0, 0);     \
-    }                                                                                              \
-  } while (0)
-
-  // One operand (six dwords) of lane `lane` from an LDS tile, as the MFMA's
-  // eight-dword argument (the last two are unused by the FP6 form).
-#define WQBMM_OPERAND(TILE_PTR_)                                                                   \
-  __builtin_shufflevector(*reinterpret_cast<const v4i*>((TILE_PTR_) + lane * 16),                  \
-                          __builtin_shufflevector(*reinterpret_cast<const v2i*>((TILE_PTR_) + TILE_LO + lane * 8), \
-                                                  v2i{0, 0}, 0, 1, -1, -1),                         \
-                          0, 1, 2, 3, 4, 5, -1, -1)
-
-  // Steps 10-11 for one 16x16 output tile (row tile PM_, column tile PN_)
-  // from its three level accumulators ACC_; or the Y_int export.
-#define WQBMM_PF_EPILOGUE(PM_, PN_, ACC_, G_)                                                      \
-  do {                                                                                             \
-    if constexpr (YINT) {                                                                          \
-      const int64_t gi = (G_) - g_begin;                                                           \
-      const int n = n0 + wn * WN + (PN_) * 16 + (lane & 15);                                       \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                              \
-        const int m = m0 + wm * WM + (PM_) * 16 + (lane >> 4) * 4 + i;                             \
-        if (m < M && n < N) {                                                                      \
-          _Pragma("unroll") for (int l = 0; l < 3; ++l)                                            \
-              y_int[((gi * 3 + l) * M + m) * (int64_t)N + n] = (int32_t)(ACC_)[l][i];              \
-        }                                                                                          \
-      }                                                                                            \
-    } else {                                                                                       \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                              \
-        float tt = (ACC_)[0][i] * q[PM_][i][0];                                                    \
-        tt = __builtin_fmaf((ACC_)[1][i], q[PM_][i][1], tt);                                       \
-        tt = __builtin_fmaf((ACC_)[2][i], q[PM_][i][2], tt);                                       \
-        yacc[PM_][PN_][i] = __builtin_fmaf(tt, sc[PN_], yacc[PM_][PN_][i]);                        \
-      }                                                                                            \
-    }                                                                                              \
-  } while (0)
-
-  // One group from one buffer: the wave's 2 x 3 A operands stay in registers;
-  // per column tile, its B operand and 2 x 3 MFMAs, the combine of each
-  // output tile interleaved with the next tile's MFMAs.
-#define WQBMM_COMPUTE(SA_, SB_, SAM_, SSC_, G_)                                                    \
-  do {                                                                                             \
-    float q[MT][4][3], sc[NT];                                                                     \
-    if constexpr (!YINT) {                                                                         \
-      _Pragma("unroll") for (int nt = 0; nt < NT; ++nt)                                            \
-          sc[nt] = half_bits_to_float((SSC_)[wn * WN + nt * 16 + (lane & 15)]);                    \
-      _Pragma("unroll") for (int mt = 0; mt < MT; ++mt) {                                          \
-        const float4 a4 = *reinterpret_cast<const float4*>(&(SAM_)[wm * WM + mt * 16 + (lane >> 4) * 4]); \
-        const float am[4] = {a4.x, a4.y, a4.z, a4.w};                                              \
-        _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                            \
-          q[mt][i][0] = am[i] * kE1;                                                               \
-          q[mt][i][1] = am[i] * kE2;                                                               \
-          q[mt][i][2] = am[i] * kE3;                                                               \
-        }                                                                                          \
-      }                                                                                            \
-    }                                                                                              \
-    v8i af[MT][3];                                                                                 \
-    _Pragma("unroll") for (int mt = 0; mt < MT; ++mt)                                              \
-      _Pragma("unroll") for (int l = 0; l < 3; ++l)                                                \
-        af[mt][l] = WQBMM_OPERAND((SA_) + (l * RT + wm * MT + mt) * TILE);                         \
-    v4f acc[2][3];                                                                                 \
-    _Pragma("unroll") for (int nt = 0; nt < NT; ++nt) {                                            \
-      const v8i bf = WQBMM_OPERAND((SB_) + (wn * NT + nt) * TILE);                                 \
-      _Pragma("unroll") for (int mt = 0; mt < MT; ++mt) {                                          \
-        const int j = nt * MT + mt, cur = j & 1;                                                   \
-        _Pragma("unroll") for (int l = 0; l < 3; ++l)                                              \
-            acc[cur][l] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(                        \
-                af[mt][l], bf, v4f{0.f, 0.f, 0.f, 0.f}, 2, 2, 0, kScaleA, 0, kScaleB);             \
-        if (j > 0) {                                                                               \
-          const int pm = (j - 1) % MT, pn = (j - 1) / MT;                                          \
-          WQBMM_PF_EPILOGUE(pm, pn, acc[cur ^ 1], G_);                                             \
-        }                                                                                          \
-      }                                                                                            \
-    }                                                                                              \
-    {                                                                                              \
-      constexpr int jl = MT * NT - 1;                                                              \
-      WQBMM_PF_EPILOGUE(jl % MT, jl / MT, acc[jl & 1], G_);                                        \
-    }                                                                                              \
-  } while (0)
+  // layout).  Pieces [0, 36) are the block's A run, the rest its B run.  The
+  // level weights (fp32) and the scales (fp16 pairs) go 4 bytes per lane, one
+  // 256-byte copy per wave.  (The 4-byte copies take byte pointers: typed
+  // float pointers made the compiler crash in its SGPR-copy pass.)
+  const uint8_t* a_run = a_t + (int64_t)rb * G * A_GROUP;
+  const uint8_t* b_run = b_t + (int64_t)cb * G * B_GROUP;
+  const int sc_col = min(n0 + 2 * (wave - QW) * 64 + 2 * lane, N - 2);
+  auto dma = [&](int g_, uint8_t* sa, uint8_t* sb, float* sq, uint16_t* ss) {
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const int p = wave * CPW + c;                   // wave-uniform
+      if (p < PIECES) {
+        const uint8_t* src = p < A_KB ? a_run + (int64_t)g_ * A_GROUP + p * 1024
+                                      : b_run + (int64_t)g_ * B_GROUP + (p - A_KB) * 1024;
+        uint8_t* dst = p < A_KB ? sa + p * 1024 : sb + (p - A_KB) * 1024;
+        __builtin_amdgcn_global_load_lds(src + lane * 16, dst, 16, 0, 0);
+      }
+    }
+    if (wave < QW) {
+      const uint8_t* src = reinterpret_cast<const uint8_t*>(q_t) +
+                           ((int64_t)g_ * RB + rb) * Q_GROUP + wave * 256 + lane * 4;
+      __builtin_amdgcn_global_load_lds(src, reinterpret_cast<uint8_t*>(sq) + wave * 256, 4, 0, 0);
+    } else if (wave < QW + SW && !YINT) {
+      const uint8_t* src = reinterpret_cast<const uint8_t*>(scale) + ((int64_t)g_ * N + sc_col) * 2;
+      __builtin_amdgcn_global_load_lds(src, reinterpret_cast<uint8_t*>(ss) + (wave - QW) * 256, 4, 0, 0);
+    }
+  };
 
   float yacc[MT][NT][4];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+  for (int r = 0; r < MT; ++r)
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+    for (int c = 0; c < NT; ++c)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) yacc[mt][nt][i] = 0.0f;
+      for (int i = 0; i < 4; ++i) yacc[r][c][i] = 0.0f;
+
+  // Steps 10-11 for output tile (row tile PR, column tile PC) from its three
+  // level results; or the Y_int export.
+  auto epilogue = [&](int pr, int pc, const v4f (&a3)[3], const v4f (&qq)[3], const uint32_t (&sraw)[NT], int g_) {
+    if constexpr (YINT) {
+      const int64_t gi = g_ - g_begin;
+      const int n = n0 + wn * WN + pc * 16 + (lane & 15);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + wm * WM + pr * 16 + (lane >> 4) * 4 + i;
+        if (m < M && n < N) {
+#pragma unroll
+          for (int l = 0; l < 3; ++l)
+            y_int[((gi * 3 + l) * M + m) * (int64_t)N + n] = (int32_t)a3[l][i];
+        }
+      }
+    } else {
+      const float sc = half_bits_to_float(sraw[pc]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float tt = a3[0][i] * qq[0][i];
+        tt = __builtin_fmaf(a3[1][i], qq[1][i], tt);
+        tt = __builtin_fmaf(a3[2][i], qq[2][i], tt);
+        yacc[pr][pc][i] = __builtin_fmaf(tt, sc, yacc[pr][pc][i]);
+      }
+    }
+  };
+
+  // Steps 9-11 for one group from one buffer.  The wave keeps its NT B
+  // operands and its 4 x 3 level operands; per row tile it reads the rows'
+  // weights, and per output tile issues 3 MFMAs, then combines the previous
+  // output tile (so the combine never waits for the MFMA it follows).
+  auto compute = [&](const uint8_t* sa, const uint8_t* sb, const float* sq, const uint16_t* ss, int g_) {
+    v8i bf[NT];
+#pragma unroll
+    for (int c = 0; c < NT; ++c) bf[c] = lds_operand(sb + (wn * NT + c) * TILE, lane);
+    uint32_t sraw[NT];
+    if constexpr (!YINT) {
+#pragma unroll
+      for (int c = 0; c < NT; ++c) sraw[c] = ss[wn * WN + c * 16 + (lane & 15)];
+    }
+    v4f q[2][3];                 // weights of the current and the previous row tile
+    v4f acc[2][3];               // MFMA results of the current and the previous output tile
+    // Every operand register of the group is loaded before the first MFMA
+    // and none is reloaded within the group (a register read by an MFMA is
+    // not the destination of a later load until the group's barrier).
+    v8i af[MT][3];
+#pragma unroll
+    for (int r = 0; r < MT; ++r)
+#pragma unroll
+      for (int l = 0; l < 3; ++l) af[r][l] = lds_operand(sa + (l * RT + wm * MT + r) * TILE, lane);
+#pragma unroll
+    for (int r = 0; r < MT; ++r) {
+      const int rt = wm * MT + r;
+      if constexpr (!YINT) {
+#pragma unroll
+        for (int l = 0; l < 3; ++l)
+          q[r & 1][l] = *reinterpret_cast<const v4f*>(sq + l * BM + rt * 16 + 4 * (lane >> 4));
+      }
+#pragma unroll
+      for (int c = 0; c < NT; ++c) {
+        const int j = r * NT + c, cur = j & 1;
+#pragma unroll
+        for (int l = 0; l < 3; ++l)
+          acc[cur][l] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              af[r][l], bf[c], v4f{0.f, 0.f, 0.f, 0.f}, 2, 2, 0, kScaleA, 0, kScaleB);
+        if (j > 0) {
+          const int pr = (j - 1) / NT, pc = (j - 1) % NT;
+          epilogue(pr, pc, acc[cur ^ 1], q[pr & 1], sraw, g_);
+        }
+      }
+    }
+    constexpr int jl = MT * NT - 1;
+    epilogue(jl / NT, jl % NT, acc[jl & 1], q[(jl / NT) & 1], sraw, g_);
+  };
 
   // Buffer 0 holds the even-indexed groups of the range, buffer 1 the odd
   // ones.  While a group is computed from one buffer, the next group is
   // copied into the other; each wave waits for its own copies, and the
   // barrier then publishes all of them and frees the buffer just read.
-  WQBMM_DMA(g_begin, sA0, sB0, sAm0, sSc0);
+  dma(g_begin, sA0, sB0, sQ0, sS0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int g = g_begin; g < g_end; g += 2) {
-    if (g + 1 < g_end) WQBMM_DMA(g + 1, sA1, sB1, sAm1, sSc1);
-    WQBMM_COMPUTE(sA0, sB0, sAm0, sSc0, g);
+    if (g + 1 < g_end) dma(g + 1, sA1, sB1, sQ1, sS1);
+    compute(sA0, sB0, sQ0, sS0, g);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (g + 1 >= g_end) break;
-    if (g + 2 < g_end) WQBMM_DMA(g + 2, sA0, sB0, sAm0, sSc0);
-    WQBMM_COMPUTE(sA1, sB1, sAm1, sSc1, g + 1);
+    if (g + 2 < g_end) dma(g + 2, sA0, sB0, sQ0, sS0);
+    compute(sA1, sB1, sQ1, sS1, g + 1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
-#undef WQBMM_COMPUTE
-#undef WQBMM_PF_EPILOGUE
-#undef WQBMM_OPERAND
-#undef WQBMM_DMA
 
   if constexpr (!YINT) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int r = 0; r < MT; ++r)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int m = m0 + wm * WM + mt * 16 + (lane >> 4) * 4 + i;
+        const int m = m0 + wm * WM + r * 16 + (lane >> 4) * 4 + i;
         if (m >= M) continue;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const int n = n0 + wn * WN + nt * 16 + (lane & 15);
-          if (n < N) y[(int64_t)m * N + n] = float_to_half_bits(yacc[mt][nt][i]);
+        for (int c = 0; c < NT; ++c) {
+          const int n = n0 + wn * WN + c * 16 + (lane & 15);
+          if (n < N) y[(int64_t)m * N + n] = float_to_half_bits(yacc[r][c][i]);
         }
       }
   }
@@ -419,53 +447,63 @@ __global__ __launch_bounds__(pf::THREADS, 1) void msd_gemm_kernel(
 
 // ---------------------------------------------------------------- launchers
 
+// Column blocks of 256 when that still gives at least one workgroup per CU
+// (256 workgroups), else of 128.
 PrefillLayout prefill_layout(int gs, int64_t M, int64_t K, int64_t N) {
   PrefillLayout L;
   L.mpad = (M + pf::BM - 1) / pf::BM * pf::BM;
-  L.npad = (N + pf::BN - 1) / pf::BN * pf::BN;
+  const int64_t tiles256 = (L.mpad / pf::BM) * ((N + 255) / 256);
+  L.bn = tiles256 >= 256 ? 256 : 128;
+  L.npad = (N + L.bn - 1) / L.bn * L.bn;
   const int64_t G = K / gs;
   L.a_bytes = (size_t)(3 * (L.mpad / 16) * G) * pf::TILE;
-  L.amax_bytes = (size_t)(G * L.mpad) * sizeof(float);
+  L.q_bytes = (size_t)(G * (L.mpad / pf::BM)) * pf::Q_GROUP;
   L.b_bytes = (size_t)((L.npad / 16) * G) * pf::TILE;
   return L;
 }
 
 hipError_t launch_prefill_prep(const void* x, const void* w, int gs, int64_t M, int64_t K,
-                               int64_t N, const PrefillLayout& L, uint8_t* a_t, float* amax_t,
+                               int64_t N, const PrefillLayout& L, uint8_t* a_t, float* q_t,
                                uint8_t* b_t, hipStream_t stream) {
   const int64_t xwaves = (L.mpad / 16) * (K / gs);                // (row tile, group) tasks
   const int64_t wwaves = (L.npad / kTileCols) * tiled_kblocks(K);  // 64 weight chunks each
   const unsigned blocks = (unsigned)((xwaves + wwaves + 3) / 4);
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   const uint8_t* wp = static_cast<const uint8_t*>(w);
-  const int m = (int)M, mp = (int)L.mpad, k = (int)K, n = (int)N, np = (int)L.npad;
+  const int m = (int)M, mp = (int)L.mpad, k = (int)K, n = (int)N, np = (int)L.npad, bn = (int)L.bn;
   if (gs == 64)
     hipLaunchKernelGGL(msd_prep_kernel<64>, dim3(blocks), dim3(256), 0, stream, xp, wp, m, mp, k, n,
-                       np, xwaves, a_t, amax_t, b_t);
+                       np, bn, xwaves, a_t, q_t, b_t);
   else
     hipLaunchKernelGGL(msd_prep_kernel<128>, dim3(blocks), dim3(256), 0, stream, xp, wp, m, mp, k,
-                       n, np, xwaves, a_t, amax_t, b_t);
+                       n, np, bn, xwaves, a_t, q_t, b_t);
   return hipGetLastError();
 }
 
-hipError_t launch_prefill_gemm(const uint8_t* a_t, const float* amax_t, const uint8_t* b_t,
+hipError_t launch_prefill_gemm(const uint8_t* a_t, const float* q_t, const uint8_t* b_t,
                                const void* scale, int gs, int64_t M, int64_t K, int64_t N,
                                const PrefillLayout& L, int64_t g_begin, int64_t g_end, void* y,
                                int32_t* y_int, hipStream_t stream) {
+  if (L.bn != 128 && L.bn != 256) return hipErrorInvalidValue;
   const int mblocks = (int)(L.mpad / pf::BM);
-  const int nblocks = (int)(L.npad / pf::BN);
+  const int nblocks = (int)(L.npad / L.bn);
   const dim3 grid((unsigned)(mblocks * nblocks));
   const uint16_t* sp = static_cast<const uint16_t*>(scale);
   uint16_t* yp = static_cast<uint16_t*>(y);
   const int m = (int)M, mp = (int)L.mpad, k = (int)K, n = (int)N, gb = (int)g_begin, ge = (int)g_end;
-#define WQBMM_GEMM_LAUNCH(GS_, Y_)                                                                 \
-  hipLaunchKernelGGL((msd_gemm_kernel<GS_, Y_>), grid, dim3(pf::THREADS), 0, stream, a_t, amax_t, \
-                     b_t, sp, m, mp, k, n, gb, ge, mblocks, nblocks, yp, y_int)
+#define WQBMM_GEMM_LAUNCH(GS_, BN_, Y_)                                                          \
+  hipLaunchKernelGGL((msd_gemm_kernel<GS_, BN_, Y_>), grid, dim3(pf::THREADS), 0, stream, a_t,  \
+                     q_t, b_t, sp, m, mp, k, n, gb, ge, mblocks, nblocks, yp, y_int)
+#define WQBMM_GEMM_BN(GS_, Y_)                                                                   \
+  do {                                                                                           \
+    if (L.bn == 256) WQBMM_GEMM_LAUNCH(GS_, 256, Y_); else WQBMM_GEMM_LAUNCH(GS_, 128, Y_);       \
+  } while (0)
   if (y_int) {
-    if (gs == 64) WQBMM_GEMM_LAUNCH(64, true); else WQBMM_GEMM_LAUNCH(128, true);
+    if (gs == 64) WQBMM_GEMM_BN(64, true); else WQBMM_GEMM_BN(128, true);
   } else {
-    if (gs == 64) WQBMM_GEMM_LAUNCH(64, false); else WQBMM_GEMM_LAUNCH(128, false);
+    if (gs == 64) WQBMM_GEMM_BN(64, false); else WQBMM_GEMM_BN(128, false);
   }
+#undef WQBMM_GEMM_BN
 #undef WQBMM_GEMM_LAUNCH
   return hipGetLastError();
 }
