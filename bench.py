@@ -251,10 +251,13 @@ def main():
                 "algorithmic_ops_per_launch": alg["exec_i8_ops"],
                 "frac_of_i8_peak": round(achieved / I8_PEAK_TOPS, 4)}
         # preparation kernel: reads x and the tiled int4 weights, writes the
-        # operand tiles (1536 bytes per 16 rows or columns x one group) and A_max
+        # operand tiles (1536 bytes each: 16 rows or columns x 128 k at group
+        # size 128, 32 x 64 k at group size 64) and the level weights
         G = K // gs
-        mpad, npad = -(-M // 128) * 128, -(-N // 128) * 128
-        prep_bytes = 2 * M * K + K * N // 2 + 1536 * (3 * mpad // 16 + npad // 16) * G + 4 * mpad * G
+        per = 16 if gs == 128 else 32
+        mpad = -(-M // 128) * 128
+        npad = -(-N // 256) * 256 if (mpad // 128) * -(-N // 256) >= 256 else -(-N // 128) * 128
+        prep_bytes = 2 * M * K + K * N // 2 + 1536 * (3 * mpad // per + npad // per) * G + 12 * mpad * G
         extra["prep"] = {"kernel": "msd_prep_kernel", "avg_kernel_us": round(prep_ms * 1e3, 3),
                          "achieved_GBps": round(prep_bytes / (prep_ms * 1e-3) / 1e9, 1)}
     if tinfo is not None and not isinstance(tinfo, str):

@@ -53,6 +53,17 @@ hipError_t launch_prefill_gemm(const uint8_t* a_t, const float* q_t, const uint8
                                const PrefillLayout& L, int64_t g_begin, int64_t g_end, void* y,
                                int32_t* y_int, hipStream_t stream);
 
+// Group size 64 (msd_prefill64.hip): the same roles on the 32x32x64 FP6 MFMA
+// (one group per instruction); the launchers above dispatch to these.
+PrefillLayout prefill64_layout(int64_t M, int64_t K, int64_t N);
+hipError_t launch_prefill64_prep(const void* x, const void* w, int64_t M, int64_t K, int64_t N,
+                                 const PrefillLayout& L, uint8_t* x_t, float* q_t, uint8_t* w_t,
+                                 hipStream_t stream);
+hipError_t launch_prefill64_gemm(const uint8_t* x_t, const float* q_t, const uint8_t* w_t,
+                                 const void* scale, int64_t M, int64_t K, int64_t N,
+                                 const PrefillLayout& L, int64_t g_begin, int64_t g_end, void* y,
+                                 int32_t* y_int, hipStream_t stream);
+
 // The fused decode kernel (M <= 16): steps 1-11 in one launch.  A K-split
 // hands its partials off through `accum` (int64 per output; zero before the
 // first launch, re-armed by the kernel).

@@ -450,6 +450,7 @@ __global__ __launch_bounds__(pf::THREADS, 1) void msd_gemm_kernel(
 // Column blocks of 256 when that still gives at least one workgroup per CU
 // (256 workgroups), else of 128.
 PrefillLayout prefill_layout(int gs, int64_t M, int64_t K, int64_t N) {
+  if (gs == 64) return prefill64_layout(M, K, N);
   PrefillLayout L;
   L.mpad = (M + pf::BM - 1) / pf::BM * pf::BM;
   const int64_t tiles256 = (L.mpad / pf::BM) * ((N + 255) / 256);
@@ -465,18 +466,15 @@ PrefillLayout prefill_layout(int gs, int64_t M, int64_t K, int64_t N) {
 hipError_t launch_prefill_prep(const void* x, const void* w, int gs, int64_t M, int64_t K,
                                int64_t N, const PrefillLayout& L, uint8_t* a_t, float* q_t,
                                uint8_t* b_t, hipStream_t stream) {
+  if (gs == 64) return launch_prefill64_prep(x, w, M, K, N, L, a_t, q_t, b_t, stream);
   const int64_t xwaves = (L.mpad / 16) * (K / gs);                // (row tile, group) tasks
   const int64_t wwaves = (L.npad / kTileCols) * tiled_kblocks(K);  // 64 weight chunks each
   const unsigned blocks = (unsigned)((xwaves + wwaves + 3) / 4);
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   const uint8_t* wp = static_cast<const uint8_t*>(w);
   const int m = (int)M, mp = (int)L.mpad, k = (int)K, n = (int)N, np = (int)L.npad, bn = (int)L.bn;
-  if (gs == 64)
-    hipLaunchKernelGGL(msd_prep_kernel<64>, dim3(blocks), dim3(256), 0, stream, xp, wp, m, mp, k, n,
-                       np, bn, xwaves, a_t, q_t, b_t);
-  else
-    hipLaunchKernelGGL(msd_prep_kernel<128>, dim3(blocks), dim3(256), 0, stream, xp, wp, m, mp, k,
-                       n, np, bn, xwaves, a_t, q_t, b_t);
+  hipLaunchKernelGGL(msd_prep_kernel<128>, dim3(blocks), dim3(256), 0, stream, xp, wp, m, mp, k,
+                     n, np, bn, xwaves, a_t, q_t, b_t);
   return hipGetLastError();
 }
 
@@ -484,6 +482,8 @@ hipError_t launch_prefill_gemm(const uint8_t* a_t, const float* q_t, const uint8
                                const void* scale, int gs, int64_t M, int64_t K, int64_t N,
                                const PrefillLayout& L, int64_t g_begin, int64_t g_end, void* y,
                                int32_t* y_int, hipStream_t stream) {
+  if (gs == 64)
+    return launch_prefill64_gemm(a_t, q_t, b_t, scale, M, K, N, L, g_begin, g_end, y, y_int, stream);
   if (L.bn != 128 && L.bn != 256) return hipErrorInvalidValue;
   const int mblocks = (int)(L.mpad / pf::BM);
   const int nblocks = (int)(L.npad / L.bn);
@@ -498,11 +498,7 @@ hipError_t launch_prefill_gemm(const uint8_t* a_t, const float* q_t, const uint8
   do {                                                                                           \
     if (L.bn == 256) WQBMM_GEMM_LAUNCH(GS_, 256, Y_); else WQBMM_GEMM_LAUNCH(GS_, 128, Y_);       \
   } while (0)
-  if (y_int) {
-    if (gs == 64) WQBMM_GEMM_BN(64, true); else WQBMM_GEMM_BN(128, true);
-  } else {
-    if (gs == 64) WQBMM_GEMM_BN(64, false); else WQBMM_GEMM_BN(128, false);
-  }
+  if (y_int) WQBMM_GEMM_BN(128, true); else WQBMM_GEMM_BN(128, false);
 #undef WQBMM_GEMM_BN
 #undef WQBMM_GEMM_LAUNCH
   return hipGetLastError();

@@ -1,0 +1,460 @@
+// msd_prefill64.hip -- the prefill path for group size 64: an operand
+// preparation kernel and an MFMA GEMM built on v_mfma_scale_f32_32x32x64_f8f6f4,
+// whose K of 64 is exactly one group.
+//
+// WQBMM-Exp page (the page "WeightQuantBatchMatmulExperiment 算子深度解析：A16W4
+// PerGroup 伪量化 MatMul 的 MSD 算法与双模板流水设计", lpnh.cn/news/2294145):
+//   §4.1 steps 1-8   per (row, group) A_max and the three levels A1..A3
+//   §4.1 step 9      Y_l = A_l . Weight_group, exact, on FP6 MFMAs
+//   §4.1 steps 10-11 combine, scale and accumulate over groups in fp32
+//   §6.2             PRELOAD_MSD: data movement ahead of the matmul
+//
+// Why a kernel of its own.  The 16x16x128 FP6 MFMA of the group-128 GEMM
+// covers 128 k; a group of 64 would fill half of every operand with zeros
+// (half the MFMA work and twice the operand bytes wasted).  The 32x32x64
+// form contracts exactly one group.  The integer arithmetic is the same: both
+// operands e2m3 (levels as they are, weights halved with the B... here the
+// weight operand's E8M0 block scale 2^1), every product exact, a group's sum
+// |Y_l| <= 7*8*64 = 3584 exact in the fp32 accumulator.
+//
+// Roles: the MFMA's A operand is the weights (its 32 "rows" are 32 output
+// columns n) and its B operand is x (its 32 "columns" are 32 rows m of x), so
+// D^T = W^T . X^T.  A lane then holds one row m of x in all 16 of its
+// results, and the step-10 weights of that row (A_max * w_l, three values)
+// are per lane; the scales vary with the result element (16 columns per
+// lane, four runs of four consecutive columns).
+//
+// Operand tiles (1536 bytes: [lane][dwords 0-3] then [lane][dwords 4-5], as
+// in the group-128 path): lane l holds row/column l%32 and the 32 values at
+// group-relative k = 32*(l/32) + j, packed by v_cvt_scalef32_2xpk16_fp6_f32
+// from u = values j = 0..15 and v = values j = 16..31 (the same packing for
+// both operands, so the MFMA pairs equal k).
+//   X_t: [row block of 128][group][level][row tile of 32: 0..3][tile]
+//   W_t: [column block of BN][group][column tile of 32][tile]
+//   Q_t: [group][row block][level][128 rows] fp32 (A_max * w_l)
+//
+// 32x32 result layout: lane l, element i -> MFMA row 8*(i/4) + 4*(l/32) + i%4
+// (output column), MFMA column l%32 (row of x).
+//
+// GEMM: workgroup tile 128 rows x BN (256 or 128) columns, 8 waves as 2
+// (rows: 64 = 2 row tiles of 32) x 4 (columns: BN/4 = 2 or 1 column tiles of
+// 32).  A pipeline stage holds GPS consecutive groups (their operands are
+// contiguous runs in X_t and W_t), double-buffered in LDS: the copies of
+// stage s+1 (global_load_lds, no staging registers) run while stage s is
+// computed, and one barrier per stage frees a buffer.  GPS groups per stage
+// put GPS groups of compute between a copy and its use, which is what hides
+// the copy latency when one group's compute is short (at M = 128 a group is
+// about 0.2 us of work per workgroup).
+#include "msd_device.hpp"
+#include "msd_launch.hpp"
+
+namespace wqbmm {
+namespace p64 {
+constexpr int BM = 128;
+constexpr int WAVES_M = 2, WAVES_N = 4, WAVES = 8, THREADS = 512;
+constexpr int XT = 2;                     // row tiles of 32 per wave
+constexpr int RT = BM / 32;               // row tiles per block: 4
+constexpr int TILE = 1536, TILE_LO = 1024;
+constexpr int X_GROUP = 3 * RT * TILE;    // 18 KB
+constexpr int Q_GROUP = 3 * BM * 4;       // 1.5 KB
+constexpr int NXCD = 8;
+constexpr int BAND = 4;
+}  // namespace p64
+
+typedef int v2i_ __attribute__((ext_vector_type(2)));
+typedef int v6i_ __attribute__((ext_vector_type(6)));
+typedef int v8i_ __attribute__((ext_vector_type(8)));
+typedef float v16f_ __attribute__((ext_vector_type(16)));
+
+namespace {
+constexpr float kW1 = (float)(1.0 / (double)kF1);
+constexpr float kW2 = (float)(1.0 / (double)(kF1 * kF2));
+constexpr float kW3 = (float)(1.0 / (double)(kF1 * kF2 * kF2));
+constexpr int kScaleX = 127;   // E8M0 2^0: levels as they are
+constexpr int kScaleW = 128;   // E8M0 2^1: weights stored halved
+
+// 32 exactly representable values -> six dwords of e2m3 (value / div); an
+// early-clobber destination (the instruction writes its result while still
+// reading its sources).
+__device__ __forceinline__ v6i_ pack6(const v16f_& u, const v16f_& v, float div) {
+  v6i_ r;
+  asm volatile("v_cvt_scalef32_2xpk16_fp6_f32 %0, %1, %2, %3" : "=&v"(r) : "v"(u), "v"(v), "v"(div));
+  return r;
+}
+
+__device__ __forceinline__ void store6(uint8_t* tile, int slot, const v6i_& p) {
+  *reinterpret_cast<v4i*>(tile + slot * 16) = v4i{p[0], p[1], p[2], p[3]};
+  *reinterpret_cast<v2i_*>(tile + p64::TILE_LO + slot * 8) = v2i_{p[4], p[5]};
+}
+
+// One operand lane (six dwords) as the MFMA's eight-dword argument; the FP6
+// form reads six, the last two are left undefined.
+__device__ __forceinline__ v8i_ operand6(const uint8_t* tile, int lane) {
+  const v4i lo = *reinterpret_cast<const v4i*>(tile + lane * 16);
+  const v2i_ hi = *reinterpret_cast<const v2i_*>(tile + p64::TILE_LO + lane * 8);
+  return __builtin_shufflevector(lo, __builtin_shufflevector(hi, hi, 0, 1, -1, -1), 0, 1, 2, 3, 4, 5, -1, -1);
+}
+}  // namespace
+
+// ---------------------------------------------------------------- preparation
+// Waves [0, xwaves): one (row tile of 32, group) each.  Lane l takes row
+// 32*tile + l%32 and the 32 elements k = 32*(l/32) + j of the group, so the
+// group maximum is the maximum of lanes l and l^32; steps 1-8 (same
+// arithmetic as every other kernel), then one packed operand lane per level
+// and the row's level weights.
+// Threads past that: one weight-operand lane each, (column tile of 32, group,
+// lane) over the padded width; lane l takes column 32*tile + l%32 and reads
+// the two 8-byte halves of the tiled-int4 chunk lanes that hold its 32 k
+// values (k-quarters 2*(l/32) and 2*(l/32)+1 of the group's 64-row step).
+__global__ __launch_bounds__(256) void msd_prep64_kernel(const uint16_t* __restrict__ x,
+                                                         const uint8_t* __restrict__ wt, int M,
+                                                         int Mpad, int K, int N, int Npad,
+                                                         int64_t xwaves, uint8_t* __restrict__ x_t,
+                                                         float* __restrict__ q_t,
+                                                         uint8_t* __restrict__ w_t, int BN) {
+  using namespace p64;
+  const int G = K / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wid < xwaves) {
+    const int mt = (int)(wid / G), g = (int)(wid % G);
+    const int h = lane >> 5;
+    const int m = mt * 32 + (lane & 31);
+    const bool real = m < M;
+    const uint16_t* src = x + (real ? (int64_t)m * K + (int64_t)g * 64 + 32 * h : 0);
+    float a[32];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (real) v = *reinterpret_cast<const uint4*>(src + 8 * c);
+      const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[8 * c + 2 * i] = half_bits_to_float(vw[i] & 0xffffu);
+        a[8 * c + 2 * i + 1] = half_bits_to_float(vw[i] >> 16);
+      }
+    }
+    float mx = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) mx = fmaxf(mx, fabsf(a[e]));
+    const float amax = fmaxf(mx, __shfl_xor(mx, 32));   // exact: max of the two halves
+    v16f_ lv[3][2];
+#pragma unroll
+    for (int l = 0; l < 3; ++l)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) lv[l][0][e] = lv[l][1][e] = 0.0f;
+    if (amax > 0.0f) {
+      const float rcp = msd_recip(amax);
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        float r1, r2, r3;
+        msd_expand_f(a[e], amax, rcp, r1, r2, r3);
+        lv[0][e / 16][e % 16] = r1;
+        lv[1][e / 16][e % 16] = r2;
+        lv[2][e / 16][e % 16] = r3;
+      }
+    }
+    const int rb = mt / RT, rt = mt % RT;
+#pragma unroll
+    for (int l = 0; l < 3; ++l) {
+      uint8_t* tile = x_t + ((((int64_t)rb * G + g) * 3 + l) * RT + rt) * TILE;
+      store6(tile, lane, pack6(lv[l][0], lv[l][1], 1.0f));
+    }
+    if (h == 0) {
+      float* q = q_t + (((int64_t)g * (Mpad / BM) + rb) * 3) * BM + (m % BM);
+      q[0] = amax * kW1;
+      q[BM] = amax * kW2;
+      q[2 * BM] = amax * kW3;
+    }
+    return;
+  }
+  // weight operand lanes: t = ((ct * G) + g) * 64 + lane over Npad/32 column tiles
+  const int64_t t = (wid - xwaves) * 64 + lane;
+  const int64_t total = (int64_t)(Npad / 32) * G * 64;
+  if (t >= total) return;
+  const int ct = (int)(t / ((int64_t)G * 64));
+  const int g = (int)((t / 64) % G);
+  const int n = ct * 32 + (lane & 31);
+  const int h = lane >> 5;
+  const int KB = (K + kTileRows - 1) / kTileRows;
+  v16f_ w[2];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    uint2 d = make_uint2(0u, 0u);
+    if (n < N) {
+      const int nt = n / kTileCols;
+      const int cl = (n % kTileCols) + 16 * (2 * h + half);        // chunk lane
+      const int64_t off = (((int64_t)nt * KB + g / 2) * 64 + cl) * 16 + 8 * (g % 2);
+      d = *reinterpret_cast<const uint2*>(wt + off);
+    }
+    const int32_t dw[2] = {(int32_t)d.x, (int32_t)d.y};
+    // element j = 8*dw + jj: low nibble of byte jj (jj < 4), high nibble of byte jj-4
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int jj = j % 8;
+      w[half][j] = (float)(int32_t)__builtin_amdgcn_sbfe(dw[j / 8], jj < 4 ? 8 * jj : 8 * (jj - 4) + 4, 4);
+    }
+  }
+  const int CT = BN / 32;
+  uint8_t* tile = w_t + (((int64_t)(ct / CT) * G + g) * CT + (ct % CT)) * TILE;
+  store6(tile, lane, pack6(w[0], w[1], 2.0f));
+}
+
+// ---------------------------------------------------------------- GEMM
+template <int BN, int GPS, bool YINT>
+__global__ __launch_bounds__(p64::THREADS, 1) void msd_gemm64_kernel(
+    const uint8_t* __restrict__ x_t, const float* __restrict__ q_t,
+    const uint8_t* __restrict__ w_t, const uint16_t* __restrict__ scale, int M, int Mpad, int K,
+    int N, int g_begin, int g_end, int mblocks, int nblocks, uint16_t* __restrict__ y,
+    int32_t* __restrict__ y_int) {
+  using namespace p64;
+  constexpr int CT = BN / 32;                     // column tiles per block: 8 or 4
+  constexpr int WT = CT / WAVES_N;                // column tiles per wave: 2 or 1
+  constexpr int WN = WT * 32;                     // columns per wave
+  constexpr int W_GROUP = CT * TILE;              // 12 or 6 KB
+  constexpr int X_KB = X_GROUP / 1024;            // 18 pieces of 1 KB
+  constexpr int PIECES = GPS * (X_GROUP + W_GROUP) / 1024;
+  constexpr int CPW = (PIECES + WAVES - 1) / WAVES;
+  constexpr int QC = Q_GROUP / 256;               // 256-byte copies of level weights per group: 6
+  constexpr int SC = BN * 2 / 256;                // of scales per group: 2 or 1
+  constexpr int SMALL = GPS * (QC + (YINT ? 0 : SC));
+  constexpr int SPW = (SMALL + WAVES - 1) / WAVES;
+  static_assert((X_GROUP + W_GROUP) % 1024 == 0, "whole pieces");
+
+  __shared__ __attribute__((aligned(16))) uint8_t sX[2][GPS * X_GROUP];
+  __shared__ __attribute__((aligned(16))) uint8_t sW[2][GPS * W_GROUP];
+  __shared__ __attribute__((aligned(16))) float sQ[2][GPS * 3 * BM];
+  __shared__ __attribute__((aligned(16))) uint16_t sS[2][GPS * BN];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WAVES_N;
+  const int wn = wave % WAVES_N;
+
+  // tile order: as the group-128 GEMM (contiguous ranges per XCD, bands of
+  // BAND row blocks, column-major within a band); speed only
+  const int total = mblocks * nblocks;
+  int t = blockIdx.x;
+  if (total % NXCD == 0) t = (blockIdx.x % NXCD) * (total / NXCD) + blockIdx.x / NXCD;
+  const int band_tiles = BAND * nblocks;
+  const int band = t / band_tiles;
+  const int in_band = t % band_tiles;
+  const int band_rows = min(BAND, mblocks - band * BAND);
+  const int rb = band * BAND + in_band % band_rows;
+  const int cb = in_band / band_rows;
+  const int m0 = rb * BM, n0 = cb * BN;
+  const int G = K / 64;
+  const int RB = Mpad / BM;
+
+  const uint8_t* x_run = x_t + (int64_t)rb * G * X_GROUP;
+  const uint8_t* w_run = w_t + (int64_t)cb * G * W_GROUP;
+
+  // Copies of stage (groups g0 .. g0+ng-1, ng <= GPS) into buffer b.  Piece p
+  // of a stage: p < ng*X_KB in the X run, then the W run; small copy s:
+  // (group s / per, kind s % per) with per = QC (+ SC).
+  auto dma = [&](int g0, int ng, int b) {
+    const int xp = ng * X_KB;
+    const int np = ng * (X_GROUP + W_GROUP) / 1024;
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const int p = wave * CPW + c;                         // wave-uniform
+      if (p < np) {
+        const uint8_t* src = p < xp ? x_run + (int64_t)g0 * X_GROUP + p * 1024
+                                    : w_run + (int64_t)g0 * W_GROUP + (p - xp) * 1024;
+        uint8_t* dst = p < xp ? &sX[b][p * 1024] : &sW[b][(p - xp) * 1024];
+        __builtin_amdgcn_global_load_lds(src + lane * 16, dst, 16, 0, 0);
+      }
+    }
+    constexpr int PER = QC + (YINT ? 0 : SC);
+#pragma unroll
+    for (int c = 0; c < SPW; ++c) {
+      const int sidx = wave * SPW + c;                      // wave-uniform
+      if (sidx < ng * PER) {
+        const int gi = sidx / PER, kind = sidx % PER;
+        const int g = g0 + gi;
+        if (kind < QC) {
+          const uint8_t* src = reinterpret_cast<const uint8_t*>(q_t) +
+                               ((int64_t)g * RB + rb) * Q_GROUP + kind * 256 + lane * 4;
+          __builtin_amdgcn_global_load_lds(src, reinterpret_cast<uint8_t*>(&sQ[b][gi * 3 * BM]) + kind * 256, 4, 0, 0);
+        } else {
+          const int col = min(n0 + (kind - QC) * 128 + 2 * lane, N - 2);
+          const uint8_t* src = reinterpret_cast<const uint8_t*>(scale) + ((int64_t)g * N + col) * 2;
+          __builtin_amdgcn_global_load_lds(src, reinterpret_cast<uint8_t*>(&sS[b][gi * BN]) + (kind - QC) * 256, 4, 0, 0);
+        }
+      }
+    }
+  };
+
+  float yacc[XT][WT][16];
+#pragma unroll
+  for (int a = 0; a < XT; ++a)
+#pragma unroll
+    for (int c = 0; c < WT; ++c)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) yacc[a][c][i] = 0.0f;
+
+  // Steps 9-11 for group g (index gi in its stage) from buffer b: the wave's
+  // WT weight operands and XT x 3 level operands, then per output tile 3
+  // MFMAs and the combine (4 VALU per output: three for the levels with the
+  // row's weights, one for the column's scale and the running sum).
+  auto compute = [&](int b, int gi, int g) {
+    const uint8_t* sx = &sX[b][gi * X_GROUP];
+    const uint8_t* sw = &sW[b][gi * W_GROUP];
+    v8i_ wop[WT];
+#pragma unroll
+    for (int c = 0; c < WT; ++c) wop[c] = operand6(sw + (wn * WT + c) * TILE, lane);
+    v8i_ xop[XT][3];
+#pragma unroll
+    for (int a = 0; a < XT; ++a)
+#pragma unroll
+      for (int l = 0; l < 3; ++l) xop[a][l] = operand6(sx + (l * RT + wm * XT + a) * TILE, lane);
+    float q[XT][3];
+    if constexpr (!YINT) {
+#pragma unroll
+      for (int a = 0; a < XT; ++a)
+#pragma unroll
+        for (int l = 0; l < 3; ++l) q[a][l] = sQ[b][gi * 3 * BM + l * BM + (wm * XT + a) * 32 + (lane & 31)];
+    }
+#pragma unroll
+    for (int c = 0; c < WT; ++c) {
+      uint2 sr[4];                                          // 16 scales: 4 runs of 4 columns
+      if constexpr (!YINT) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          sr[r] = *reinterpret_cast<const uint2*>(&sS[b][gi * BN + wn * WN + c * 32 + 8 * r + 4 * (lane >> 5)]);
+      }
+#pragma unroll
+      for (int a = 0; a < XT; ++a) {
+        v16f_ d[3];
+#pragma unroll
+        for (int l = 0; l < 3; ++l)
+          d[l] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              wop[c], xop[a][l], v16f_{}, 2, 2, 0, kScaleW, 0, kScaleX);
+        // An (empty) use of the operands together with the results: the
+        // operands are live after the MFMAs, so no result is given registers
+        // of its own A or B operand (the 16 result registers of this form are
+        // written over several passes).
+        asm volatile("" ::"v"(wop[c]), "v"(xop[a][0]), "v"(xop[a][1]), "v"(xop[a][2]), "v"(d[0]),
+                     "v"(d[1]), "v"(d[2]));
+        if constexpr (YINT) {
+          const int m = m0 + (wm * XT + a) * 32 + (lane & 31);
+          const int64_t gi_out = g - g_begin;
+          if (m < M) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int n = n0 + wn * WN + c * 32 + 8 * (i / 4) + 4 * (lane >> 5) + (i % 4);
+              if (n < N) {
+#pragma unroll
+                for (int l = 0; l < 3; ++l)
+                  y_int[((gi_out * 3 + l) * M + m) * (int64_t)N + n] = (int32_t)d[l][i];
+              }
+            }
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const uint32_t sw2 = (i % 4) < 2 ? sr[i / 4].x : sr[i / 4].y;
+            const float sc = half_bits_to_float((i % 2) ? (sw2 >> 16) : (sw2 & 0xffffu));
+            float tt = d[0][i] * q[a][0];
+            tt = __builtin_fmaf(d[1][i], q[a][1], tt);
+            tt = __builtin_fmaf(d[2][i], q[a][2], tt);
+            yacc[a][c][i] = __builtin_fmaf(tt, sc, yacc[a][c][i]);
+          }
+        }
+      }
+    }
+  };
+
+  // stages of GPS groups over [g_begin, g_end), double-buffered
+  const int ngroups = g_end - g_begin;
+  const int nstages = (ngroups + GPS - 1) / GPS;
+  dma(g_begin, min(GPS, ngroups), 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int s = 0; s < nstages; ++s) {
+    const int b = s & 1;
+    const int g0 = g_begin + s * GPS;
+    const int ng = min(GPS, g_end - g0);
+    if (s + 1 < nstages) dma(g0 + GPS, min(GPS, g_end - g0 - GPS), b ^ 1);
+#pragma unroll
+    for (int gi = 0; gi < GPS; ++gi)
+      if (gi < ng) compute(b, gi, g0 + gi);                 // constant LDS offsets per gi
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  if constexpr (!YINT) {
+#pragma unroll
+    for (int a = 0; a < XT; ++a) {
+      const int m = m0 + (wm * XT + a) * 32 + (lane & 31);
+      if (m >= M) continue;
+#pragma unroll
+      for (int c = 0; c < WT; ++c)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int n = n0 + wn * WN + c * 32 + 8 * r + 4 * (lane >> 5);   // 4 consecutive columns
+          if (n >= N) continue;
+          const uint32_t lo = (uint32_t)float_to_half_bits(yacc[a][c][4 * r]) |
+                              ((uint32_t)float_to_half_bits(yacc[a][c][4 * r + 1]) << 16);
+          const uint32_t hi = (uint32_t)float_to_half_bits(yacc[a][c][4 * r + 2]) |
+                              ((uint32_t)float_to_half_bits(yacc[a][c][4 * r + 3]) << 16);
+          *reinterpret_cast<uint2*>(y + (int64_t)m * N + n) = make_uint2(lo, hi);
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+
+PrefillLayout prefill64_layout(int64_t M, int64_t K, int64_t N) {
+  PrefillLayout L;
+  L.mpad = (M + p64::BM - 1) / p64::BM * p64::BM;
+  const int64_t tiles256 = (L.mpad / p64::BM) * ((N + 255) / 256);
+  L.bn = tiles256 >= 256 ? 256 : 128;
+  L.npad = (N + L.bn - 1) / L.bn * L.bn;
+  const int64_t G = K / 64;
+  L.a_bytes = (size_t)(3 * (L.mpad / 32) * G) * p64::TILE;
+  L.q_bytes = (size_t)(G * (L.mpad / p64::BM)) * p64::Q_GROUP;
+  L.b_bytes = (size_t)((L.npad / 32) * G) * p64::TILE;
+  return L;
+}
+
+hipError_t launch_prefill64_prep(const void* x, const void* w, int64_t M, int64_t K, int64_t N,
+                                 const PrefillLayout& L, uint8_t* x_t, float* q_t, uint8_t* w_t,
+                                 hipStream_t stream) {
+  const int64_t G = K / 64;
+  const int64_t xwaves = (L.mpad / 32) * G;
+  const int64_t wwaves = (L.npad / 32) * G;                 // one wave per (column tile, group)
+  const unsigned blocks = (unsigned)((xwaves + wwaves + 3) / 4);
+  hipLaunchKernelGGL(msd_prep64_kernel, dim3(blocks), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(x), static_cast<const uint8_t*>(w), (int)M,
+                     (int)L.mpad, (int)K, (int)N, (int)L.npad, xwaves, x_t, q_t, w_t, (int)L.bn);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill64_gemm(const uint8_t* x_t, const float* q_t, const uint8_t* w_t,
+                                 const void* scale, int64_t M, int64_t K, int64_t N,
+                                 const PrefillLayout& L, int64_t g_begin, int64_t g_end, void* y,
+                                 int32_t* y_int, hipStream_t stream) {
+  if (L.bn != 128 && L.bn != 256) return hipErrorInvalidValue;
+  const int mblocks = (int)(L.mpad / p64::BM);
+  const int nblocks = (int)(L.npad / L.bn);
+  const dim3 grid((unsigned)(mblocks * nblocks));
+  const uint16_t* sp = static_cast<const uint16_t*>(scale);
+  uint16_t* yp = static_cast<uint16_t*>(y);
+  const int m = (int)M, mp = (int)L.mpad, k = (int)K, n = (int)N, gb = (int)g_begin, ge = (int)g_end;
+  // stages: 2 groups at BN = 256 (2 x 64 KB of LDS), 3 at BN = 128 (2 x 77 KB)
+#define WQBMM_G64_LAUNCH(BN_, GPS_, Y_)                                                          \
+  hipLaunchKernelGGL((msd_gemm64_kernel<BN_, GPS_, Y_>), grid, dim3(p64::THREADS), 0, stream,    \
+                     x_t, q_t, w_t, sp, m, mp, k, n, gb, ge, mblocks, nblocks, yp, y_int)
+  if (y_int) {
+    if (L.bn == 256) WQBMM_G64_LAUNCH(256, 2, true); else WQBMM_G64_LAUNCH(128, 3, true);
+  } else {
+    if (L.bn == 256) WQBMM_G64_LAUNCH(256, 2, false); else WQBMM_G64_LAUNCH(128, 3, false);
+  }
+#undef WQBMM_G64_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace wqbmm
