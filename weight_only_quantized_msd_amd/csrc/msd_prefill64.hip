@@ -102,10 +102,10 @@ __device__ __forceinline__ v8i_ operand6(const uint8_t* tile, int lane) {
 // group maximum is the maximum of lanes l and l^32; steps 1-8 (same
 // arithmetic as every other kernel), then one packed operand lane per level
 // and the row's level weights.
-// Threads past that: one weight-operand lane each, (column tile of 32, group,
-// lane) over the padded width; lane l takes column 32*tile + l%32 and reads
-// the two 8-byte halves of the tiled-int4 chunk lanes that hold its 32 k
-// values (k-quarters 2*(l/32) and 2*(l/32)+1 of the group's 64-row step).
+// Threads past that: lane l of (column tile of 32, 128-row block) takes
+// column 32*tile + l%32 and the two tiled-int4 chunk lanes that hold its 32 k
+// values of each 64-row step (k-quarters 2*(l/32) and 2*(l/32)+1), and writes
+// its weight-operand lane of both groups of the block.
 __global__ __launch_bounds__(256) void msd_prep64_kernel(const uint16_t* __restrict__ x,
                                                          const uint8_t* __restrict__ wt, int M,
                                                          int Mpad, int K, int N, int Npad,
@@ -168,36 +168,47 @@ __global__ __launch_bounds__(256) void msd_prep64_kernel(const uint16_t* __restr
     }
     return;
   }
-  // weight operand lanes: t = ((ct * G) + g) * 64 + lane over Npad/32 column tiles
+  // weight operand lanes of both groups of a 128-row block: t = ((ct * KB) +
+  // kb) * 64 + lane over Npad/32 column tiles.  The thread reads the two
+  // 16-byte chunk lanes that hold its 32 k values of both 64-row steps and
+  // writes one operand lane of group 2*kb (first half of each chunk lane)
+  // and, if it exists, of group 2*kb + 1 (second half).
+  const int KB = (K + kTileRows - 1) / kTileRows;
   const int64_t t = (wid - xwaves) * 64 + lane;
-  const int64_t total = (int64_t)(Npad / 32) * G * 64;
+  const int64_t total = (int64_t)(Npad / 32) * KB * 64;
   if (t >= total) return;
-  const int ct = (int)(t / ((int64_t)G * 64));
-  const int g = (int)((t / 64) % G);
+  const int ct = (int)(t / ((int64_t)KB * 64));
+  const int kb = (int)((t / 64) % KB);
   const int n = ct * 32 + (lane & 31);
   const int h = lane >> 5;
-  const int KB = (K + kTileRows - 1) / kTileRows;
-  v16f_ w[2];
+  uint4 c[2] = {make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};
+  if (n < N) {
+    const int nt = n / kTileCols;
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    uint2 d = make_uint2(0u, 0u);
-    if (n < N) {
-      const int nt = n / kTileCols;
-      const int cl = (n % kTileCols) + 16 * (2 * h + half);        // chunk lane
-      const int64_t off = (((int64_t)nt * KB + g / 2) * 64 + cl) * 16 + 8 * (g % 2);
-      d = *reinterpret_cast<const uint2*>(wt + off);
-    }
-    const int32_t dw[2] = {(int32_t)d.x, (int32_t)d.y};
-    // element j = 8*dw + jj: low nibble of byte jj (jj < 4), high nibble of byte jj-4
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int jj = j % 8;
-      w[half][j] = (float)(int32_t)__builtin_amdgcn_sbfe(dw[j / 8], jj < 4 ? 8 * jj : 8 * (jj - 4) + 4, 4);
+    for (int half = 0; half < 2; ++half) {
+      const int cl = (n % kTileCols) + 16 * (2 * h + half);       // chunk lane
+      c[half] = *reinterpret_cast<const uint4*>(wt + (((int64_t)nt * KB + kb) * 64 + cl) * 16);
     }
   }
   const int CT = BN / 32;
-  uint8_t* tile = w_t + (((int64_t)(ct / CT) * G + g) * CT + (ct % CT)) * TILE;
-  store6(tile, lane, pack6(w[0], w[1], 2.0f));
+#pragma unroll
+  for (int step = 0; step < 2; ++step) {
+    const int g = 2 * kb + step;
+    if (g >= G) break;                                   // K % 128 == 64: one group in the last block
+    v16f_ w[2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int32_t dw[2] = {(int32_t)(step ? c[half].z : c[half].x), (int32_t)(step ? c[half].w : c[half].y)};
+      // element j = 8*d + jj: low nibble of byte jj (jj < 4), high nibble of byte jj-4
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int jj = j % 8;
+        w[half][j] = (float)(int32_t)__builtin_amdgcn_sbfe(dw[j / 8], jj < 4 ? 8 * jj : 8 * (jj - 4) + 4, 4);
+      }
+    }
+    uint8_t* tile = w_t + (((int64_t)(ct / CT) * G + g) * CT + (ct % CT)) * TILE;
+    store6(tile, lane, pack6(w[0], w[1], 2.0f));
+  }
 }
 
 // ---------------------------------------------------------------- GEMM
@@ -425,7 +436,7 @@ hipError_t launch_prefill64_prep(const void* x, const void* w, int64_t M, int64_
                                  hipStream_t stream) {
   const int64_t G = K / 64;
   const int64_t xwaves = (L.mpad / 32) * G;
-  const int64_t wwaves = (L.npad / 32) * G;                 // one wave per (column tile, group)
+  const int64_t wwaves = (L.npad / 32) * tiled_kblocks(K);  // one wave per (column tile, 128-row block)
   const unsigned blocks = (unsigned)((xwaves + wwaves + 3) / 4);
   hipLaunchKernelGGL(msd_prep64_kernel, dim3(blocks), dim3(256), 0, stream,
                      static_cast<const uint16_t*>(x), static_cast<const uint8_t*>(w), (int)M,
