@@ -36,9 +36,9 @@
 // 32x32 result layout: lane l, element i -> MFMA row 8*(i/4) + 4*(l/32) + i%4
 // (output column), MFMA column l%32 (row of x).
 //
-// GEMM: workgroup tile 128 rows x BN (256 or 128) columns, 8 waves as 2
-// (rows: 64 = 2 row tiles of 32) x 4 (columns: BN/4 = 2 or 1 column tiles of
-// 32).  A pipeline stage holds GPS consecutive groups (their operands are
+// GEMM: workgroup tile 128 rows x BN (256 or 128) columns; at BN = 256 8
+// waves as 2 (rows: 64 = 2 row tiles of 32) x 4 (columns: 2 column tiles of
+// 32), at BN = 128 16 waves as 4 x 4 (one 32x32 tile each).  A pipeline stage holds GPS consecutive groups (their operands are
 // contiguous runs in X_t and W_t), double-buffered in LDS: the copies of
 // stage s+1 (global_load_lds, no staging registers) run while stage s is
 // computed, and one barrier per stage frees a buffer.  GPS groups per stage
@@ -51,8 +51,7 @@
 namespace wqbmm {
 namespace p64 {
 constexpr int BM = 128;
-constexpr int WAVES_M = 2, WAVES_N = 4, WAVES = 8, THREADS = 512;
-constexpr int XT = 2;                     // row tiles of 32 per wave
+constexpr int WAVES_N = 4;                // waves along the columns
 constexpr int RT = BM / 32;               // row tiles per block: 4
 constexpr int TILE = 1536, TILE_LO = 1024;
 constexpr int X_GROUP = 3 * RT * TILE;    // 18 KB
@@ -212,13 +211,15 @@ __global__ __launch_bounds__(256) void msd_prep64_kernel(const uint16_t* __restr
 }
 
 // ---------------------------------------------------------------- GEMM
-template <int BN, int GPS, bool YINT>
-__global__ __launch_bounds__(p64::THREADS, 1) void msd_gemm64_kernel(
+template <int BN, int GPS, int WAVES_M, bool YINT>
+__global__ __launch_bounds__(64 * WAVES_M * p64::WAVES_N, 1) void msd_gemm64_kernel(
     const uint8_t* __restrict__ x_t, const float* __restrict__ q_t,
     const uint8_t* __restrict__ w_t, const uint16_t* __restrict__ scale, int M, int Mpad, int K,
     int N, int g_begin, int g_end, int mblocks, int nblocks, uint16_t* __restrict__ y,
     int32_t* __restrict__ y_int) {
   using namespace p64;
+  constexpr int WAVES = WAVES_M * WAVES_N;        // 8 or 16
+  constexpr int XT = RT / WAVES_M;                // row tiles of 32 per wave: 2 or 1
   constexpr int CT = BN / 32;                     // column tiles per block: 8 or 4
   constexpr int WT = CT / WAVES_N;                // column tiles per wave: 2 or 1
   constexpr int WN = WT * 32;                     // columns per wave
@@ -335,19 +336,33 @@ __global__ __launch_bounds__(p64::THREADS, 1) void msd_gemm64_kernel(
         for (int r = 0; r < 4; ++r)
           sr[r] = *reinterpret_cast<const uint2*>(&sS[b][gi * BN + wn * WN + c * 32 + 8 * r + 4 * (lane >> 5)]);
       }
+      // The MFMAs of AB row tiles first, then their combines: with AB = XT
+      // (one column tile per wave) the second row tile's MFMAs run while the
+      // first tile's results are combined; with two column tiles per wave the
+      // registers allow one row tile at a time.
+      constexpr int AB = WT == 1 ? XT : 1;
 #pragma unroll
-      for (int a = 0; a < XT; ++a) {
-        v16f_ d[3];
+      for (int a0 = 0; a0 < XT; a0 += AB) {
+      v16f_ d[XT][3];
+#pragma unroll
+      for (int a = a0; a < a0 + AB; ++a) {
 #pragma unroll
         for (int l = 0; l < 3; ++l)
-          d[l] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          d[a][l] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
               wop[c], xop[a][l], v16f_{}, 2, 2, 0, kScaleW, 0, kScaleX);
         // An (empty) use of the operands together with the results: the
         // operands are live after the MFMAs, so no result is given registers
         // of its own A or B operand (the 16 result registers of this form are
         // written over several passes).
-        asm volatile("" ::"v"(wop[c]), "v"(xop[a][0]), "v"(xop[a][1]), "v"(xop[a][2]), "v"(d[0]),
-                     "v"(d[1]), "v"(d[2]));
+        // (VGPR constraints exist on the device pass only; on the host pass a
+        // dependent operand would make the kernel template fail to instantiate.)
+#if defined(__HIP_DEVICE_COMPILE__)
+        asm volatile("" ::"v"(wop[c]), "v"(xop[a][0]), "v"(xop[a][1]), "v"(xop[a][2]), "v"(d[a][0]),
+                     "v"(d[a][1]), "v"(d[a][2]));
+#endif
+      }
+#pragma unroll
+      for (int a = a0; a < a0 + AB; ++a) {
         if constexpr (YINT) {
           const int m = m0 + (wm * XT + a) * 32 + (lane & 31);
           const int64_t gi_out = g - g_begin;
@@ -358,7 +373,7 @@ __global__ __launch_bounds__(p64::THREADS, 1) void msd_gemm64_kernel(
               if (n < N) {
 #pragma unroll
                 for (int l = 0; l < 3; ++l)
-                  y_int[((gi_out * 3 + l) * M + m) * (int64_t)N + n] = (int32_t)d[l][i];
+                  y_int[((gi_out * 3 + l) * M + m) * (int64_t)N + n] = (int32_t)d[a][l][i];
               }
             }
           }
@@ -367,12 +382,13 @@ __global__ __launch_bounds__(p64::THREADS, 1) void msd_gemm64_kernel(
           for (int i = 0; i < 16; ++i) {
             const uint32_t sw2 = (i % 4) < 2 ? sr[i / 4].x : sr[i / 4].y;
             const float sc = half_bits_to_float((i % 2) ? (sw2 >> 16) : (sw2 & 0xffffu));
-            float tt = d[0][i] * q[a][0];
-            tt = __builtin_fmaf(d[1][i], q[a][1], tt);
-            tt = __builtin_fmaf(d[2][i], q[a][2], tt);
+            float tt = d[a][0][i] * q[a][0];
+            tt = __builtin_fmaf(d[a][1][i], q[a][1], tt);
+            tt = __builtin_fmaf(d[a][2][i], q[a][2], tt);
             yacc[a][c][i] = __builtin_fmaf(tt, sc, yacc[a][c][i]);
           }
         }
+      }
       }
     }
   };
@@ -455,14 +471,16 @@ hipError_t launch_prefill64_gemm(const uint8_t* x_t, const float* q_t, const uin
   const uint16_t* sp = static_cast<const uint16_t*>(scale);
   uint16_t* yp = static_cast<uint16_t*>(y);
   const int m = (int)M, mp = (int)L.mpad, k = (int)K, n = (int)N, gb = (int)g_begin, ge = (int)g_end;
-  // stages: 2 groups at BN = 256 (2 x 64 KB of LDS), 3 at BN = 128 (2 x 77 KB)
-#define WQBMM_G64_LAUNCH(BN_, GPS_, Y_)                                                          \
-  hipLaunchKernelGGL((msd_gemm64_kernel<BN_, GPS_, Y_>), grid, dim3(p64::THREADS), 0, stream,    \
-                     x_t, q_t, w_t, sp, m, mp, k, n, gb, ge, mblocks, nblocks, yp, y_int)
+  // stages: 2 groups at BN = 256 (2 x 64 KB of LDS), 3 at BN = 128 (2 x 77 KB);
+  // at BN = 128 a wave holds one 32x32 output tile, 16 waves per workgroup
+  // (four per SIMD hide the MFMA and copy latencies of the short groups)
+#define WQBMM_G64_LAUNCH(BN_, GPS_, WM_, Y_)                                                     \
+  hipLaunchKernelGGL((msd_gemm64_kernel<BN_, GPS_, WM_, Y_>), grid, dim3(64 * 4 * (WM_)), 0,     \
+                     stream, x_t, q_t, w_t, sp, m, mp, k, n, gb, ge, mblocks, nblocks, yp, y_int)
   if (y_int) {
-    if (L.bn == 256) WQBMM_G64_LAUNCH(256, 2, true); else WQBMM_G64_LAUNCH(128, 3, true);
+    if (L.bn == 256) WQBMM_G64_LAUNCH(256, 2, 2, true); else WQBMM_G64_LAUNCH(128, 3, 4, true);
   } else {
-    if (L.bn == 256) WQBMM_G64_LAUNCH(256, 2, false); else WQBMM_G64_LAUNCH(128, 3, false);
+    if (L.bn == 256) WQBMM_G64_LAUNCH(256, 2, 2, false); else WQBMM_G64_LAUNCH(128, 3, 4, false);
   }
 #undef WQBMM_G64_LAUNCH
   return hipGetLastError();
