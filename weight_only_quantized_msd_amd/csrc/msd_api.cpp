@@ -185,7 +185,7 @@ wqbmm_status run_prefill(int dev, const void* x, const void* w, const void* scal
     st = launch_status(wqbmm::launch_prefill_prep(x, w, (int)gs, M, K, N, L, a_t, q_t, b_t, stream));
     if (st != WQBMM_OK || stage == 1) return st;
   }
-  return launch_status(wqbmm::launch_prefill_gemm(a_t, q_t, b_t, scale, (int)gs, M, K, N, L,
+  return launch_status(wqbmm::launch_prefill_gemm(a_t, q_t, b_t, w, scale, (int)gs, M, K, N, L,
                                                   g_begin, g_end, y, y_int, stream));
 }
 

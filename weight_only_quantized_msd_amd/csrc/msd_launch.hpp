@@ -38,7 +38,8 @@ struct PrefillLayout {
   int64_t npad;        // columns padded to a multiple of bn
   size_t a_bytes;      // level tiles of x: 3 * (mpad/16) * G tiles of 1536 bytes
   size_t q_bytes;      // level weights, [group][row block][level][128] fp32
-  size_t b_bytes;      // weight tiles: (npad/16) * G tiles of 1536 bytes
+  size_t b_bytes;      // weight tiles: (npad/16) * G tiles of 1536 bytes (0 if w_in_gemm)
+  bool w_in_gemm;      // the GEMM converts the tiled int4 weights itself (few row blocks)
 };
 PrefillLayout prefill_layout(int gs, int64_t M, int64_t K, int64_t N);
 
@@ -49,6 +50,7 @@ hipError_t launch_prefill_prep(const void* x, const void* w, int gs, int64_t M, 
 // y_int == nullptr: groups [g_begin, g_end) are combined into y (fp16 [M][N]);
 // otherwise they are stored as int32 Y_int.
 hipError_t launch_prefill_gemm(const uint8_t* a_t, const float* q_t, const uint8_t* b_t,
+                               const void* w_tiled,
                                const void* scale, int gs, int64_t M, int64_t K, int64_t N,
                                const PrefillLayout& L, int64_t g_begin, int64_t g_end, void* y,
                                int32_t* y_int, hipStream_t stream);
@@ -60,6 +62,7 @@ hipError_t launch_prefill64_prep(const void* x, const void* w, int64_t M, int64_
                                  const PrefillLayout& L, uint8_t* x_t, float* q_t, uint8_t* w_t,
                                  hipStream_t stream);
 hipError_t launch_prefill64_gemm(const uint8_t* x_t, const float* q_t, const uint8_t* w_t,
+                                 const void* w_tiled,
                                  const void* scale, int64_t M, int64_t K, int64_t N,
                                  const PrefillLayout& L, int64_t g_begin, int64_t g_end, void* y,
                                  int32_t* y_int, hipStream_t stream);

@@ -460,6 +460,7 @@ PrefillLayout prefill_layout(int gs, int64_t M, int64_t K, int64_t N) {
   L.a_bytes = (size_t)(3 * (L.mpad / 16) * G) * pf::TILE;
   L.q_bytes = (size_t)(G * (L.mpad / pf::BM)) * pf::Q_GROUP;
   L.b_bytes = (size_t)((L.npad / 16) * G) * pf::TILE;
+  L.w_in_gemm = false;
   return L;
 }
 
@@ -479,11 +480,12 @@ hipError_t launch_prefill_prep(const void* x, const void* w, int gs, int64_t M, 
 }
 
 hipError_t launch_prefill_gemm(const uint8_t* a_t, const float* q_t, const uint8_t* b_t,
-                               const void* scale, int gs, int64_t M, int64_t K, int64_t N,
+                               const void* w_tiled, const void* scale, int gs, int64_t M, int64_t K, int64_t N,
                                const PrefillLayout& L, int64_t g_begin, int64_t g_end, void* y,
                                int32_t* y_int, hipStream_t stream) {
   if (gs == 64)
-    return launch_prefill64_gemm(a_t, q_t, b_t, scale, M, K, N, L, g_begin, g_end, y, y_int, stream);
+    return launch_prefill64_gemm(a_t, q_t, b_t, w_tiled, scale, M, K, N, L, g_begin, g_end, y, y_int,
+                                 stream);
   if (L.bn != 128 && L.bn != 256) return hipErrorInvalidValue;
   const int mblocks = (int)(L.mpad / pf::BM);
   const int nblocks = (int)(L.npad / L.bn);

@@ -45,6 +45,8 @@
 // put GPS groups of compute between a copy and its use, which is what hides
 // the copy latency when one group's compute is short (at M = 128 a group is
 // about 0.2 us of work per workgroup).
+#include <type_traits>
+
 #include "msd_device.hpp"
 #include "msd_launch.hpp"
 
@@ -72,13 +74,51 @@ constexpr float kW3 = (float)(1.0 / (double)(kF1 * kF2 * kF2));
 constexpr int kScaleX = 127;   // E8M0 2^0: levels as they are
 constexpr int kScaleW = 128;   // E8M0 2^1: weights stored halved
 
-// 32 exactly representable values -> six dwords of e2m3 (value / div); an
-// early-clobber destination (the instruction writes its result while still
-// reading its sources).
-__device__ __forceinline__ v6i_ pack6(const v16f_& u, const v16f_& v, float div) {
+typedef _Float16 v2h_ __attribute__((ext_vector_type(2)));
+typedef _Float16 v32h_ __attribute__((ext_vector_type(32)));
+
+// Operand slot order, the same for both operands: slot 8*i + t of lane l's
+// 32 (i = 0..3, t = 0..7) holds group-relative k = 32*(l/32) + 8*i + kSlotK[t],
+// the order in which weight_operand6 takes the nibbles of a tiled-weight dword.
+// The MFMA pairs equal slots, so any order shared by both operands is exact.
+constexpr int kSlotK[8] = {0, 2, 4, 6, 1, 3, 5, 7};
+
+// 32 exactly representable fp16 values -> six dwords of e2m3 (value / div),
+// slot e from element e.  An early-clobber destination: the instruction
+// writes its result while it still reads its sources, and the builtin can be
+// given a destination that overlaps them.
+__device__ __forceinline__ v6i_ pack6h(const v32h_& v, float div) {
   v6i_ r;
-  asm volatile("v_cvt_scalef32_2xpk16_fp6_f32 %0, %1, %2, %3" : "=&v"(r) : "v"(u), "v"(v), "v"(div));
+  asm volatile("v_cvt_scalef32_pk32_fp6_f16 %0, %1, %2" : "=&v"(r) : "v"(v), "v"(div));
   return r;
+}
+
+// One weight-operand lane from its four tiled-int4 dwords (dword i: k-offsets
+// 8i + j in the low nibble of byte j and 8i + 4 + j in its high nibble) -> the
+// e2m3 operand of w/2.  Nibble n (4-bit two's complement) XOR 8 is u = w + 8;
+// in the low mantissa bits of the fp16 number 1024 it reads 1024 + u (one
+// nibble higher, 1024 + 16u), so one packed fp16 add (or fma by 1/16) per two
+// values gives w exactly: 9 VALU per dword, no table.
+__device__ __forceinline__ v6i_ weight_operand6(const uint32_t (&dw)[4]) {
+  v32h_ h;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = dw[i], hi = dw[i] >> 8;
+    const v2h_ a = __builtin_bit_cast(v2h_, (lo & 0x000F000Fu) ^ 0x64086408u) - (_Float16)1032.0f;
+    const v2h_ c = __builtin_bit_cast(v2h_, (hi & 0x000F000Fu) ^ 0x64086408u) - (_Float16)1032.0f;
+    const v2h_ b = __builtin_elementwise_fma(__builtin_bit_cast(v2h_, (lo & 0x00F000F0u) ^ 0x64806480u),
+                                             v2h_{(_Float16)0.0625f, (_Float16)0.0625f},
+                                             v2h_{(_Float16)-72.0f, (_Float16)-72.0f});
+    const v2h_ d = __builtin_elementwise_fma(__builtin_bit_cast(v2h_, (hi & 0x00F000F0u) ^ 0x64806480u),
+                                             v2h_{(_Float16)0.0625f, (_Float16)0.0625f},
+                                             v2h_{(_Float16)-72.0f, (_Float16)-72.0f});
+    // k-offsets: a = (0, 2), b = (4, 6), c = (1, 3), d = (5, 7)
+    h[8 * i + 0] = a[0]; h[8 * i + 1] = a[1];
+    h[8 * i + 2] = b[0]; h[8 * i + 3] = b[1];
+    h[8 * i + 4] = c[0]; h[8 * i + 5] = c[1];
+    h[8 * i + 6] = d[0]; h[8 * i + 7] = d[1];
+  }
+  return pack6h(h, 2.0f);
 }
 
 __device__ __forceinline__ void store6(uint8_t* tile, int slot, const v6i_& p) {
@@ -137,27 +177,24 @@ __global__ __launch_bounds__(256) void msd_prep64_kernel(const uint16_t* __restr
 #pragma unroll
     for (int e = 0; e < 32; ++e) mx = fmaxf(mx, fabsf(a[e]));
     const float amax = fmaxf(mx, __shfl_xor(mx, 32));   // exact: max of the two halves
-    v16f_ lv[3][2];
+    float lv[3][32];
 #pragma unroll
     for (int l = 0; l < 3; ++l)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) lv[l][0][e] = lv[l][1][e] = 0.0f;
+      for (int e = 0; e < 32; ++e) lv[l][e] = 0.0f;
     if (amax > 0.0f) {
       const float rcp = msd_recip(amax);
 #pragma unroll
-      for (int e = 0; e < 32; ++e) {
-        float r1, r2, r3;
-        msd_expand_f(a[e], amax, rcp, r1, r2, r3);
-        lv[0][e / 16][e % 16] = r1;
-        lv[1][e / 16][e % 16] = r2;
-        lv[2][e / 16][e % 16] = r3;
-      }
+      for (int e = 0; e < 32; ++e) msd_expand_f(a[e], amax, rcp, lv[0][e], lv[1][e], lv[2][e]);
     }
     const int rb = mt / RT, rt = mt % RT;
 #pragma unroll
     for (int l = 0; l < 3; ++l) {
+      v32h_ hv;                                        // levels in slot order (exact in fp16)
+#pragma unroll
+      for (int e = 0; e < 32; ++e) hv[e] = (_Float16)lv[l][8 * (e / 8) + kSlotK[e % 8]];
       uint8_t* tile = x_t + ((((int64_t)rb * G + g) * 3 + l) * RT + rt) * TILE;
-      store6(tile, lane, pack6(lv[l][0], lv[l][1], 1.0f));
+      store6(tile, lane, pack6h(hv, 1.0f));
     }
     if (h == 0) {
       float* q = q_t + (((int64_t)g * (Mpad / BM) + rb) * 3) * BM + (m % BM);
@@ -194,19 +231,10 @@ __global__ __launch_bounds__(256) void msd_prep64_kernel(const uint16_t* __restr
   for (int step = 0; step < 2; ++step) {
     const int g = 2 * kb + step;
     if (g >= G) break;                                   // K % 128 == 64: one group in the last block
-    v16f_ w[2];
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int32_t dw[2] = {(int32_t)(step ? c[half].z : c[half].x), (int32_t)(step ? c[half].w : c[half].y)};
-      // element j = 8*d + jj: low nibble of byte jj (jj < 4), high nibble of byte jj-4
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int jj = j % 8;
-        w[half][j] = (float)(int32_t)__builtin_amdgcn_sbfe(dw[j / 8], jj < 4 ? 8 * jj : 8 * (jj - 4) + 4, 4);
-      }
-    }
+    const uint32_t dw[4] = {step ? c[0].z : c[0].x, step ? c[0].w : c[0].y,
+                            step ? c[1].z : c[1].x, step ? c[1].w : c[1].y};
     uint8_t* tile = w_t + (((int64_t)(ct / CT) * G + g) * CT + (ct % CT)) * TILE;
-    store6(tile, lane, pack6(w[0], w[1], 2.0f));
+    store6(tile, lane, weight_operand6(dw));
   }
 }
 
@@ -432,18 +460,276 @@ __global__ __launch_bounds__(64 * WAVES_M * p64::WAVES_N, 1) void msd_gemm64_ker
   }
 }
 
+// ---------------------------------------------------------------- GEMM, weights converted in the kernel
+// With one or two row blocks (M <= 256) every weight is used by one or two
+// workgroups, so converting the whole weight matrix into operand tiles ahead
+// of the GEMM (read K*N/2, write 3*K*N/4 bytes, read again) costs more than
+// the GEMM's own use of it.  This variant reads the tiled int4 weights itself
+// and converts them to e2m3 operands one stage ahead of their use:
+//   iteration s:  waves 0-3 convert the int4 block of stage s+1 (loaded into
+//                 their registers during iteration s-1; column tile w, both
+//                 groups) into the e2m3 buffer of the other parity; copies
+//                 (global_load_lds) of stage s+1's x operands, level weights
+//                 and scales; waves 0-3 load the int4 block of stage s+2; all
+//                 16 waves compute stage s; one barrier.
+// The int4 loads are the last memory operations of an iteration and stay in
+// flight across its barrier (the wait before it leaves them outstanding).
+// Buffers: x operands, level weights, scales and e2m3 weights double, 103 KB
+// of LDS.  Workgroup tile 128 rows x 128 columns, 16 waves of one 32x32 tile
+// each.
+namespace p64w {
+constexpr int BN = 128;
+constexpr int CT = BN / 32;                 // column tiles of 32: 4
+constexpr int WF_GROUP = CT * p64::TILE;    // e2m3 weight operands of a group: 6 KB
+constexpr int X_STAGE = 2 * p64::X_GROUP;   // 36 KB
+constexpr int XPW = 3;                      // 1 KB x pieces per wave (48 >= 36)
+}  // namespace p64w
+
+template <bool YINT>
+__global__ __launch_bounds__(1024, 1) void msd_gemm64w_kernel(
+    const uint8_t* __restrict__ x_t, const float* __restrict__ q_t,
+    const uint8_t* __restrict__ wt, const uint16_t* __restrict__ scale, int M, int Mpad, int K,
+    int N, int g_begin, int g_end, int mblocks, int nblocks, uint16_t* __restrict__ y,
+    int32_t* __restrict__ y_int) {
+  using namespace p64;
+  using namespace p64w;
+  static_assert(16 * XPW * 1024 >= X_STAGE, "x pieces");
+
+  // One variable per buffer, named at compile time in every access (the
+  // stage loop is unrolled by two), so that the compiler sees the reads of
+  // one parity apart from the copies in flight into the other.
+  __shared__ __attribute__((aligned(16))) uint8_t sX0[X_STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sX1[X_STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sWf0[2 * WF_GROUP];
+  __shared__ __attribute__((aligned(16))) uint8_t sWf1[2 * WF_GROUP];
+  __shared__ __attribute__((aligned(16))) float sQ0[2 * 3 * BM];
+  __shared__ __attribute__((aligned(16))) float sQ1[2 * 3 * BM];
+  __shared__ __attribute__((aligned(16))) uint16_t sS0[2 * BN];
+  __shared__ __attribute__((aligned(16))) uint16_t sS1[2 * BN];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / CT;                    // row tile of 32
+  const int wn = wave % CT;                    // column tile of 32
+  const bool converter = wave < CT;            // wave-uniform
+
+  // tile order: as the other GEMMs (contiguous ranges per XCD, bands of BAND
+  // row blocks, column-major within a band); speed only
+  const int total = mblocks * nblocks;
+  int t = blockIdx.x;
+  if (total % NXCD == 0) t = (blockIdx.x % NXCD) * (total / NXCD) + blockIdx.x / NXCD;
+  const int band_tiles = BAND * nblocks;
+  const int band = t / band_tiles;
+  const int in_band = t % band_tiles;
+  const int band_rows = min(BAND, mblocks - band * BAND);
+  const int rb = band * BAND + in_band % band_rows;
+  const int cb = in_band / band_rows;
+  const int m0 = rb * BM, n0 = cb * BN;
+  const int G = K / 64;
+  const int RB = Mpad / BM;
+  const int KB = (K + kTileRows - 1) / kTileRows;
+
+  // stage s: 128-row block kb0 + s, groups 2(kb0 + s) and 2(kb0 + s) + 1
+  const int kb0 = g_begin / 2;
+  const int nst = (g_end + 1) / 2 - kb0;
+  const uint8_t* x_run = x_t + (int64_t)rb * G * X_GROUP;
+  const uint32_t s_off = 2u * (uint32_t)min(n0 + 2 * lane, N - 2);   // this lane's scale pair
+
+  // Converter wave c, lane l: column 32c + l%32 of the block, k-half l/32 of
+  // each group; its int4 tile (16 columns; tiles past N read a valid tile,
+  // their outputs are not stored) and the chunk lanes of k-quarters 2(l/32)
+  // and 2(l/32)+1, whose 16 bytes hold the lane's 32 k of both groups.
+  const int wcol = wn * 32 + (lane & 31);
+  const int wtile = min(cb * (BN / kTileCols) + wcol / kTileCols, N / kTileCols - 1);
+  const uint8_t* w_lane = wt + (int64_t)wtile * KB * 1024 + ((wcol % kTileCols) + 32 * (lane >> 5)) * 16;
+
+  // x operands, level weights and scales of the existing groups of stage s
+  auto dma_x = [&](int s, uint8_t* sx, float* sq, uint16_t* ss) {
+    const int g0 = 2 * (kb0 + s);
+    const int ng = min(2, G - g0);
+#pragma unroll
+    for (int c = 0; c < XPW; ++c) {
+      const int p = wave * XPW + c;                         // wave-uniform
+      if (p < ng * (X_GROUP / 1024))
+        __builtin_amdgcn_global_load_lds(x_run + (int64_t)g0 * X_GROUP + p * 1024 + lane * 16,
+                                         sx + p * 1024, 16, 0, 0);
+    }
+    constexpr int PER = Q_GROUP / 256 + 1;                  // 6 level-weight copies + 1 scale copy
+    if (wave < 2 * PER) {
+      const int gi = wave / PER, kind = wave % PER;
+      const int g = g0 + gi;
+      if (gi < ng) {
+        if (kind < PER - 1) {
+          const uint8_t* src = reinterpret_cast<const uint8_t*>(q_t) + ((int64_t)g * RB + rb) * Q_GROUP + kind * 256;
+          __builtin_amdgcn_global_load_lds(src + lane * 4, reinterpret_cast<uint8_t*>(sq + gi * 3 * BM) + kind * 256, 4, 0, 0);
+        } else if (!YINT) {
+          const uint8_t* row = reinterpret_cast<const uint8_t*>(scale) + (int64_t)g * N * 2;
+          __builtin_amdgcn_global_load_lds(row + s_off, reinterpret_cast<uint8_t*>(ss + gi * BN), 4, 0, 0);
+        }
+      }
+    }
+  };
+  // the int4 chunk lanes of stage s (converter waves)
+  auto load_w = [&](int s, uint4 (&wr)[2]) {
+    const uint8_t* p = w_lane + (int64_t)(kb0 + s) * 1024;
+    wr[0] = *reinterpret_cast<const uint4*>(p);
+    wr[1] = *reinterpret_cast<const uint4*>(p + 256);
+  };
+  // int4 chunk lanes -> the e2m3 operand lanes of both groups (step st:
+  // dwords 2st, 2st+1 of each chunk lane)
+  auto convert = [&](const uint4 (&wr)[2], uint8_t* swf) {
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const uint32_t dw[4] = {st ? wr[0].z : wr[0].x, st ? wr[0].w : wr[0].y,
+                              st ? wr[1].z : wr[1].x, st ? wr[1].w : wr[1].y};
+      store6(swf + st * WF_GROUP + wn * TILE, lane, weight_operand6(dw));
+    }
+  };
+
+  float yacc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) yacc[i] = 0.0f;
+
+  // Steps 9-11 for group g (index gi in its stage).  The levels are
+  // multiplied and combined one after another, so that at most two 16-value
+  // MFMA results are live (registers: four waves per SIMD).
+  auto compute = [&](const uint8_t* sx, const uint8_t* swf, const float* sq, const uint16_t* ss, int gi,
+                     int g) {
+    const v8i_ wop = operand6(swf + gi * WF_GROUP + wn * TILE, lane);
+    auto level = [&](int l) {
+      const v8i_ xop = operand6(sx + gi * X_GROUP + (l * RT + wm) * TILE, lane);
+      const v16f_ d = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wop, xop, v16f_{}, 2, 2, 0, kScaleW, 0,
+                                                                       kScaleX);
+      // operands kept live past the MFMA (its result is not given their
+      // registers); their six defined dwords only, so that the undefined
+      // upper two (which may share registers with the int4 loads in flight)
+      // do not make the compiler wait for those loads
+#if defined(__HIP_DEVICE_COMPILE__)
+      asm volatile("" ::"v"(__builtin_shufflevector(wop, wop, 0, 1, 2, 3, 4, 5)),
+                   "v"(__builtin_shufflevector(xop, xop, 0, 1, 2, 3, 4, 5)), "v"(d));
+#endif
+      return d;
+    };
+    if constexpr (YINT) {
+      const int m = m0 + wm * 32 + (lane & 31);
+      const int64_t gi_out = g - g_begin;
+#pragma unroll
+      for (int l = 0; l < 3; ++l) {
+        const v16f_ d = level(l);
+        if (m < M) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int n = n0 + wn * 32 + 8 * (i / 4) + 4 * (lane >> 5) + (i % 4);
+            if (n < N) y_int[((gi_out * 3 + l) * M + m) * (int64_t)N + n] = (int32_t)d[i];
+          }
+        }
+      }
+    } else {
+      const int r0 = gi * 3 * BM + wm * 32 + (lane & 31);
+      const float q0 = sq[r0], q1 = sq[r0 + BM], q2 = sq[r0 + 2 * BM];
+      uint2 sr[4];                                          // 16 scales: 4 runs of 4 columns
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        sr[r] = *reinterpret_cast<const uint2*>(ss + gi * BN + wn * 32 + 8 * r + 4 * (lane >> 5));
+      const v16f_ d0 = level(0);
+      const v16f_ d1 = level(1);
+      float tt[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) tt[i] = __builtin_fmaf(d1[i], q1, d0[i] * q0);
+      const v16f_ d2 = level(2);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t sw2 = (i % 4) < 2 ? sr[i / 4].x : sr[i / 4].y;
+        const float sc = half_bits_to_float((i % 2) ? (sw2 >> 16) : (sw2 & 0xffffu));
+        yacc[i] = __builtin_fmaf(__builtin_fmaf(d2[i], q2, tt[i]), sc, yacc[i]);
+      }
+    }
+  };
+
+  // Iteration s from the buffers of parity B = s % 2 (see the top of this
+  // kernel).  The barrier is issued without a fence (a workgroup fence would
+  // wait for the int4 loads in flight); the compiler-level memory barriers
+  // keep every LDS access on its side, and the explicit wait drains the LDS
+  // operations and every copy except, in the converter waves, the two int4
+  // loads issued last.
+  uint4 wr[2];
+  auto iteration = [&](auto P, int s) {
+    constexpr int B = decltype(P)::value;
+    uint8_t* sx = B ? sX1 : sX0;
+    uint8_t* sxn = B ? sX0 : sX1;
+    uint8_t* swf = B ? sWf1 : sWf0;
+    uint8_t* swfn = B ? sWf0 : sWf1;
+    float* sq = B ? sQ1 : sQ0;
+    float* sqn = B ? sQ0 : sQ1;
+    uint16_t* ss = B ? sS1 : sS0;
+    uint16_t* ssn = B ? sS0 : sS1;
+    if (converter && s + 1 < nst) convert(wr, swfn);
+    if (s + 1 < nst) dma_x(s + 1, sxn, sqn, ssn);
+    const bool w_ahead = converter && s + 2 < nst;          // wave-uniform
+    if (w_ahead) load_w(s + 2, wr);
+    const int g0 = 2 * (kb0 + s);
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      const int g = g0 + gi;
+      if (g >= g_begin && g < g_end) compute(sx, swf, sq, ss, gi, g);   // wave-uniform
+    }
+    // s_waitcnt immediates: vmcnt (bits 3:0) 2 or 0, expcnt (6:4) 7 = no
+    // wait, lgkmcnt (11:8) 0
+    if (w_ahead)
+      __builtin_amdgcn_s_waitcnt(0x0072);
+    else
+      __builtin_amdgcn_s_waitcnt(0x0070);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  dma_x(0, sX0, sQ0, sS0);
+  if (converter) {
+    load_w(0, wr);
+    convert(wr, sWf0);
+    if (nst > 1) load_w(1, wr);
+  }
+  __syncthreads();
+  for (int s = 0; s < nst; s += 2) {
+    iteration(std::integral_constant<int, 0>{}, s);
+    if (s + 1 < nst) iteration(std::integral_constant<int, 1>{}, s + 1);
+  }
+
+  if constexpr (!YINT) {
+    const int m = m0 + wm * 32 + (lane & 31);
+    if (m < M) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int n = n0 + wn * 32 + 8 * r + 4 * (lane >> 5);   // 4 consecutive columns
+        if (n >= N) continue;
+        const uint32_t lo = (uint32_t)float_to_half_bits(yacc[4 * r]) |
+                            ((uint32_t)float_to_half_bits(yacc[4 * r + 1]) << 16);
+        const uint32_t hi = (uint32_t)float_to_half_bits(yacc[4 * r + 2]) |
+                            ((uint32_t)float_to_half_bits(yacc[4 * r + 3]) << 16);
+        *reinterpret_cast<uint2*>(y + (int64_t)m * N + n) = make_uint2(lo, hi);
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- launchers
 
+// Up to two row blocks: weights converted in the GEMM (128-column blocks);
+// more: converted once by the preparation kernel, column blocks of 256 when
+// that still gives at least one workgroup per CU, else of 128.
 PrefillLayout prefill64_layout(int64_t M, int64_t K, int64_t N) {
   PrefillLayout L;
   L.mpad = (M + p64::BM - 1) / p64::BM * p64::BM;
+  L.w_in_gemm = L.mpad / p64::BM <= 2;
   const int64_t tiles256 = (L.mpad / p64::BM) * ((N + 255) / 256);
-  L.bn = tiles256 >= 256 ? 256 : 128;
+  L.bn = (!L.w_in_gemm && tiles256 >= 256) ? 256 : 128;
   L.npad = (N + L.bn - 1) / L.bn * L.bn;
   const int64_t G = K / 64;
   L.a_bytes = (size_t)(3 * (L.mpad / 32) * G) * p64::TILE;
   L.q_bytes = (size_t)(G * (L.mpad / p64::BM)) * p64::Q_GROUP;
-  L.b_bytes = (size_t)((L.npad / 32) * G) * p64::TILE;
+  L.b_bytes = L.w_in_gemm ? 0 : (size_t)((L.npad / 32) * G) * p64::TILE;
   return L;
 }
 
@@ -452,7 +738,8 @@ hipError_t launch_prefill64_prep(const void* x, const void* w, int64_t M, int64_
                                  hipStream_t stream) {
   const int64_t G = K / 64;
   const int64_t xwaves = (L.mpad / 32) * G;
-  const int64_t wwaves = (L.npad / 32) * tiled_kblocks(K);  // one wave per (column tile, 128-row block)
+  // one wave per (column tile, 128-row block), unless the GEMM converts them
+  const int64_t wwaves = L.w_in_gemm ? 0 : (L.npad / 32) * tiled_kblocks(K);
   const unsigned blocks = (unsigned)((xwaves + wwaves + 3) / 4);
   hipLaunchKernelGGL(msd_prep64_kernel, dim3(blocks), dim3(256), 0, stream,
                      static_cast<const uint16_t*>(x), static_cast<const uint8_t*>(w), (int)M,
@@ -461,7 +748,7 @@ hipError_t launch_prefill64_prep(const void* x, const void* w, int64_t M, int64_
 }
 
 hipError_t launch_prefill64_gemm(const uint8_t* x_t, const float* q_t, const uint8_t* w_t,
-                                 const void* scale, int64_t M, int64_t K, int64_t N,
+                                 const void* w_tiled, const void* scale, int64_t M, int64_t K, int64_t N,
                                  const PrefillLayout& L, int64_t g_begin, int64_t g_end, void* y,
                                  int32_t* y_int, hipStream_t stream) {
   if (L.bn != 128 && L.bn != 256) return hipErrorInvalidValue;
@@ -471,6 +758,17 @@ hipError_t launch_prefill64_gemm(const uint8_t* x_t, const float* q_t, const uin
   const uint16_t* sp = static_cast<const uint16_t*>(scale);
   uint16_t* yp = static_cast<uint16_t*>(y);
   const int m = (int)M, mp = (int)L.mpad, k = (int)K, n = (int)N, gb = (int)g_begin, ge = (int)g_end;
+  if (L.w_in_gemm) {
+    if (L.bn != p64w::BN) return hipErrorInvalidValue;
+    const uint8_t* wp = static_cast<const uint8_t*>(w_tiled);
+    if (y_int)
+      hipLaunchKernelGGL(msd_gemm64w_kernel<true>, grid, dim3(1024), 0, stream, x_t, q_t, wp, sp, m,
+                         mp, k, n, gb, ge, mblocks, nblocks, yp, y_int);
+    else
+      hipLaunchKernelGGL(msd_gemm64w_kernel<false>, grid, dim3(1024), 0, stream, x_t, q_t, wp, sp, m,
+                         mp, k, n, gb, ge, mblocks, nblocks, yp, y_int);
+    return hipGetLastError();
+  }
   // stages: 2 groups at BN = 256 (2 x 64 KB of LDS), 3 at BN = 128 (2 x 77 KB);
   // at BN = 128 a wave holds one 32x32 output tile, 16 waves per workgroup
   // (four per SIMD hide the MFMA and copy latencies of the short groups)
