@@ -257,6 +257,33 @@ def test_ragged_shapes(torch_dev, M, K, N, gs):
         assert np.array_equal(yi.cpu().numpy(), ref_yi), f"path {p} Y_int"
 
 
+# Group size 64 with many row blocks: the weights are converted by the
+# preparation kernel and the GEMM runs 128 x 256 tiles (at least 256 of them);
+# K = 192 leaves a last stage of one group.  Sampled rows against the oracle.
+WIDE64 = [(512, 192, 16384), (640, 320, 13312)]
+
+
+@pytest.mark.parametrize("M,K,N", WIDE64, ids=[f"M{c[0]}K{c[1]}N{c[2]}" for c in WIDE64])
+def test_group64_wide_tiles(torch_dev, M, K, N):
+    import weight_only_quantized_msd_amd as W
+    torch = torch_dev
+    gs = 64
+    d = datagen.random_case(M, K, N, gs, seed=M + K)
+    x, w, s = to_dev(torch, d)
+    G = K // gs
+    rows = sample_rows(M, 12, 5)
+    announce(f"group64 wide M={M} K={K} N={N}")
+    y = W.wqbmm_a16w4_msd_path(x, w, s, gs, PREFILL)
+    yi = W.wqbmm_a16w4_msd_yint(x, w, gs, G - 1, G, path=PREFILL)
+    torch.cuda.synchronize()
+    y32, _ = oracle.matmul(d["x"], d["w_packed"], d["scale"], gs, rows=rows)
+    check_y(y.cpu().numpy()[rows], y32, "group64 wide")
+    ra, _ = oracle.decompose(d["x"][rows], gs)
+    ref = oracle.yint(ra, d["w"], gs, G - 1, G)
+    got = yi.cpu().numpy()[:, :, rows, :]
+    assert np.array_equal(got, ref), f"{np.count_nonzero(got != ref)} words differ"
+
+
 def test_zero_weights_give_exact_zero(torch_dev):
     import weight_only_quantized_msd_amd as W
     torch = torch_dev
