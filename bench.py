@@ -117,6 +117,26 @@ def timed_graph(torch, stream, fn_list, steps, warmup):
     return (t1 - t0) * 1e3 / steps, e0.elapsed_time(e1) / steps
 
 
+def prefill_prep_bytes(M, K, N, gs):
+    """Algorithmic bytes of the prefill preparation kernel: it reads x and
+    writes the level operand tiles (1536 bytes each: 16 rows x 128 k at group
+    size 128, 32 rows x 64 k at group size 64) and the level weights (fp32,
+    three per row and group); unless the GEMM converts the weights itself (group
+    size 64 with at most two 128-row blocks), it also reads the tiled int4
+    weights and writes their operand tiles (columns padded to the GEMM's
+    column block of 256, or 128 when 256 would give fewer than 256 tiles)."""
+    G = K // gs
+    per = 16 if gs == 128 else 32
+    mpad = -(-M // 128) * 128
+    w_in_gemm = gs == 64 and mpad // 128 <= 2
+    bn = 256 if (not w_in_gemm and (mpad // 128) * -(-N // 256) >= 256) else 128
+    npad = -(-N // bn) * bn
+    b = 2 * M * K + 1536 * (3 * mpad // per) * G + 12 * mpad * G
+    if not w_in_gemm:
+        b += K * N // 2 + 1536 * (npad // per) * G
+    return b
+
+
 def cpu_baseline(name, M, K, N, gs, seconds):
     import numpy as np
     import oracle
@@ -218,46 +238,55 @@ def main():
     extra = {}
     sha = kernel_sources_sha()
     traffic, tinfo = read_traffic(args.workload, sha)
+
+    # The path's kernels timed alone, each in its own graph over the rotating
+    # sets (MALL-cold): stage 1 = the operand kernel, stage 2 = the
+    # contraction on the operands the last stage 1 left in this stream's
+    # workspace (rotating scale, y and, for the weights, w).  The fused decode
+    # kernel (M <= 4) is stage 2 alone.
+    def stage(st, k):
+        def f():
+            rc = lib.wqbmm_a16w4_msd_profile_stage(st["x"].data_ptr(), st["w"].data_ptr(),
+                                                   st["s"].data_ptr(), gs, M, K, N,
+                                                   st["y"].data_ptr(), path, k, sptr)
+            if rc:
+                raise W.WqbmmError(rc, "wqbmm_a16w4_msd_profile_stage")
+        return f
+
+    G = K // gs
+    two_kernels = path == 2 or M > 4
+    prep_ms = None
+    if two_kernels:
+        _, prep_ms = timed_graph(torch, stream, [stage(st, 1) for st in sets], args.steps, args.warmup)
+    _, kern_ms = timed_graph(torch, stream, [stage(st, 2) for st in sets], args.steps, args.warmup)
     if path == 1:
-        kern_ms = ev_step
-        achieved = alg["bytes"] / (kern_ms * 1e-3) / 1e9
+        if M > 4:
+            # contraction kernel: tiled int4 weights, scales, the 16-row level
+            # operands (three int4 levels) and level weights once, y
+            kb = -(-K // 128)
+            kbytes = alg["w_bytes"] + 2 * G * N + 3 * 1024 * kb + 192 * G + 2 * M * N
+            kname = "msd_decode_gemv_kernel"
+            extra["prep"] = {"kernel": "msd_decode_operands_kernel", "avg_kernel_us": round(prep_ms * 1e3, 3),
+                             "algorithmic_bytes_per_launch": 2 * M * K + 3 * 1024 * kb + 192 * G}
+        else:
+            kbytes = alg["bytes"]
+            kname = "msd_decode_kernel"
+        achieved = kbytes / (kern_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "msd_decode_kernel", "avg_kernel_us": round(kern_ms * 1e3, 3),
-                "algorithmic_bytes_per_launch": alg["bytes"]}
+                "kernel": kname, "avg_kernel_us": round(kern_ms * 1e3, 3),
+                "algorithmic_bytes_per_launch": kbytes}
     else:
-        # The two kernels of the prefill path timed alone (each its own graph):
-        # the preparation kernel over the rotating sets (MALL-cold), and the
-        # GEMM kernel on the operands the last preparation left in this
-        # stream's workspace (rotating scale and y).
-        def stage(st, k):
-            def f():
-                rc = lib.wqbmm_a16w4_msd_profile_stage(st["x"].data_ptr(), st["w"].data_ptr(),
-                                                       st["s"].data_ptr(), gs, M, K, N,
-                                                       st["y"].data_ptr(), k, sptr)
-                if rc:
-                    raise W.WqbmmError(rc, "wqbmm_a16w4_msd_profile_stage")
-            return f
-
-        _, prep_ms = timed_graph(torch, stream, [stage(st, 1) for st in sets], args.steps, args.warmup)
-        _, gemm_ms = timed_graph(torch, stream, [stage(st, 2) for st in sets], args.steps, args.warmup)
         # The GEMM contracts on FP6 (e2m3) MFMAs, so its roofline peak is the
         # dense FP6 rate; the fraction of the int8 rate is reported beside it.
-        achieved = alg["exec_i8_ops"] / (gemm_ms * 1e-3) / 1e12
+        achieved = alg["exec_i8_ops"] / (kern_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP6_PEAK_TOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / FP6_PEAK_TOPS, 4), "traffic": traffic,
                 "kernel": "msd_gemm_kernel", "mfma_dtype": "fp6 e2m3",
-                "avg_kernel_us": round(gemm_ms * 1e3, 3),
+                "avg_kernel_us": round(kern_ms * 1e3, 3),
                 "algorithmic_ops_per_launch": alg["exec_i8_ops"],
                 "frac_of_i8_peak": round(achieved / I8_PEAK_TOPS, 4)}
-        # preparation kernel: reads x and the tiled int4 weights, writes the
-        # operand tiles (1536 bytes each: 16 rows or columns x 128 k at group
-        # size 128, 32 x 64 k at group size 64) and the level weights
-        G = K // gs
-        per = 16 if gs == 128 else 32
-        mpad = -(-M // 128) * 128
-        npad = -(-N // 256) * 256 if (mpad // 128) * -(-N // 256) >= 256 else -(-N // 128) * 128
-        prep_bytes = 2 * M * K + K * N // 2 + 1536 * (3 * mpad // per + npad // per) * G + 12 * mpad * G
+        prep_bytes = prefill_prep_bytes(M, K, N, gs)
         extra["prep"] = {"kernel": "msd_prep_kernel", "avg_kernel_us": round(prep_ms * 1e3, 3),
                          "achieved_GBps": round(prep_bytes / (prep_ms * 1e-3) / 1e9, 1)}
     if tinfo is not None and not isinstance(tinfo, str):

@@ -77,7 +77,7 @@ typedef enum wqbmm_status {
 /* Kernel path selector for the *_path / *_yint entry points. */
 typedef enum wqbmm_path {
   WQBMM_PATH_AUTO = 0,     /* what wqbmm_a16w4_msd picks (wqbmm_select_path)      */
-  WQBMM_PATH_DECODE = 1,   /* fused split-K decode kernel; valid for M <= 16     */
+  WQBMM_PATH_DECODE = 1,   /* weight-streaming kernels; valid for M <= 16        */
   WQBMM_PATH_PREFILL = 2   /* operand preparation + MFMA GEMM; any M            */
 } wqbmm_path;
 
@@ -145,24 +145,26 @@ wqbmm_status wqbmm_a16w4_msd_yint(const void* x, const void* w_tiled,
                                   int32_t* y_int, int path, void* stream);
 
 /*
- * Profiling support: run ONE stage of the prefill path (the path for large
- * M), so that its kernels can be timed separately.
- *   stage 1: the preparation kernel only (WQBMM-Exp page §6.1 UnfoldA plus the
- *            weight conversion): x -> the three levels of §4.1 steps 1-8 and
- *            A_max, w -> MFMA operand tiles, into this stream's workspace;
- *            y is not written.
- *   stage 2: the GEMM kernel only (§4.1 steps 9-11) on the operands that the
- *            most recent prefill-path call on the SAME stream prepared; y is
- *            written.  Returns WQBMM_ERR_INVALID if that call had a different
- *            shape or group size (or none happened).  The operands of x and w
- *            themselves are not re-read in this stage.
- * Arguments and rules as for wqbmm_a16w4_msd; other stage values give
+ * Profiling support: run ONE stage of a kernel path (WQBMM_PATH_* as in
+ * wqbmm_a16w4_msd_path), so that its kernels can be timed separately.
+ *   stage 1: the operand kernel only (WQBMM-Exp page §6.1 UnfoldA: x -> the
+ *            three levels of §4.1 steps 1-8 and the rows' step-10 level
+ *            weights; on the prefill path also w -> MFMA operand tiles), into
+ *            this stream's workspace; y is not written.  The decode path at
+ *            M <= 4 is one fused kernel: nothing is launched.
+ *   stage 2: the contraction kernel only (§4.1 steps 9-11) on the operands
+ *            that the most recent call of the same path on the SAME stream
+ *            prepared; y is written.  Returns WQBMM_ERR_INVALID if that call
+ *            had another path, shape or group size (or none happened).  x is
+ *            not re-read in this stage.  The decode path at M <= 4 runs its
+ *            fused kernel (all of steps 1-11).
+ * Arguments and rules as for wqbmm_a16w4_msd_path; other stage values give
  * WQBMM_ERR_INVALID.
  */
 wqbmm_status wqbmm_a16w4_msd_profile_stage(const void* x, const void* w_tiled,
                                            const void* antiquant_scale, int64_t group_size,
                                            int64_t M, int64_t K, int64_t N, void* y,
-                                           int stage, void* stream);
+                                           int path, int stage, void* stream);
 
 /* The path wqbmm_a16w4_msd takes for this shape (WQBMM_PATH_DECODE or
  * WQBMM_PATH_PREFILL).  Pure host function. */

@@ -126,13 +126,16 @@ def test_yint_validation(over, want):
     (dict(N=40), L.WQBMM_ERR_INVALID),
     (dict(y=MIS), L.WQBMM_ERR_INVALID),
     (dict(gs=96, K=192), L.WQBMM_ERR_UNSUPPORTED),
+    (dict(path=3), L.WQBMM_ERR_INVALID),
+    (dict(path=-1), L.WQBMM_ERR_INVALID),
+    (dict(path=L.WQBMM_PATH_DECODE, M=17), L.WQBMM_ERR_INVALID),
     (dict(M=0, x=0, y=0), L.WQBMM_OK),
 ])
 def test_profile_stage_validation(over, want):
-    a = dict(x=FAKE, w=FAKE, s=FAKE, gs=64, M=2, K=256, N=64, y=FAKE, stage=1)
+    a = dict(x=FAKE, w=FAKE, s=FAKE, gs=64, M=2, K=256, N=64, y=FAKE, path=0, stage=1)
     a.update(over)
     st = L.wqbmm_a16w4_msd_profile_stage_raw(a["x"], a["w"], a["s"], a["gs"], a["M"], a["K"],
-                                             a["N"], a["y"], a["stage"], None)
+                                             a["N"], a["y"], a["path"], a["stage"], None)
     assert st == want
 
 

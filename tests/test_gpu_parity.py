@@ -340,25 +340,35 @@ def test_side_stream_and_alternating_shapes(torch_dev):
             assert torch.equal(y_side.view(torch.int16), ref.view(torch.int16)), name
 
 
-@pytest.mark.parametrize("name", ["decode_m16", "prefill_m2048", "outlier_m128"])
-def test_profile_stages_compose_to_prefill_path(torch_dev, name):
-    """Stage 1 (preparation) then stage 2 (GEMM) give the same bits as the
-    one-call prefill path; stage 2 refuses operands prepared for another shape."""
+@pytest.mark.parametrize("name,path", [("decode_m16", PREFILL), ("prefill_m2048", PREFILL),
+                                       ("outlier_m128", PREFILL), ("decode_m16", DECODE),
+                                       ("ffn_up_m16", DECODE), ("decode_m1", DECODE)])
+def test_profile_stages_compose_to_path(torch_dev, name, path):
+    """Stage 1 (operand kernel) then stage 2 (contraction) give the same bits
+    as the one-call path; stage 2 refuses operands prepared for another shape
+    or by another path (the fused kernel at M <= 4 needs no operands)."""
     import weight_only_quantized_msd_amd as W
     torch = torch_dev
     d = workload(name)
     gs = d["group_size"]
     x, w, s = to_dev(torch, d)
-    announce(f"profile stages {name}")
-    y1 = W.wqbmm_a16w4_msd_path(x, w, s, gs, PREFILL)
-    W.wqbmm_a16w4_msd_profile_stage(x, w, s, gs, 1)
-    y2 = W.wqbmm_a16w4_msd_profile_stage(x, w, s, gs, 2)
-    y3 = W.wqbmm_a16w4_msd_profile_stage(x, w, s, gs, 2)   # operands stay prepared
+    announce(f"profile stages {name} path={path}")
+    y1 = W.wqbmm_a16w4_msd_path(x, w, s, gs, path)
+    W.wqbmm_a16w4_msd_profile_stage(x, w, s, gs, 1, path=path)
+    y2 = W.wqbmm_a16w4_msd_profile_stage(x, w, s, gs, 2, path=path)
+    y3 = W.wqbmm_a16w4_msd_profile_stage(x, w, s, gs, 2, path=path)   # operands stay prepared
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
     assert torch.equal(y1.view(torch.int16), y3.view(torch.int16))
+    if path == DECODE and d["M"] <= 4:
+        return
     with pytest.raises(W.WqbmmError):
-        W.wqbmm_a16w4_msd_profile_stage(x[: max(1, d["M"] // 2)].contiguous(), w, s, gs, 2)
+        W.wqbmm_a16w4_msd_profile_stage(x[: max(1, d["M"] // 2)].contiguous(), w, s, gs, 2, path=path)
+    other = PREFILL if path == DECODE else DECODE
+    if d["M"] <= 16:   # operands of the other path are not these
+        W.wqbmm_a16w4_msd_profile_stage(x, w, s, gs, 1, path=other)
+        with pytest.raises(W.WqbmmError):
+            W.wqbmm_a16w4_msd_profile_stage(x, w, s, gs, 2, path=path)
 
 
 @pytest.mark.parametrize("name,path", [("decode_m16", DECODE), ("ffn_up_m16", DECODE),

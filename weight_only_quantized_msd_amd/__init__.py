@@ -139,9 +139,9 @@ def wqbmm_a16w4_msd_yint(x, w_tiled, group_size: int, g_begin: int, g_end: int,
 
 
 def wqbmm_a16w4_msd_profile_stage(x, w_tiled, antiquant_scale, group_size: int,
-                                  stage: int, y=None, stream=None):
-    """Run one stage of the prefill path (1: preparation, 2: GEMM on the
-    operands the last prefill call on this stream prepared); returns y."""
+                                  stage: int, path: int = 0, y=None, stream=None):
+    """Run one stage of a kernel path (1: operand kernel, 2: contraction on the
+    operands the last call of that path on this stream prepared); returns y."""
     import torch
     _require(x, torch.float16, 2, "x")
     _require(antiquant_scale, torch.float16, 2, "antiquant_scale")
@@ -151,6 +151,6 @@ def wqbmm_a16w4_msd_profile_stage(x, w_tiled, antiquant_scale, group_size: int,
         y = torch.empty((M, N), dtype=torch.float16, device=x.device)
     st = lib().wqbmm_a16w4_msd_profile_stage(x.data_ptr(), w_tiled.data_ptr(),
                                              antiquant_scale.data_ptr(), int(group_size), M, K, N,
-                                             y.data_ptr(), int(stage), _stream_ptr(stream))
+                                             y.data_ptr(), int(path), int(stage), _stream_ptr(stream))
     check(st, "wqbmm_a16w4_msd_profile_stage")
     return y

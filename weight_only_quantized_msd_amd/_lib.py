@@ -37,7 +37,7 @@ SIGNATURES = {
     "wqbmm_a16w4_msd_path": (_int, [_p, _p, _p, _i64, _i64, _i64, _i64, _p, _int, _p]),
     "wqbmm_a16w4_msd_prepass": (_int, [_p, _i64, _i64, _i64, _p, _p, _p]),
     "wqbmm_a16w4_msd_yint": (_int, [_p, _p, _i64, _i64, _i64, _i64, _i64, _i64, _p, _int, _p]),
-    "wqbmm_a16w4_msd_profile_stage": (_int, [_p, _p, _p, _i64, _i64, _i64, _i64, _p, _int, _p]),
+    "wqbmm_a16w4_msd_profile_stage": (_int, [_p, _p, _p, _i64, _i64, _i64, _i64, _p, _int, _int, _p]),
     "wqbmm_select_path": (_int, [_i64, _i64, _i64, _i64]),
     "wqbmm_status_string": (ctypes.c_char_p, [_int]),
     "wqbmm_version": (_int, []),
@@ -110,8 +110,8 @@ def wqbmm_a16w4_msd_yint_raw(x, w, group_size, M, K, N, g_begin, g_end, y_int, p
     return lib().wqbmm_a16w4_msd_yint(x, w, group_size, M, K, N, g_begin, g_end, y_int, path, stream)
 
 
-def wqbmm_a16w4_msd_profile_stage_raw(x, w, scale, group_size, M, K, N, y, stage, stream) -> int:
-    return lib().wqbmm_a16w4_msd_profile_stage(x, w, scale, group_size, M, K, N, y, stage, stream)
+def wqbmm_a16w4_msd_profile_stage_raw(x, w, scale, group_size, M, K, N, y, path, stage, stream) -> int:
+    return lib().wqbmm_a16w4_msd_profile_stage(x, w, scale, group_size, M, K, N, y, path, stage, stream)
 
 
 def wqbmm_select_path(M, K, N, group_size) -> int:

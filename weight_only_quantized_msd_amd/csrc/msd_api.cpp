@@ -74,7 +74,9 @@ struct Workspace {
   void* base = nullptr;
   size_t acc_bytes = 0;
   size_t scratch_bytes = 0;
-  // shape whose prefill operands the scratch region currently holds
+  // path and shape whose operands the scratch region currently holds
+  // (prep_path 0: none, WQBMM_PATH_DECODE or WQBMM_PATH_PREFILL)
+  int prep_path = 0;
   int64_t prep_gs = 0, prep_m = -1, prep_k = 0, prep_n = 0;
 };
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
@@ -112,7 +114,7 @@ wqbmm_status get_workspace(int dev, hipStream_t stream, size_t acc, size_t scrat
     ws.base = p;
     ws.acc_bytes = round_up(new_acc, 256);
     ws.scratch_bytes = round_up(new_scratch, 256);
-    ws.prep_m = -1;
+    ws.prep_path = 0;
   }
   *acc_out = static_cast<uint64_t*>(ws.base);
   *scratch_out = static_cast<uint8_t*>(ws.base) + ws.acc_bytes;
@@ -126,9 +128,50 @@ int resolve_path(int path, int64_t M, int64_t K, int64_t N, int64_t gs) {
 
 wqbmm_status launch_status(hipError_t e) { return e == hipSuccess ? WQBMM_OK : WQBMM_ERR_LAUNCH; }
 
+// Records (stage 0 or 1) or checks (stage 2) which path and shape the
+// operands in the scratch region of (dev, stream) belong to.
+wqbmm_status track_operands(int dev, hipStream_t stream, int path, int stage, int64_t gs, int64_t M,
+                            int64_t K, int64_t N) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  Workspace& ws = g_ws[std::make_pair(dev, stream)];
+  if (stage == 2)
+    return (ws.prep_path == path && ws.prep_gs == gs && ws.prep_m == M && ws.prep_k == K && ws.prep_n == N)
+               ? WQBMM_OK : WQBMM_ERR_INVALID;
+  ws.prep_path = path;
+  ws.prep_gs = gs; ws.prep_m = M; ws.prep_k = K; ws.prep_n = N;
+  return WQBMM_OK;
+}
+
 wqbmm_status run_prefill(int dev, const void* x, const void* w, const void* scale, int64_t gs,
                          int64_t M, int64_t K, int64_t N, int64_t g_begin, int64_t g_end, void* y,
                          int32_t* y_int, int stage, hipStream_t stream);
+
+// The decode path.  M <= 4: one fused kernel (stage 1 launches nothing);
+// 4 < M <= 16: the operand kernel (stage 1) and the contraction (stage 2).
+wqbmm_status run_decode(int dev, const void* x, const void* w, const void* scale, int64_t gs,
+                        int64_t M, int64_t K, int64_t N, int64_t g_begin, int64_t g_end, void* y,
+                        int32_t* y_int, int stage, hipStream_t stream) {
+  uint64_t* accum = nullptr;
+  uint8_t* scratch = nullptr;
+  wqbmm_status st;
+  if (M > 4) {
+    st = get_workspace(dev, stream, 0, wqbmm::decode_gemv_workspace_bytes((int)gs, K), &accum, &scratch);
+    if (st != WQBMM_OK) return st;
+    st = track_operands(dev, stream, WQBMM_PATH_DECODE, stage, gs, M, K, N);
+    if (st != WQBMM_OK) return st;
+    return launch_status(wqbmm::launch_decode_gemv(x, w, scale, (int)gs, M, K, N, g_begin, g_end, y,
+                                                   y_int, scratch, stage, stream));
+  }
+  if (stage == 1) return WQBMM_OK;
+  const DecodePlan plan = wqbmm::decode_plan((int)gs, M, K, N, g_begin, g_end);
+  const size_t abytes = y_int ? 0 : wqbmm::decode_accum_bytes(plan, M, N);
+  if (abytes) {
+    st = get_workspace(dev, stream, abytes, 0, &accum, &scratch);
+    if (st != WQBMM_OK) return st;
+  }
+  return launch_status(wqbmm::launch_decode(x, w, scale, (int)gs, M, K, N, g_begin, g_end, y,
+                                            y_int, accum, plan, stream));
+}
 
 // Steps 1-11 (or 1-9 with y_int) on one of the two kernel paths.
 wqbmm_status run(const void* x, const void* w, const void* scale, int64_t gs, int64_t M,
@@ -137,18 +180,8 @@ wqbmm_status run(const void* x, const void* w, const void* scale, int64_t gs, in
   int dev = -1;
   wqbmm_status st = check_device(&dev);
   if (st != WQBMM_OK) return st;
-  if (path == WQBMM_PATH_DECODE) {
-    const DecodePlan plan = wqbmm::decode_plan((int)gs, M, K, N, g_begin, g_end);
-    uint64_t* accum = nullptr;
-    uint8_t* scratch = nullptr;
-    const size_t abytes = y_int ? 0 : wqbmm::decode_accum_bytes(plan, M, N);
-    if (abytes) {
-      st = get_workspace(dev, stream, abytes, 0, &accum, &scratch);
-      if (st != WQBMM_OK) return st;
-    }
-    return launch_status(wqbmm::launch_decode(x, w, scale, (int)gs, M, K, N, g_begin, g_end, y,
-                                              y_int, accum, plan, stream));
-  }
+  if (path == WQBMM_PATH_DECODE)
+    return run_decode(dev, x, w, scale, gs, M, K, N, g_begin, g_end, y, y_int, 0, stream);
   // prefill: operand preparation into the workspace, then the MFMA GEMM
   return run_prefill(dev, x, w, scale, gs, M, K, N, g_begin, g_end, y, y_int, 0, stream);
 }
@@ -171,16 +204,8 @@ wqbmm_status run_prefill(int dev, const void* x, const void* w, const void* scal
   uint8_t* a_t = scratch + a_off;
   float* q_t = reinterpret_cast<float*>(scratch + q_off);
   uint8_t* b_t = scratch + b_off;
-  {
-    std::lock_guard<std::mutex> lk(g_mu);
-    Workspace& ws = g_ws[std::make_pair(dev, stream)];
-    if (stage == 2) {
-      if (ws.prep_gs != gs || ws.prep_m != M || ws.prep_k != K || ws.prep_n != N)
-        return WQBMM_ERR_INVALID;
-    } else {
-      ws.prep_gs = gs; ws.prep_m = M; ws.prep_k = K; ws.prep_n = N;
-    }
-  }
+  st = track_operands(dev, stream, WQBMM_PATH_PREFILL, stage, gs, M, K, N);
+  if (st != WQBMM_OK) return st;
   if (stage != 2) {
     st = launch_status(wqbmm::launch_prefill_prep(x, w, (int)gs, M, K, N, L, a_t, q_t, b_t, stream));
     if (st != WQBMM_OK || stage == 1) return st;
@@ -291,23 +316,30 @@ wqbmm_status wqbmm_a16w4_msd_yint(const void* x, const void* w_tiled, int64_t gr
 
 wqbmm_status wqbmm_a16w4_msd_profile_stage(const void* x, const void* w_tiled,
                                            const void* antiquant_scale, int64_t group_size,
-                                           int64_t M, int64_t K, int64_t N, void* y, int stage,
-                                           void* stream) {
-  if (stage < 1 || stage > 2) return WQBMM_ERR_INVALID;
+                                           int64_t M, int64_t K, int64_t N, void* y, int path,
+                                           int stage, void* stream) {
   if ((!x && M != 0) || !w_tiled || !antiquant_scale || (!y && M != 0))
     return WQBMM_ERR_NULLPTR;
   wqbmm_status st = check_shape(group_size, M, K, N);
   if (st != WQBMM_OK) return st;
   if (!aligned16(x) || !aligned16(w_tiled) || !aligned16(antiquant_scale) || !aligned16(y))
     return WQBMM_ERR_INVALID;
+  if (stage < 1 || stage > 2) return WQBMM_ERR_INVALID;
+  if (path < WQBMM_PATH_AUTO || path > WQBMM_PATH_PREFILL) return WQBMM_ERR_INVALID;
+  const int p = resolve_path(path, M, K, N, group_size);
+  if (p == WQBMM_PATH_DECODE && M > kDecodeMaxM) return WQBMM_ERR_INVALID;
   st = check_support(group_size);
   if (st != WQBMM_OK) return st;
   if (M == 0) return WQBMM_OK;
   int dev = -1;
   st = check_device(&dev);
   if (st != WQBMM_OK) return st;
-  return run_prefill(dev, x, w_tiled, antiquant_scale, group_size, M, K, N, 0,
-                     K / group_size, y, nullptr, stage, static_cast<hipStream_t>(stream));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p == WQBMM_PATH_DECODE)
+    return run_decode(dev, x, w_tiled, antiquant_scale, group_size, M, K, N, 0, K / group_size, y,
+                      nullptr, stage, s);
+  return run_prefill(dev, x, w_tiled, antiquant_scale, group_size, M, K, N, 0, K / group_size, y,
+                     nullptr, stage, s);
 }
 
 }  // extern "C"

@@ -1,4 +1,4 @@
-// msd_decode.hip -- fused MSD kernel for small M (decode, M <= 16).
+// msd_decode.hip -- fused MSD kernel for the smallest M (decode, M <= 4).
 //
 // WQBMM-Exp page (the page "WeightQuantBatchMatmulExperiment 算子深度解析：A16W4
 // PerGroup 伪量化 MatMul 的 MSD 算法与双模板流水设计", lpnh.cn/news/2294145):
@@ -18,22 +18,19 @@
 //               slice of x (R = WK*KBW*128 rows) in LDS;
 //   grid      = (column blocks) x (K-splits).
 // The decomposition is recomputed by every column block, M*R elements per
-// workgroup, and is VALU-bound; the split-K hand-off costs three dependent
-// device-memory round trips.  Two shapes balance them:
-//   M <= 4:  1 column tile x 16 waves x 2 blocks: R = 4096, so K <= 4096 needs
-//            no split and no hand-off (cheap to decompose at small M);
-//   M <= 16: 8 column tiles x 1 wave x 4 blocks: 128 columns share a 512-row
-//            decomposition; K-splits of 512 rows are handed off.
+// workgroup; at M <= 4 that is cheap, so a workgroup is 1 column tile x 16
+// waves x 2 blocks: R = 4096, and K <= 4096 needs no split and no hand-off.
+// (For 4 < M <= 16 the repeated decomposition would cost more than the
+// weight stream; that range decomposes x once in a kernel of its own, see
+// msd_decode_gemv.hip.)
 // The tiled layout makes each 16-byte chunk exactly a lane's B operand of
 // v_mfma_i32_16x16x64_i8 for two 64-row steps (16*w per byte after masking the
 // nibbles), so the weights need no transposition.
-// Rows of the MFMA A operand ("slots"):
-//   LAYOUT 0 (M <= 4):  slot 4*m + level, one 16-row tile; the levels of a
-//                       row land in elements 0..2 of one lane's accumulator;
-//   LAYOUT 1 (M <= 16): tile = level, slot = m, three tiles.
+// Rows of the MFMA A operand ("slots"): slot 4*m + level, one 16-row tile;
+// the levels of a row land in elements 0..2 of one lane's accumulator.
 //
 // Split-K: the WK waves of a column tile are summed in LDS; when K is split
-// over several workgroups, each adds its partial, as a 2^-24 fixed-point
+// over several workgroups (K > 4096), each adds its partial, as a 2^-24 fixed-point
 // integer, into a per-output int64 accumulator whose low 6 bits count the
 // adds (one device-scope atomic with return per output).  The add that
 // completes the count finishes that output: fp16 y, accumulator back to 0.
@@ -61,7 +58,7 @@ __device__ __forceinline__ int64_t fixed_partial(float v) {
   return (int64_t)__builtin_rint((double)c * 16777216.0);
 }
 
-template <int GS, int LAYOUT, int WC, int WK, int KBW, bool YINT>
+template <int GS, int WC, int WK, int KBW, bool YINT>
 __global__ __launch_bounds__(64 * WC * WK) void msd_decode_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ wt,
     const uint16_t* __restrict__ scale, int M, int K, int N, int g_begin, int g_end,
@@ -72,11 +69,11 @@ __global__ __launch_bounds__(64 * WC * WK) void msd_decode_kernel(
   constexpr int PAD = dc::PAD;
   constexpr int R = WK * KBW * kTileRows;       // K rows per chunk
   constexpr int ROWA = R + PAD;                 // LDS bytes per A slot row
-  constexpr int RT = LAYOUT == 0 ? 1 : 3;       // 16-row A tiles
-  constexpr int MT = LAYOUT == 0 ? 4 : 16;      // rows of x covered by the slots
+  constexpr int RT = 1;                         // 16-row A tiles
+  constexpr int MT = 4;                         // rows of x covered by the slots
   constexpr int GPB = R / GS;                   // groups per chunk
   constexpr int GPW = KBW * kTileRows / GS;     // groups per wave and chunk
-  constexpr int MROWS = LAYOUT == 0 ? 1 : 4;    // output rows per lane
+  constexpr int MROWS = 1;                      // output rows per lane
 
   __shared__ __attribute__((aligned(16))) int8_t sA[16 * RT * ROWA];
   __shared__ float sAmax[MT][GPB];
@@ -172,7 +169,7 @@ __global__ __launch_bounds__(64 * WC * WK) void msd_decode_kernel(
       if (it < items) {
 #pragma unroll
         for (int l = 0; l < 3; ++l) {
-          const int slot = LAYOUT == 0 ? (4 * m + l) : (l * 16 + m);
+          const int slot = 4 * m + l;
           *reinterpret_cast<uint2*>(sA + slot * ROWA + ch * 8) = make_uint2(lv[l][0], lv[l][1]);
         }
         if ((ch & (GS / 8 - 1)) == 0) sAmax[m][(ch * 8) / GS] = amax;
@@ -211,22 +208,22 @@ __global__ __launch_bounds__(64 * WC * WK) void msd_decode_kernel(
           const int64_t gi = g - g_begin;
 #pragma unroll
           for (int i = 0; i < MROWS; ++i) {
-            const int m = LAYOUT == 0 ? (lane >> 4) : 4 * (lane >> 4) + i;
+            const int m = (lane >> 4) + i;
             if (m >= M || !nt_ok) continue;
 #pragma unroll
             for (int l = 0; l < 3; ++l)
-              y_int[((gi * 3 + l) * M + m) * (int64_t)N + n] = (LAYOUT == 0 ? acc[0][l] : acc[l][i]) >> 4;
+              y_int[((gi * 3 + l) * M + m) * (int64_t)N + n] = acc[0][l] >> 4;
           }
         } else {
           const float sc = half_bits_to_float(sraw[gl]);
 #pragma unroll
           for (int i = 0; i < MROWS; ++i) {
-            const int m = LAYOUT == 0 ? (lane >> 4) : 4 * (lane >> 4) + i;
+            const int m = (lane >> 4) + i;
             const float am = sAmax[m][gloc];
             const float q1 = am * kC1, q2 = am * kC2, q3 = am * kC3;
-            const int y1 = LAYOUT == 0 ? acc[0][0] : acc[0][i];
-            const int y2 = LAYOUT == 0 ? acc[0][1] : acc[1][i];
-            const int y3 = LAYOUT == 0 ? acc[0][2] : acc[2][i];
+            const int y1 = acc[0][0];
+            const int y2 = acc[0][1];
+            const int y3 = acc[0][2];
             float tt = (float)y1 * q1;
             tt = __builtin_fmaf((float)y2, q2, tt);
             tt = __builtin_fmaf((float)y3, q3, tt);
@@ -261,7 +258,7 @@ __global__ __launch_bounds__(64 * WC * WK) void msd_decode_kernel(
   // associative, so the result does not depend on the order of arrival.
 #pragma unroll
   for (int i = 0; i < MROWS; ++i) {
-    const int m = LAYOUT == 0 ? (lane >> 4) : 4 * (lane >> 4) + i;
+    const int m = (lane >> 4) + i;
     if (m >= M) continue;
     uint16_t* out = y + (int64_t)m * N + n;
     if (splits == 1) {
@@ -293,19 +290,19 @@ hipError_t launch_zero_words(uint32_t* p, int64_t n, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// The two workgroup shapes (see the top of this file).
+// The workgroup shape (see the top of this file).
 namespace dc {
-constexpr int S0_WC = 1, S0_WK = 16, S0_KBW = 2;   // M <= 4
-constexpr int S1_WC = 8, S1_WK = 1, S1_KBW = 4;    // M <= 16
+constexpr int S0_WC = 1, S0_WK = 16, S0_KBW = 2;
 constexpr int64_t kMaxSplits = 32;                 // < 64: the accumulators' count field
 }  // namespace dc
 
 DecodePlan decode_plan(int gs, int64_t M, int64_t K, int64_t N, int64_t g_begin, int64_t g_end) {
   (void)K;
   DecodePlan p;
-  p.shape = M <= 4 ? 0 : 1;
-  const int wc = p.shape == 0 ? dc::S0_WC : dc::S1_WC;
-  const int64_t per = p.shape == 0 ? dc::S0_WK * dc::S0_KBW : dc::S1_WK * dc::S1_KBW;   // blocks per chunk
+  (void)M;
+  p.shape = 0;
+  const int wc = dc::S0_WC;
+  const int64_t per = dc::S0_WK * dc::S0_KBW;   // blocks per chunk
   p.cols = wc * kTileCols;
   p.col_blocks = (N + p.cols - 1) / p.cols;
   p.kb_begin = g_begin * gs / kTileRows;
@@ -333,23 +330,18 @@ hipError_t launch_decode(const void* x, const void* w, const void* scale, int gs
   uint16_t* yp = static_cast<uint16_t*>(y);
   const int m = (int)M, k = (int)K, n = (int)N, gb = (int)g_begin, ge = (int)g_end;
   const int kb0 = (int)plan.kb_begin, S = (int)plan.splits, nch = (int)plan.nch;
-  if ((plan.shape == 0) != (M <= 4) || M > 16 || S > dc::kMaxSplits) return hipErrorInvalidValue;
+  if (M > 4 || S > dc::kMaxSplits) return hipErrorInvalidValue;
   if (S > 1 && !y_int && !accum) return hipErrorInvalidValue;
-#define WQBMM_DECODE_LAUNCH(GS_, L_, WC_, WK_, KBW_, Y_)                                         \
-  hipLaunchKernelGGL((msd_decode_kernel<GS_, L_, WC_, WK_, KBW_, Y_>), grid, dim3(64 * (WC_) * (WK_)), \
-                     0, stream, xp, wp, sp, m, k, n, gb, ge, kb0, S, nch, yp, y_int, accum)
-#define WQBMM_DECODE_SHAPE(GS_, Y_)                                                              \
-  do {                                                                                           \
-    if (plan.shape == 0) WQBMM_DECODE_LAUNCH(GS_, 0, dc::S0_WC, dc::S0_WK, dc::S0_KBW, Y_);       \
-    else WQBMM_DECODE_LAUNCH(GS_, 1, dc::S1_WC, dc::S1_WK, dc::S1_KBW, Y_);                       \
-  } while (0)
+#define WQBMM_DECODE_SHAPE(GS_, Y_)                                                                      \
+  hipLaunchKernelGGL((msd_decode_kernel<GS_, dc::S0_WC, dc::S0_WK, dc::S0_KBW, Y_>), grid,             \
+                     dim3(64 * dc::S0_WC * dc::S0_WK), 0, stream, xp, wp, sp, m, k, n, gb, ge, kb0, S, nch, \
+                     yp, y_int, accum)
   if (gs == 64) {
     if (y_int) WQBMM_DECODE_SHAPE(64, true); else WQBMM_DECODE_SHAPE(64, false);
   } else {
     if (y_int) WQBMM_DECODE_SHAPE(128, true); else WQBMM_DECODE_SHAPE(128, false);
   }
 #undef WQBMM_DECODE_SHAPE
-#undef WQBMM_DECODE_LAUNCH
   return hipGetLastError();
 }
 

@@ -1,0 +1,262 @@
+// msd_decode_gemv.hip -- the MSD matmul for 4 < M <= 16 as two kernels: x is
+// decomposed ONCE into int4-packed MFMA operands, then a GEMV-shaped
+// contraction streams the weights with every workgroup covering whole K.
+//
+// WQBMM-Exp page (the page "WeightQuantBatchMatmulExperiment 算子深度解析：A16W4
+// PerGroup 伪量化 MatMul 的 MSD 算法与双模板流水设计", lpnh.cn/news/2294145):
+// §4.1 steps 1-8 in the operand kernel (the page's pre-processing stage,
+// UnfoldA, §6.1), steps 9-11 in the contraction kernel (its Cube matmul and
+// MergeY stages).
+//
+// Why two kernels at this M.  A fused kernel whose workgroups each decompose
+// the slice of x they contract repeats the decomposition once per column
+// block (about 20 VALU operations per element of x); to keep that slice short
+// it has to split K over workgroups and hand partial sums between them, and
+// at 16 rows those hand-offs (device-scope atomics, executed past the L2) cost
+// more than the weight stream itself.  Decomposing x once costs one short
+// launch; the contraction then needs no hand-off at all:
+//   workgroup = one 16-column tile of the tiled weights x all of K,
+//   wave      = a contiguous run of 128-row blocks (WK waves split K),
+//   reduction = the WK waves' fp32 sums added in LDS in a fixed order.
+//
+// Level operands.  Every level value lies in [-7, 7] (7.49 < 7.5 and a
+// residual is at most 1/2), so the levels are stored as 4-bit two's
+// complement in exactly the nibble arrangement of the tiled weights: chunk
+// (128-row block kb, level l, lane) is 16 bytes at ((kb*3 + l)*64 + lane)*16;
+// the lane holds row m = lane%16 at k = 128kb + 64s + 16(lane/16) + 8d + j
+// (low nibble of byte 4d + j of step s's 8 bytes) and k + 4 (high nibble).
+// The same two masks that turn a weight chunk into the i8 MFMA's B operand
+// (16*w per byte) turn a level chunk into its A operand (16*a per byte), so
+// each product is 256*a*w, exact in int32 (|sum| <= 256*7*8*128 < 2^21).
+// Rows m >= M and rows k >= K hold 0.  Beside them the operand kernel stores
+// each group's step-10 level weights A_max * w_l as fp32 [G][level][16 rows]
+// (rows >= M: 0), so that the contraction does not form them once per
+// column tile.
+#include "msd_device.hpp"
+#include "msd_launch.hpp"
+
+namespace wqbmm {
+
+// Step-10 weights of the three levels with the 1/256 that undoes the two
+// nibble unpacks (16*a times 16*w).  kC1..kC3 carry 1/16; a further 1/16 is
+// an exact power-of-two scaling.
+constexpr float kD1 = kC1 * 0.0625f;
+constexpr float kD2 = kC2 * 0.0625f;
+constexpr float kD3 = kC3 * 0.0625f;
+
+// ---- steps 1-8: x fp16 [M][K] -> level chunks + group maxima ---------------
+// One workgroup per 128-row block; thread t = 16m + 8s + 2q + d decomposes the
+// 8 elements of row m at k = 128kb + 64s + 16q + 8d + (0..7), which is one
+// dword of each level chunk (lane m + 16q, step s, dword d).  A group is
+// GS/8 consecutive, aligned threads (16 at GS = 128: all (s, q, d) of a row;
+// 8 at GS = 64: all (q, d) of a row and step), as msd_decompose8 requires.
+template <int GS>
+__global__ __launch_bounds__(256) void msd_decode_operands_kernel(
+    const uint16_t* __restrict__ x, int M, int K, uint32_t* __restrict__ lvl,
+    float* __restrict__ qt) {
+  const int kb = blockIdx.x;
+  const int t = threadIdx.x;
+  const int m = t >> 4, s = (t >> 3) & 1, q = (t >> 1) & 3, d = t & 1;
+  const int k = kb * kTileRows + 64 * s + 16 * q + 8 * d;
+  const bool ok = m < M && k < K;
+  const uint4 v = *reinterpret_cast<const uint4*>(x + (ok ? (int64_t)m * K + k : 0));
+  const uint4 xv = ok ? v : make_uint4(0u, 0u, 0u, 0u);
+  uint32_t lv[3][2];
+  float amax;
+  msd_decompose8<GS>(xv, lv, amax);
+  const int64_t base = ((int64_t)kb * 3 * 64 + m + 16 * q) * 4 + 2 * s + d;   // dword index, level 0
+#pragma unroll
+  for (int l = 0; l < 3; ++l)   // byte j: element j (low nibble), element j + 4 (high nibble)
+    lvl[base + (int64_t)l * 64 * 4] = (lv[l][0] & 0x0F0F0F0Fu) | ((lv[l][1] & 0x0F0F0F0Fu) << 4);
+  if ((t & (GS / 8 - 1)) == 0 && k < K) {   // the group's level weights A_max * w_l (step 10)
+    float* q = qt + (int64_t)((kb * kTileRows + 64 * s) / GS) * 48 + m;
+    q[0] = amax * kD1;
+    q[16] = amax * kD2;
+    q[32] = amax * kD3;
+  }
+}
+
+// ---- steps 9-11: contraction, combine, accumulate -----------------------------
+// Grid: one workgroup per 16-column tile; WK waves, wave w owning the 128-row
+// blocks [kb_lo + w*kbw, kb_lo + (w+1)*kbw) of the group range, KBW blocks per
+// round.  A round issues every load first -- the weight chunks (HBM) ahead of
+// the level chunks, level weights and scales (L2 hits after the first
+// workgroup) -- unconditionally and unmodified (a block past the wave's range
+// reads the round's first block again, and its groups are dropped by a zero
+// scale; a load under a branch, or a select on its result, makes the compiler
+// wait for it right there).  Per 64-row step it then runs one
+// v_mfma_i32_16x16x64_i8 per level with the weight chunk as the A operand
+// (MFMA row = output column) and the level chunk as the B operand (MFMA
+// column = row m of x): D^T = W^T . A_l^T.  Lane l then holds row m = l%16 of
+// x for the four consecutive columns 16nt + 4(l/16) + r (element r), so its
+// level weights are three scalars per group and its scales one 8-byte load.
+// Per completed group the three level sums combine with A_max*w_l and the
+// scale (step 10) into the lane's fp32 sums (step 11, groups ascending within
+// the wave).  The waves' sums are then added in LDS, wave 0 first, and wave 0
+// stores y, 8 bytes per lane.
+template <int GS, int WK, int KBW, bool YINT>
+__global__ __launch_bounds__(64 * WK) void msd_decode_gemv_kernel(
+    const uint8_t* __restrict__ lvl, const float* __restrict__ qt,
+    const uint8_t* __restrict__ wt, const uint16_t* __restrict__ scale, int M, int K, int N,
+    int g_begin, int g_end, int kb_lo, int kb_hi, int kbw, uint16_t* __restrict__ y,
+    int32_t* __restrict__ y_int) {
+  constexpr int GPB = kTileRows / GS;            // groups per block
+  __shared__ float4 sRed[WK > 1 ? WK - 1 : 1][64];
+
+  const int lane = threadIdx.x & 63;
+  const int wk = threadIdx.x >> 6;
+  const int nt = blockIdx.x;
+  const int KB = (K + kTileRows - 1) / kTileRows;
+  const int G = K / GS;
+  const int m = lane & 15;                       // this lane's row of x
+  const int n0 = nt * kTileCols + 4 * (lane >> 4);   // first of its 4 columns
+  const int wb_lo = kb_lo + wk * kbw;
+  const int wb_hi = min(wb_lo + kbw, kb_hi);
+
+  float yacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  const uint8_t* wcol = wt + (int64_t)nt * KB * 1024 + lane * 16;
+
+  for (int kb0 = wb_lo; kb0 < wb_hi; kb0 += KBW) {
+    v4i av[KBW][3], wv[KBW];
+    float qv[KBW][GPB][3];
+    uint2 sraw[KBW][GPB];
+#pragma unroll
+    for (int j = 0; j < KBW; ++j) {
+      const int kbc = kb0 + j < wb_hi ? kb0 + j : kb0;
+      wv[j] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wcol + (int64_t)kbc * 1024));
+    }
+#pragma unroll
+    for (int j = 0; j < KBW; ++j) {
+      const int kb = kb0 + j;
+      const bool ok = kb < wb_hi;
+      const int kbc = ok ? kb : kb0;
+#pragma unroll
+      for (int l = 0; l < 3; ++l)
+        av[j][l] = *reinterpret_cast<const v4i*>(lvl + (((int64_t)kbc * 3 + l) * 64 + lane) * 16);
+      if constexpr (!YINT) {
+#pragma unroll
+        for (int gl = 0; gl < GPB; ++gl) {
+          const int g = kbc * GPB + gl;
+          const bool gok = ok && g >= g_begin && g < g_end;
+          const int gc = g < G ? g : G - 1;
+#pragma unroll
+          for (int l = 0; l < 3; ++l) qv[j][gl][l] = qt[(int64_t)gc * 48 + l * 16 + m];
+          const uint2 sv = *reinterpret_cast<const uint2*>(scale + (int64_t)gc * N + n0);
+          sraw[j][gl] = gok ? sv : make_uint2(0u, 0u);   // a zero scale drops the group
+        }
+      }
+    }
+    // keep every load of the round ahead of the first MFMA: without this the
+    // scheduler interleaves waits into the loads to save registers
+    __builtin_amdgcn_sched_barrier(0);
+
+#pragma unroll
+    for (int j = 0; j < KBW; ++j) {
+      v4i acc[3];
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        if ((64 * st) % GS == 0) {
+#pragma unroll
+          for (int l = 0; l < 3; ++l) acc[l] = v4i{0, 0, 0, 0};
+        }
+        const uint32_t w0 = (uint32_t)wv[j][2 * st], w1 = (uint32_t)wv[j][2 * st + 1];
+        const v4i b = v4i{(int)lo16(w0), (int)hi16(w0), (int)lo16(w1), (int)hi16(w1)};
+#pragma unroll
+        for (int l = 0; l < 3; ++l) {
+          const uint32_t a0 = (uint32_t)av[j][l][2 * st], a1 = (uint32_t)av[j][l][2 * st + 1];
+          const v4i a = v4i{(int)lo16(a0), (int)hi16(a0), (int)lo16(a1), (int)hi16(a1)};
+          acc[l] = mfma_i8(b, a, acc[l]);
+        }
+        if ((64 * st + 64) % GS != 0) continue;                      // group not complete
+        const int gl = (64 * st) / GS;
+        if constexpr (YINT) {
+          const int g = (kb0 + j) * GPB + gl;
+          if (kb0 + j >= wb_hi || g < g_begin || g >= g_end || m >= M) continue;
+          const int64_t gi = g - g_begin;
+#pragma unroll
+          for (int l = 0; l < 3; ++l)
+            *reinterpret_cast<v4i*>(y_int + ((gi * 3 + l) * M + m) * (int64_t)N + n0) = acc[l] >> 8;
+        } else {
+          const uint32_t s01 = sraw[j][gl].x, s23 = sraw[j][gl].y;
+          const float sc[4] = {half_bits_to_float(s01 & 0xffffu), half_bits_to_float(s01 >> 16),
+                               half_bits_to_float(s23 & 0xffffu), half_bits_to_float(s23 >> 16)};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float tt = (float)acc[0][r] * qv[j][gl][0];
+            tt = __builtin_fmaf((float)acc[1][r], qv[j][gl][1], tt);
+            tt = __builtin_fmaf((float)acc[2][r], qv[j][gl][2], tt);
+            yacc[r] = __builtin_fmaf(tt, sc[r], yacc[r]);
+          }
+        }
+      }
+    }
+  }
+  if constexpr (YINT) return;
+
+  // ---- the WK waves' sums, added in wave order; wave 0 stores y
+  if constexpr (WK > 1) {
+    if (wk > 0) sRed[wk - 1][lane] = make_float4(yacc[0], yacc[1], yacc[2], yacc[3]);
+    __syncthreads();
+    if (wk != 0) return;
+#pragma unroll
+    for (int v = 0; v < WK - 1; ++v) {
+      const float4 p = sRed[v][lane];
+      yacc[0] += p.x; yacc[1] += p.y; yacc[2] += p.z; yacc[3] += p.w;
+    }
+  }
+  if (m < M) {
+    const uint32_t lo = (uint32_t)float_to_half_bits(yacc[0]) | ((uint32_t)float_to_half_bits(yacc[1]) << 16);
+    const uint32_t hi = (uint32_t)float_to_half_bits(yacc[2]) | ((uint32_t)float_to_half_bits(yacc[3]) << 16);
+    *reinterpret_cast<uint2*>(y + (int64_t)m * N + n0) = make_uint2(lo, hi);
+  }
+}
+
+namespace dg {
+constexpr int WK = 8;    // waves per workgroup (K split within the workgroup)
+constexpr int KBW = 4;   // 128-row blocks per wave and load round
+}  // namespace dg
+
+size_t decode_gemv_workspace_bytes(int gs, int64_t K) {
+  const int64_t KB = (K + kTileRows - 1) / kTileRows;
+  return (size_t)KB * 3 * 1024 + (size_t)(K / gs) * 48 * sizeof(float);
+}
+
+hipError_t launch_decode_gemv(const void* x, const void* w, const void* scale, int gs, int64_t M,
+                              int64_t K, int64_t N, int64_t g_begin, int64_t g_end, void* y,
+                              int32_t* y_int, uint8_t* ws, int stage, hipStream_t stream) {
+  if (M < 1 || M > 16 || N % kTileCols != 0 || stage < 0 || stage > 2) return hipErrorInvalidValue;
+  const int KB = (int)((K + kTileRows - 1) / kTileRows);
+  uint32_t* lvl = reinterpret_cast<uint32_t*>(ws);
+  float* qt = reinterpret_cast<float*>(ws + (size_t)KB * 3 * 1024);
+  if (stage != 2) {
+    const uint16_t* xp = static_cast<const uint16_t*>(x);
+    if (gs == 64)
+      hipLaunchKernelGGL(msd_decode_operands_kernel<64>, dim3(KB), dim3(256), 0, stream, xp, (int)M, (int)K, lvl, qt);
+    else
+      hipLaunchKernelGGL(msd_decode_operands_kernel<128>, dim3(KB), dim3(256), 0, stream, xp, (int)M, (int)K, lvl, qt);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || stage == 1) return e;
+  }
+
+  const int kb_lo = (int)(g_begin * gs / kTileRows);
+  const int kb_hi = (int)((g_end * gs + kTileRows - 1) / kTileRows);
+  const int kbw = (kb_hi - kb_lo + dg::WK - 1) / dg::WK;
+  const dim3 grid((unsigned)(N / kTileCols));
+  const uint8_t* lp = ws;
+  const uint8_t* wp = static_cast<const uint8_t*>(w);
+  const uint16_t* sp = static_cast<const uint16_t*>(scale);
+  uint16_t* yp = static_cast<uint16_t*>(y);
+  const int m = (int)M, k = (int)K, n = (int)N, gb = (int)g_begin, ge = (int)g_end;
+#define WQBMM_GEMV_LAUNCH(GS_, Y_)                                                                   \
+  hipLaunchKernelGGL((msd_decode_gemv_kernel<GS_, dg::WK, dg::KBW, Y_>), grid, dim3(64 * dg::WK), 0, stream, lp, \
+                     qt, wp, sp, m, k, n, gb, ge, kb_lo, kb_hi, kbw, yp, y_int)
+  if (gs == 64) {
+    if (y_int) WQBMM_GEMV_LAUNCH(64, true); else WQBMM_GEMV_LAUNCH(64, false);
+  } else {
+    if (y_int) WQBMM_GEMV_LAUNCH(128, true); else WQBMM_GEMV_LAUNCH(128, false);
+  }
+#undef WQBMM_GEMV_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace wqbmm

@@ -67,11 +67,11 @@ hipError_t launch_prefill64_gemm(const uint8_t* x_t, const float* q_t, const uin
                                  const PrefillLayout& L, int64_t g_begin, int64_t g_end, void* y,
                                  int32_t* y_int, hipStream_t stream);
 
-// The fused decode kernel (M <= 16): steps 1-11 in one launch.  A K-split
-// hands its partials off through `accum` (int64 per output; zero before the
-// first launch, re-armed by the kernel).
+// The fused decode kernel (M <= 4): steps 1-11 in one launch.  A K-split
+// (K > 4096) hands its partials off through `accum` (int64 per output; zero
+// before the first launch, re-armed by the kernel).
 struct DecodePlan {
-  int shape;            // workgroup shape: 0 for M <= 4, 1 for M <= 16
+  int shape;            // workgroup shape (one shape: 0)
   int64_t cols;         // columns per workgroup
   int64_t col_blocks;   // column blocks
   int64_t splits;       // K-slices per column block (<= 32)
@@ -84,6 +84,16 @@ size_t decode_accum_bytes(const DecodePlan& p, int64_t M, int64_t N);
 hipError_t launch_decode(const void* x, const void* w, const void* scale, int gs, int64_t M,
                          int64_t K, int64_t N, int64_t g_begin, int64_t g_end, void* y,
                          int32_t* y_int, uint64_t* accum, const DecodePlan& plan, hipStream_t stream);
+
+// Decode for 4 < M <= 16 (msd_decode_gemv.hip): an operand kernel decomposes
+// x once into int4-packed level operands and level weights in `ws`
+// (decode_gemv_workspace_bytes), then a contraction kernel covers all of K
+// per 16-column tile (no K-split hand-off).  stage 0: both kernels; 1: the
+// operand kernel only; 2: the contraction only, on the operands in `ws`.
+size_t decode_gemv_workspace_bytes(int gs, int64_t K);
+hipError_t launch_decode_gemv(const void* x, const void* w, const void* scale, int gs, int64_t M,
+                              int64_t K, int64_t N, int64_t g_begin, int64_t g_end, void* y,
+                              int32_t* y_int, uint8_t* ws, int stage, hipStream_t stream);
 
 // Zero n 32-bit words (a kernel, not a memset).
 hipError_t launch_zero_words(uint32_t* p, int64_t n, hipStream_t stream);
