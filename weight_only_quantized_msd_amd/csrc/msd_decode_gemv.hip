@@ -79,9 +79,9 @@ __global__ __launch_bounds__(256) void msd_decode_operands_kernel(
 // ---- steps 9-11: contraction, combine, accumulate -----------------------------
 // Grid: one workgroup per 16-column tile; WK waves, wave w owning the 128-row
 // blocks [kb_lo + w*kbw, kb_lo + (w+1)*kbw) of the group range, KBW blocks per
-// round.  A round issues every load first -- the weight chunks (HBM) ahead of
-// the level chunks, level weights and scales (L2 hits after the first
-// workgroup) -- unconditionally and unmodified (a block past the wave's range
+// round.  A round issues every load first, block by block (weight chunk, level
+// chunks, level weights, scales: the first block's MFMAs wait only for its
+// own loads), unconditionally and unmodified (a block past the wave's range
 // reads the round's first block again, and its groups are dropped by a zero
 // scale; a load under a branch, or a select on its result, makes the compiler
 // wait for it right there).  Per 64-row step it then runs one
@@ -122,14 +122,10 @@ __global__ __launch_bounds__(64 * WK) void msd_decode_gemv_kernel(
     uint2 sraw[KBW][GPB];
 #pragma unroll
     for (int j = 0; j < KBW; ++j) {
-      const int kbc = kb0 + j < wb_hi ? kb0 + j : kb0;
-      wv[j] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wcol + (int64_t)kbc * 1024));
-    }
-#pragma unroll
-    for (int j = 0; j < KBW; ++j) {
       const int kb = kb0 + j;
       const bool ok = kb < wb_hi;
       const int kbc = ok ? kb : kb0;
+      wv[j] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wcol + (int64_t)kbc * 1024));
 #pragma unroll
       for (int l = 0; l < 3; ++l)
         av[j][l] = *reinterpret_cast<const v4i*>(lvl + (((int64_t)kbc * 3 + l) * 64 + lane) * 16);
