@@ -257,6 +257,37 @@ def test_ragged_shapes(torch_dev, M, K, N, gs):
         assert np.array_equal(yi.cpu().numpy(), ref_yi), f"path {p} Y_int"
 
 
+# The decode contraction for 4 < M <= 16 (operand kernel + full-K contraction):
+# K beyond 4096 (several load rounds per wave), a single 128-row block, K not
+# a multiple of 128 at group size 64, and Y_int over group ranges that start
+# and end inside a 128-row block.
+GEMV_CASES = [  # (M, K, N, gs, g_begin, g_end)
+    (16, 8192, 512, 128, 0, 64), (8, 12288, 256, 128, 37, 91), (16, 8192, 384, 64, 5, 118),
+    (5, 64, 96, 64, 0, 1), (9, 128, 64, 128, 0, 1), (12, 320, 160, 64, 1, 4),
+]
+
+
+@pytest.mark.parametrize("M,K,N,gs,gb,ge", GEMV_CASES,
+                         ids=[f"M{c[0]}K{c[1]}N{c[2]}g{c[3]}r{c[4]}-{c[5]}" for c in GEMV_CASES])
+def test_decode_contraction_shapes(torch_dev, M, K, N, gs, gb, ge):
+    import weight_only_quantized_msd_amd as W
+    torch = torch_dev
+    d = datagen.random_case(M, K, N, gs, seed=M * 31 + K + N)
+    if K >= 4 * gs:
+        d["x"] = adversarial_x(M + K + 1, M, K, gs)
+    x, w, s = to_dev(torch, d)
+    announce(f"decode contraction M={M} K={K} N={N} gs={gs} groups=[{gb},{ge})")
+    y = W.wqbmm_a16w4_msd_path(x, w, s, gs, DECODE)
+    yi = W.wqbmm_a16w4_msd_yint(x, w, gs, gb, ge, path=DECODE)
+    torch.cuda.synchronize()
+    y32, _ = oracle.matmul(d["x"], d["w_packed"], d["scale"], gs)
+    check_y(y.cpu().numpy(), y32, "decode contraction")
+    ra, _ = oracle.decompose(d["x"], gs)
+    ref = oracle.yint(ra, d["w"], gs, gb, ge)
+    got = yi.cpu().numpy()
+    assert np.array_equal(got, ref), f"{np.count_nonzero(got != ref)} words differ"
+
+
 # Group size 64 with many row blocks: the weights are converted by the
 # preparation kernel and the GEMM runs 128 x 256 tiles (at least 256 of them);
 # K = 192 leaves a last stage of one group.  Sampled rows against the oracle.
