@@ -233,6 +233,8 @@ RAGGED = [  # (M, K, N, gs)
     (1, 64, 32, 64), (2, 128, 96, 128), (3, 192, 160, 64), (4, 640, 288, 128),
     (5, 576, 4128, 64), (13, 1024, 416, 128), (16, 2560, 544, 128), (17, 512, 160, 64),
     (130, 384, 288, 128), (257, 256, 128, 64),
+    # M <= 4 with K split over workgroups and a last chunk that ends inside it
+    (1, 4736, 96, 64), (3, 6272, 160, 128),
 ]
 
 

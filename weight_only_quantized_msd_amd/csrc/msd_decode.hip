@@ -110,20 +110,33 @@ __global__ __launch_bounds__(64 * WC * WK) void msd_decode_kernel(
 
     // ---- 1. this thread's x chunks first (so waiting for them does not wait
     //         for the weights), the per-group scales, then every W load of the
-    //         wave.  Loads are unconditional (out-of-range ones read a valid
-    //         address and are zeroed afterwards): a load under a branch makes
-    //         the compiler wait for every outstanding load at the join.
+    //         wave.  Loads are unconditional: an out-of-range one reads a valid
+    //         address.  Its weights and scale are used as loaded, since they
+    //         only reach groups >= G, which step 3 skips; zeroing them would
+    //         be a select on the load result, and the compiler would wait for
+    //         the load right there, i.e. before the barrier below.  (A load
+    //         under a branch makes it wait for every outstanding load at the
+    //         join.)  Out-of-range x chunks are zeroed: they are decomposed.
     // Only the M real rows and the rows below K are decomposed.  The other LDS
     // rows and A_max entries are left as they are: they only meet zero
-    // weights (rows >= K of the tiled format are zero) or feed accumulator
-    // rows that are never stored, and integer MFMAs cannot trap.
+    // weights (rows >= K of the tiled format are zero), feed groups >= G, or
+    // feed accumulator rows that are never stored; integer MFMAs cannot trap.
     constexpr int ROUNDS = (MT * (R / 8) + THREADS - 1) / THREADS;
+    // row of item `it` (it / kch for it < items <= MT * kch), by comparisons:
+    // a division by the runtime kch costs about 25 VALU per lane, and it sits
+    // in front of every load of the wave
+    auto row_of = [&](int it) __attribute__((always_inline)) {
+      int r = 0;
+#pragma unroll
+      for (int i = 1; i < MT; ++i) r += it >= i * kch ? 1 : 0;
+      return r;
+    };
     uint4 xv[ROUNDS];
 #pragma unroll
     for (int rd = 0; rd < ROUNDS; ++rd) {
       const int it = rd * THREADS + tid;
       const bool ok = it < items;
-      const int m = ok ? it / kch : 0;
+      const int m = ok ? row_of(it) : 0;
       const int k = ok ? kbase + (it - m * kch) * 8 : 0;
       const uint4 v = *reinterpret_cast<const uint4*>(x + (ok ? (int64_t)m * K + k : 0));
       xv[rd] = ok ? v : make_uint4(0u, 0u, 0u, 0u);
@@ -137,8 +150,7 @@ __global__ __launch_bounds__(64 * WC * WK) void msd_decode_kernel(
       } else {
         const int g = gw0 + gl;
         const bool ok = nt_ok && g < G;
-        const uint32_t v = scale[ok ? (int64_t)g * N + n : 0];
-        sraw[gl] = ok ? v : 0u;
+        sraw[gl] = scale[ok ? (int64_t)g * N + n : 0];
       }
     }
     v4i wv[KBW];
@@ -148,8 +160,7 @@ __global__ __launch_bounds__(64 * WC * WK) void msd_decode_kernel(
       for (int j = 0; j < KBW; ++j) {
         const int kb = kb0 + wk * KBW + j;
         const bool ok = nt_ok && kb < KB;
-        const v4i v = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wb + (int64_t)(ok ? kb : 0) * 1024));
-        wv[j] = ok ? v : v4i{0, 0, 0, 0};
+        wv[j] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wb + (int64_t)(ok ? kb : 0) * 1024));
       }
     }
 
@@ -160,8 +171,11 @@ __global__ __launch_bounds__(64 * WC * WK) void msd_decode_kernel(
 #pragma unroll
     for (int rd = 0; rd < ROUNDS; ++rd) {
       if (rd * THREADS >= items) break;              // workgroup-uniform
+      // wave-uniform: a wave with no item in this round skips it (at M = 1 half
+      // of the waves), leaving its SIMD to the waves that have items
+      if (rd * THREADS + wave * 64 >= items) continue;
       const int it = rd * THREADS + tid;
-      const int m = it < items ? it / kch : 0;
+      const int m = it < items ? row_of(it) : 0;
       const int ch = it - m * kch;
       uint32_t lv[3][2];
       float amax;

@@ -78,21 +78,26 @@ __global__ __launch_bounds__(256) void msd_decode_operands_kernel(
 
 // ---- steps 9-11: contraction, combine, accumulate -----------------------------
 // Grid: one workgroup per 16-column tile; WK waves, wave w owning the 128-row
-// blocks [kb_lo + w*kbw, kb_lo + (w+1)*kbw) of the group range, KBW blocks per
-// round.  A round issues every load first, block by block (weight chunk, level
-// chunks, level weights, scales: the first block's MFMAs wait only for its
-// own loads), unconditionally and unmodified (a block past the wave's range
-// reads the round's first block again, and its groups are dropped by a zero
-// scale; a load under a branch, or a select on its result, makes the compiler
-// wait for it right there).  Per 64-row step it then runs one
-// v_mfma_i32_16x16x64_i8 per level with the weight chunk as the A operand
-// (MFMA row = output column) and the level chunk as the B operand (MFMA
-// column = row m of x): D^T = W^T . A_l^T.  Lane l then holds row m = l%16 of
-// x for the four consecutive columns 16nt + 4(l/16) + r (element r), so its
-// level weights are three scalars per group and its scales one 8-byte load.
-// Per completed group the three level sums combine with A_max*w_l and the
-// scale (step 10) into the lane's fp32 sums (step 11, groups ascending within
-// the wave).  The waves' sums are then added in LDS, wave 0 first, and wave 0
+// blocks [kb_lo + w*kbw, kb_lo + (w+1)*kbw) of the group range, in rounds of
+// KBW blocks.  Per round a wave
+//   - loads the round's level weights (contiguous, a few floats per lane) and
+//     scales (16 columns x KBW*GS/128 groups, 2-4 bytes per lane) with one or
+//     two loads and keeps them in its own LDS slice: per block, per lane
+//     loads of them would cost three 4-byte and one 8-byte access of 64 lanes
+//     for 48 and 32 distinct bytes;
+//   - keeps two blocks of weight and level chunks in flight: the loads of
+//     block j+2 are issued after the compute of block j;
+//   - per 64-row step runs one v_mfma_i32_16x16x64_i8 per level with the
+//     weight chunk as the A operand (MFMA row = output column) and the level
+//     chunk as the B operand (MFMA column = row m of x): D^T = W^T . A_l^T.
+// Every load is unconditional and its result unmodified (a block past the
+// wave's range reads the round's first block again and its groups are
+// dropped by a zero scale; a load under a branch, or a select on its result,
+// makes the compiler wait for it right there).  Lane l holds row m = l%16 of
+// x for the four consecutive columns 16nt + 4(l/16) + r (element r).  Per
+// completed group the three level sums combine with A_max*w_l and the scale
+// (step 10) into the lane's fp32 sums (step 11, groups ascending within the
+// wave).  The waves' sums are then added in LDS, wave 0 first, and wave 0
 // stores y, 8 bytes per lane.
 template <int GS, int WK, int KBW, bool YINT>
 __global__ __launch_bounds__(64 * WK) void msd_decode_gemv_kernel(
@@ -101,7 +106,15 @@ __global__ __launch_bounds__(64 * WK) void msd_decode_gemv_kernel(
     int g_begin, int g_end, int kb_lo, int kb_hi, int kbw, uint16_t* __restrict__ y,
     int32_t* __restrict__ y_int) {
   constexpr int GPB = kTileRows / GS;            // groups per block
+  constexpr int RG = KBW * GPB;                  // groups per round
+  constexpr int QF = RG * 48 / 64;               // staged level weights per lane
+  constexpr int SV = RG * 16 / 64;               // staged scales per lane
+  constexpr int D = 2;                           // blocks in flight
+  static_assert(QF * 64 == RG * 48 && SV * 64 == RG * 16 && (SV == 1 || SV == 2), "round shape");
+  static_assert(48 % QF == 0, "a lane's staged level weights lie in one group");
   __shared__ float4 sRed[WK > 1 ? WK - 1 : 1][64];
+  __shared__ float sQ[YINT ? 1 : WK][YINT ? 1 : RG * 48];                // [group][level][row]
+  __shared__ __attribute__((aligned(8))) uint16_t sS[YINT ? 1 : WK][YINT ? 4 : RG * 16];   // [group][col]
 
   const int lane = threadIdx.x & 63;
   const int wk = threadIdx.x >> 6;
@@ -115,39 +128,45 @@ __global__ __launch_bounds__(64 * WK) void msd_decode_gemv_kernel(
 
   float yacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   const uint8_t* wcol = wt + (int64_t)nt * KB * 1024 + lane * 16;
+  // staging: lane covers level weights [QF*lane, QF*lane + QF) of the round
+  // and scales of group sgi, columns sc0 .. sc0 + SV - 1
+  const int sgi = lane / (16 / SV);
+  const int sc0 = SV * (lane % (16 / SV));
 
   for (int kb0 = wb_lo; kb0 < wb_hi; kb0 += KBW) {
     v4i av[KBW][3], wv[KBW];
-    float qv[KBW][GPB][3];
-    uint2 sraw[KBW][GPB];
+    float qst[QF];
+    uint32_t sst = 0;
+    if constexpr (!YINT) {
+      const int g0 = kb0 * GPB;
+      const int qo = min(g0 * 48 + QF * lane, G * 48 - QF);   // past G: any valid floats
 #pragma unroll
-    for (int j = 0; j < KBW; ++j) {
+      for (int i = 0; i < QF; ++i) qst[i] = qt[qo + i];
+      const int gc = min(g0 + sgi, G - 1);
+      const uint16_t* sp = scale + (int64_t)gc * N + nt * kTileCols + sc0;
+      if constexpr (SV == 1) sst = *sp;
+      else sst = *reinterpret_cast<const uint32_t*>(sp);
+    }
+    auto load_block = [&](int j) __attribute__((always_inline)) {
       const int kb = kb0 + j;
-      const bool ok = kb < wb_hi;
-      const int kbc = ok ? kb : kb0;
+      const int kbc = kb < wb_hi ? kb : kb0;
       wv[j] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wcol + (int64_t)kbc * 1024));
 #pragma unroll
       for (int l = 0; l < 3; ++l)
         av[j][l] = *reinterpret_cast<const v4i*>(lvl + (((int64_t)kbc * 3 + l) * 64 + lane) * 16);
+    };
+    auto stage = [&]() __attribute__((always_inline)) {
       if constexpr (!YINT) {
 #pragma unroll
-        for (int gl = 0; gl < GPB; ++gl) {
-          const int g = kbc * GPB + gl;
-          const bool gok = ok && g >= g_begin && g < g_end;
-          const int gc = g < G ? g : G - 1;
-#pragma unroll
-          for (int l = 0; l < 3; ++l) qv[j][gl][l] = qt[(int64_t)gc * 48 + l * 16 + m];
-          const uint2 sv = *reinterpret_cast<const uint2*>(scale + (int64_t)gc * N + n0);
-          sraw[j][gl] = gok ? sv : make_uint2(0u, 0u);   // a zero scale drops the group
-        }
+        for (int i = 0; i < QF; ++i) sQ[wk][QF * lane + i] = qst[i];
+        const int g = kb0 * GPB + sgi;
+        const bool gok = kb0 + sgi / GPB < wb_hi && g >= g_begin && g < g_end;
+        const uint32_t v = gok ? sst : 0u;       // a zero scale drops the group
+        if constexpr (SV == 1) sS[wk][lane] = (uint16_t)v;
+        else *reinterpret_cast<uint32_t*>(&sS[wk][2 * lane]) = v;
       }
-    }
-    // keep every load of the round ahead of the first MFMA: without this the
-    // scheduler interleaves waits into the loads to save registers
-    __builtin_amdgcn_sched_barrier(0);
-
-#pragma unroll
-    for (int j = 0; j < KBW; ++j) {
+    };
+    auto compute_block = [&](int j) __attribute__((always_inline)) {
       v4i acc[3];
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
@@ -173,17 +192,35 @@ __global__ __launch_bounds__(64 * WK) void msd_decode_gemv_kernel(
           for (int l = 0; l < 3; ++l)
             *reinterpret_cast<v4i*>(y_int + ((gi * 3 + l) * M + m) * (int64_t)N + n0) = acc[l] >> 8;
         } else {
-          const uint32_t s01 = sraw[j][gl].x, s23 = sraw[j][gl].y;
-          const float sc[4] = {half_bits_to_float(s01 & 0xffffu), half_bits_to_float(s01 >> 16),
-                               half_bits_to_float(s23 & 0xffffu), half_bits_to_float(s23 >> 16)};
+          const int gi = j * GPB + gl;
+          const float q0 = sQ[wk][gi * 48 + m], q1 = sQ[wk][gi * 48 + 16 + m], q2 = sQ[wk][gi * 48 + 32 + m];
+          const uint2 sv = *reinterpret_cast<const uint2*>(&sS[wk][gi * 16 + 4 * (lane >> 4)]);
+          const float sc[4] = {half_bits_to_float(sv.x & 0xffffu), half_bits_to_float(sv.x >> 16),
+                               half_bits_to_float(sv.y & 0xffffu), half_bits_to_float(sv.y >> 16)};
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            float tt = (float)acc[0][r] * qv[j][gl][0];
-            tt = __builtin_fmaf((float)acc[1][r], qv[j][gl][1], tt);
-            tt = __builtin_fmaf((float)acc[2][r], qv[j][gl][2], tt);
+            float tt = (float)acc[0][r] * q0;
+            tt = __builtin_fmaf((float)acc[1][r], q1, tt);
+            tt = __builtin_fmaf((float)acc[2][r], q2, tt);
             yacc[r] = __builtin_fmaf(tt, sc[r], yacc[r]);
           }
         }
+      }
+    };
+    // the scheduling barriers keep each stage's loads where they are written:
+    // without them the scheduler moves waits into the loads to save registers
+#pragma unroll
+    for (int j = 0; j < (D < KBW ? D : KBW); ++j) load_block(j);
+    __builtin_amdgcn_sched_barrier(0);
+    stage();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < KBW; ++j) {
+      compute_block(j);
+      __builtin_amdgcn_sched_barrier(0);
+      if (j + D < KBW) {
+        load_block(j + D);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
