@@ -34,9 +34,9 @@ METRIC = "A16W4 MSD matmul effective TOPS + weight GB/s (% roofline) at M=1..204
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 I8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, published (5.0 POP/s)
 FP6_PEAK_TOPS = 10100.0      # MI355X dense FP6 MFMA, published (10.1 PFLOP/s): the GEMM's own dtype
-# fp32 VALU instruction rate without packed math: 256 CUs x 4 SIMDs x 16 lanes
-# x 2.4 GHz (one fp32 operation per lane per cycle; packed fp32 is not used)
-VALU_F32_OPS_PEAK_T = 256 * 4 * 16 * 2.4e9 / 1e12
+# fp32 vector rate in lane-operations: the published 157.3 TFLOP/s counts an FMA
+# as two flops, i.e. 256 CUs x 4 SIMDs x 32 lanes x 2.4 GHz operations per second
+VALU_F32_OPS_PEAK_T = 256 * 4 * 32 * 2.4e9 / 1e12
 MALL_COLD_BYTES = 512 << 20
 
 
@@ -289,9 +289,10 @@ def main():
                 "avg_kernel_us": round(kern_ms * 1e3, 3),
                 "algorithmic_ops_per_launch": alg["exec_i8_ops"],
                 "frac_of_i8_peak": round(achieved / I8_PEAK_TOPS, 4)}
-        # The GEMM is bound by the fp32 combine of step 10 rather than by the
-        # MFMA: 4 fp32 operations per (row, column, group) -- three for the
-        # level weights, one for the scale and the running sum.
+        # The GEMM spends more SIMD time on the fp32 combine of step 10 than on
+        # the MFMA (and the two do not overlap): 4 fp32 operations per (row,
+        # column, group) -- three for the level weights, one for the scale and
+        # the running sum.
         combine_ops = 4 * M * N * G
         alu = combine_ops / (kern_ms * 1e-3) / 1e12
         extra["alu_view"] = {"bound": "alu", "ops_per_launch": combine_ops, "achieved": round(alu, 2),

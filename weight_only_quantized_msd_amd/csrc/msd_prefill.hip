@@ -85,6 +85,9 @@ constexpr int NXCD = 8;
 constexpr int BAND = 4;        // row blocks per band of the tile order
 }  // namespace pf
 
+// runs of 64 tiled-weight chunks converted per wave of the prep kernel
+constexpr int kPrepWChunks = 4;
+
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v6i __attribute__((ext_vector_type(6)));
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -131,9 +134,12 @@ __device__ __forceinline__ void store_operand(uint8_t* tile, int slot, const v6i
 // lane 16*kq + row (u: k = 16*kq + j, v: k = 64 + 16*kq + j), so a group's
 // maximum is a 4-lane reduction and the wave's stores fill one whole tile per
 // level; the rows' level weights A_max * w_l go to Q_t.
-// Waves [xwaves, ...): one 16-byte tiled-weight chunk per thread (column
-// tiles up to the padded width; those beyond N become zeros), converted in
-// place into operand lane l of its column tile (column blocks of BN).
+// Waves [xwaves, ...): kPrepWChunks runs of 64 tiled-weight chunks each, one
+// 16-byte chunk per lane and run (column tiles up to the padded width; those
+// beyond N become zeros), each converted in place into operand lane l of its
+// column tile (column blocks of BN).  A wave issues all its loads before
+// converting: at one run per wave the waves spent most of their time
+// waiting for a single load.
 template <int GS>
 __global__ __launch_bounds__(256) void msd_prep_kernel(const uint16_t* __restrict__ x,
                                                        const uint8_t* __restrict__ wt, int M,
@@ -197,40 +203,55 @@ __global__ __launch_bounds__(256) void msd_prep_kernel(const uint16_t* __restric
     }
     return;
   }
-  // tiled weights: chunk t = (nt * KB + kb) * 64 + lane
+  // tiled weights: chunk t = (nt * KB + kb) * 64 + lane; a wave converts
+  // kPrepWChunks consecutive runs of 64 chunks, all loads issued first
   const int KB = (K + kTileRows - 1) / kTileRows;
-  const int64_t t = (wid - xwaves) * 64 + lane;
-  if (t >= (int64_t)(Npad / kTileCols) * KB * 64) return;
-  const int kb = (int)((t >> 6) % KB);
-  const int nt = (int)((t >> 6) / KB);
-  uint4 v = make_uint4(0u, 0u, 0u, 0u);
-  if (nt < N / kTileCols) v = *reinterpret_cast<const uint4*>(wt + t * 16);
-  const int32_t dw[4] = {(int32_t)v.x, (int32_t)v.y, (int32_t)v.z, (int32_t)v.w};
-  // step s (dwords 2s, 2s+1), element i = 8d + j: dword 2s + d, low nibble of
-  // byte j for j < 4, high nibble of byte j - 4 otherwise
-  v16f w[2];
+  const int64_t nchunks = (int64_t)(Npad / kTileCols) * KB * 64;
+  const int64_t t0 = (wid - xwaves) * (kPrepWChunks * 64) + lane;
+  const int NTR = N / kTileCols;                     // real column tiles
+  uint4 v[kPrepWChunks];
 #pragma unroll
-  for (int st = 0; st < 2; ++st)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int j = i % 8;
-      w[st][i] = sfield(dw[2 * st + i / 8], j < 4 ? 8 * j : 8 * (j - 4) + 4, 4);
-    }
+  for (int c = 0; c < kPrepWChunks; ++c) {
+    const int64_t t = t0 + c * 64;
+    const bool ok = t < nchunks && (int)((t >> 6) / KB) < NTR;
+    v[c] = *reinterpret_cast<const uint4*>(wt + (ok ? t : 0) * 16);
+  }
+  __builtin_amdgcn_sched_barrier(0);                 // every load ahead of the first conversion
   const int CT = BN / 16;
-  const int cb = nt / CT, ct = nt % CT;
-  if constexpr (GS == 128) {
-    uint8_t* tile = b_t + (((int64_t)cb * G + kb) * CT + ct) * TILE;
-    store_operand(tile, lane, pack_e2m3(w[0], w[1], 2.0f));
-  } else {
-    v16f zero;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) zero[i] = 0.0f;
+  for (int c = 0; c < kPrepWChunks; ++c) {
+    const int64_t t = t0 + c * 64;
+    if (t >= nchunks) break;                          // wave-uniform (runs of 64)
+    const int kb = (int)((t >> 6) % KB);
+    const int nt = (int)((t >> 6) / KB);
+    const bool real = nt < NTR;                       // columns beyond N become zeros
+    const int32_t dw[4] = {real ? (int32_t)v[c].x : 0, real ? (int32_t)v[c].y : 0,
+                           real ? (int32_t)v[c].z : 0, real ? (int32_t)v[c].w : 0};
+    // step s (dwords 2s, 2s+1), element i = 8d + j: dword 2s + d, low nibble of
+    // byte j for j < 4, high nibble of byte j - 4 otherwise
+    v16f w[2];
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const int g = 2 * kb + st;
-      if (g >= G) break;                              // padding rows of the last block
-      uint8_t* tile = b_t + (((int64_t)cb * G + g) * CT + ct) * TILE;
-      store_operand(tile, lane, pack_e2m3(w[st], zero, 2.0f));
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int j = i % 8;
+        w[st][i] = sfield(dw[2 * st + i / 8], j < 4 ? 8 * j : 8 * (j - 4) + 4, 4);
+      }
+    const int cb = nt / CT, ct = nt % CT;
+    if constexpr (GS == 128) {
+      uint8_t* tile = b_t + (((int64_t)cb * G + kb) * CT + ct) * TILE;
+      store_operand(tile, lane, pack_e2m3(w[0], w[1], 2.0f));
+    } else {
+      v16f zero;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) zero[i] = 0.0f;
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int g = 2 * kb + st;
+        if (g >= G) break;                            // padding rows of the last block
+        uint8_t* tile = b_t + (((int64_t)cb * G + g) * CT + ct) * TILE;
+        store_operand(tile, lane, pack_e2m3(w[st], zero, 2.0f));
+      }
     }
   }
 }
@@ -469,7 +490,8 @@ hipError_t launch_prefill_prep(const void* x, const void* w, int gs, int64_t M, 
                                uint8_t* b_t, hipStream_t stream) {
   if (gs == 64) return launch_prefill64_prep(x, w, M, K, N, L, a_t, q_t, b_t, stream);
   const int64_t xwaves = (L.mpad / 16) * (K / gs);                // (row tile, group) tasks
-  const int64_t wwaves = (L.npad / kTileCols) * tiled_kblocks(K);  // 64 weight chunks each
+  const int64_t wwaves =                                           // kPrepWChunks x 64 chunks each
+      ((L.npad / kTileCols) * tiled_kblocks(K) + kPrepWChunks - 1) / kPrepWChunks;
   const unsigned blocks = (unsigned)((xwaves + wwaves + 3) / 4);
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   const uint8_t* wp = static_cast<const uint8_t*>(w);
