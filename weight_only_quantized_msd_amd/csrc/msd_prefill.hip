@@ -47,12 +47,16 @@
 //   contiguous runs: 36 KB of A and BN/16 * 1.5 KB of B.
 //
 // GEMM tiling: workgroup tile BM = 128 rows x BN = 256 (or 128) columns, 8
-// waves as 2 (along M) x 4 (along N), wave tile 64 rows x BN/4 columns =
-// 4 x NT MFMA tiles of 16x16, times 3 levels.  A wave holds its NT B
-// operands for the group and walks its row tiles: per row tile the 3 level
-// operands and the rows' weights, then per column tile 3 MFMAs, with the
-// fp32 combine of the previous output tile interleaved (4 VALU per output
-// and group: three for the levels, one for the scale and the running sum).
+// waves as 4 (along M) x 2 (along N), wave tile 32 rows x BN/2 columns =
+// 2 x NT MFMA tiles of 16x16, times 3 levels.  A wave holds its 2 x 3 level
+// operands and the rows' weights for the group and walks its column tiles,
+// reading the next column tile's B operand while the current one is used:
+// per output tile 3 MFMAs, with the fp32 combine of the previous output tile
+// interleaved (4 VALU per output and group: three for the levels, one for
+// the scale and the running sum).  The operand reads from LDS are the
+// GEMM's largest cost after the MFMA and the combine (FP6 MFMA and VALU
+// issue do not overlap here): a wave reads 6 A + NT B tiles per group, the
+// fewest for 16 x 16 output tiles per wave (64 x 64 waves read 12 + 4).
 // Per group a workgroup reads 36 KB + BN/16 * 1.5 KB of operands; LDS holds
 // one group's operands, weights and scales, double-buffered: the next group
 // is copied global -> LDS directly (global_load_lds, no staging registers;
@@ -70,12 +74,12 @@
 namespace wqbmm {
 namespace pf {
 constexpr int BM = 128;
-constexpr int WAVES_M = 2;     // waves along M
-constexpr int WAVES_N = 4;     // waves along N
+constexpr int WAVES_M = 4;     // waves along M
+constexpr int WAVES_N = 2;     // waves along N
 constexpr int WAVES = WAVES_M * WAVES_N;
 constexpr int THREADS = 64 * WAVES;
-constexpr int WM = BM / WAVES_M;   // 64 rows per wave
-constexpr int MT = WM / 16;    // 4 row tiles per wave
+constexpr int WM = BM / WAVES_M;   // 32 rows per wave
+constexpr int MT = WM / 16;    // 2 row tiles per wave
 constexpr int RT = BM / 16;    // 8 row tiles per block
 constexpr int TILE = 1536;     // bytes of one operand tile (16 x 128 k, e2m3)
 constexpr int TILE_LO = 1024;  // its [lane][dwords 0-3] part
@@ -273,7 +277,7 @@ __global__ __launch_bounds__(pf::THREADS, 1) void msd_gemm_kernel(
     int32_t* __restrict__ y_int) {
   using namespace pf;
   constexpr int CT = BN / 16;                          // column tiles per block
-  constexpr int NT = CT / WAVES_N;                     // column tiles per wave: 4 or 2
+  constexpr int NT = CT / WAVES_N;                     // column tiles per wave: 8 or 4
   constexpr int WN = NT * 16;                          // columns per wave
   constexpr int B_GROUP = CT * TILE;                   // one group of a column block
   constexpr int A_KB = A_GROUP / 1024;                 // 36 pieces of 1 KB
@@ -383,52 +387,50 @@ __global__ __launch_bounds__(pf::THREADS, 1) void msd_gemm_kernel(
     }
   };
 
-  // Steps 9-11 for one group from one buffer.  The wave keeps its NT B
-  // operands and its 4 x 3 level operands; per row tile it reads the rows'
-  // weights, and per output tile issues 3 MFMAs, then combines the previous
-  // output tile (so the combine never waits for the MFMA it follows).
+  // Steps 9-11 for one group from one buffer.  The wave reads its first B
+  // operand and its MT x 3 level operands, then walks its column tiles with
+  // the next column tile's B operand read ahead (two B registers in turn):
+  // per output tile 3 MFMAs, then the combine of the previous output tile (so
+  // the combine never waits for the MFMA it follows).  A register that a
+  // load overwrites was last read by MFMAs issued before that load.
   auto compute = [&](const uint8_t* sa, const uint8_t* sb, const float* sq, const uint16_t* ss, int g_) {
-    v8i bf[NT];
-#pragma unroll
-    for (int c = 0; c < NT; ++c) bf[c] = lds_operand(sb + (wn * NT + c) * TILE, lane);
-    uint32_t sraw[NT];
-    if constexpr (!YINT) {
-#pragma unroll
-      for (int c = 0; c < NT; ++c) sraw[c] = ss[wn * WN + c * 16 + (lane & 15)];
-    }
-    v4f q[2][3];                 // weights of the current and the previous row tile
-    v4f acc[2][3];               // MFMA results of the current and the previous output tile
-    // Every operand register of the group is loaded before the first MFMA
-    // and none is reloaded within the group (a register read by an MFMA is
-    // not the destination of a later load until the group's barrier).
+    v8i bf[2];
+    bf[0] = lds_operand(sb + (wn * NT) * TILE, lane);
     v8i af[MT][3];
 #pragma unroll
     for (int r = 0; r < MT; ++r)
 #pragma unroll
       for (int l = 0; l < 3; ++l) af[r][l] = lds_operand(sa + (l * RT + wm * MT + r) * TILE, lane);
+    uint32_t sraw[NT];
+    v4f q[MT][3];                // the row tiles' level weights
+    if constexpr (!YINT) {
 #pragma unroll
-    for (int r = 0; r < MT; ++r) {
-      const int rt = wm * MT + r;
-      if constexpr (!YINT) {
+      for (int c = 0; c < NT; ++c) sraw[c] = ss[wn * WN + c * 16 + (lane & 15)];
+#pragma unroll
+      for (int r = 0; r < MT; ++r)
 #pragma unroll
         for (int l = 0; l < 3; ++l)
-          q[r & 1][l] = *reinterpret_cast<const v4f*>(sq + l * BM + rt * 16 + 4 * (lane >> 4));
-      }
+          q[r][l] = *reinterpret_cast<const v4f*>(sq + l * BM + (wm * MT + r) * 16 + 4 * (lane >> 4));
+    }
+    v4f acc[2][3];               // MFMA results of the current and the previous output tile
 #pragma unroll
-      for (int c = 0; c < NT; ++c) {
-        const int j = r * NT + c, cur = j & 1;
+    for (int c = 0; c < NT; ++c) {
+      if (c + 1 < NT) bf[(c + 1) & 1] = lds_operand(sb + (wn * NT + c + 1) * TILE, lane);
+#pragma unroll
+      for (int r = 0; r < MT; ++r) {
+        const int j = c * MT + r, cur = j & 1;
 #pragma unroll
         for (int l = 0; l < 3; ++l)
           acc[cur][l] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              af[r][l], bf[c], v4f{0.f, 0.f, 0.f, 0.f}, 2, 2, 0, kScaleA, 0, kScaleB);
+              af[r][l], bf[c & 1], v4f{0.f, 0.f, 0.f, 0.f}, 2, 2, 0, kScaleA, 0, kScaleB);
         if (j > 0) {
-          const int pr = (j - 1) / NT, pc = (j - 1) % NT;
-          epilogue(pr, pc, acc[cur ^ 1], q[pr & 1], sraw, g_);
+          const int pc = (j - 1) / MT, pr = (j - 1) % MT;
+          epilogue(pr, pc, acc[cur ^ 1], q[pr], sraw, g_);
         }
       }
     }
     constexpr int jl = MT * NT - 1;
-    epilogue(jl / NT, jl % NT, acc[jl & 1], q[(jl / NT) & 1], sraw, g_);
+    epilogue(jl % MT, jl / MT, acc[jl & 1], q[jl % MT], sraw, g_);
   };
 
   // Buffer 0 holds the even-indexed groups of the range, buffer 1 the odd
