@@ -34,9 +34,14 @@
 //   which are the two 64-row steps of tiled-weight chunk lane l, so a chunk
 //   converts in place.  For GS = 64 only u is real and v is zero.  A and B
 //   are packed by the same instruction from the same k assignment, so the
-//   MFMA pairs equal k (whatever its own slot order).  A tile is stored as
-//   [lane][dwords 0-3] (1 KB) then [lane][dwords 4-5] (512 bytes), 1536
-//   bytes, read by one conflict-free ds_read_b128 and one ds_read_b64.
+//   MFMA pairs equal k (whatever its own slot order).  Tiles are stored in
+//   pairs (tile 2j, 2j+1; 3072 bytes): [lane][dwords 0-3 of tile 2j] (1 KB),
+//   [lane][dwords 0-3 of tile 2j+1] (1 KB), then [lane][dwords 4-5 of tile
+//   2j, dwords 4-5 of tile 2j+1] (1 KB), so that a pair is read by three
+//   conflict-free ds_read_b128 (on gfx950 a ds_read_b64 moves half the bytes
+//   per cycle of a ds_read_b128: 128 against about 230 bytes per cycle and
+//   CU, measured).  The pairs are the two row tiles of a level that one
+//   GEMM wave holds, and two adjacent column tiles.
 //   A_t: [row block of 128][group][level][row tile 0..7][tile]
 //   B_t: [column block of BN][group][column tile 0..BN/16-1][tile]
 //   Q_t: [group][row block][level][128 rows] fp32: A_max * w_l, the row's
@@ -89,9 +94,6 @@ constexpr int NXCD = 8;
 constexpr int BAND = 4;        // row blocks per band of the tile order
 }  // namespace pf
 
-// runs of 64 tiled-weight chunks converted per wave of the prep kernel
-constexpr int kPrepWChunks = 4;
-
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v6i __attribute__((ext_vector_type(6)));
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -125,25 +127,18 @@ __device__ __forceinline__ v6i pack_e2m3(const v16f& u, const v16f& v, float div
   return r;
 }
 
-// One packed operand lane -> its tile slot: dwords 0-3 at 16*slot, dwords 4-5
-// at 1024 + 8*slot.
-__device__ __forceinline__ void store_operand(uint8_t* tile, int slot, const v6i& p) {
-  *reinterpret_cast<v4i*>(tile + slot * 16) = v4i{p[0], p[1], p[2], p[3]};
-  *reinterpret_cast<v2i*>(tile + pf::TILE_LO + slot * 8) = v2i{p[4], p[5]};
-}
-
 // ---------------------------------------------------------------- prep kernel
-// Waves [0, xwaves): one (16-row tile, group) each, steps 1-8 for its 16 x GS
-// elements.  Lane l takes row l/4 and, with kq = l%4, the elements of operand
-// lane 16*kq + row (u: k = 16*kq + j, v: k = 64 + 16*kq + j), so a group's
-// maximum is a 4-lane reduction and the wave's stores fill one whole tile per
-// level; the rows' level weights A_max * w_l go to Q_t.
-// Waves [xwaves, ...): kPrepWChunks runs of 64 tiled-weight chunks each, one
-// 16-byte chunk per lane and run (column tiles up to the padded width; those
-// beyond N become zeros), each converted in place into operand lane l of its
-// column tile (column blocks of BN).  A wave issues all its loads before
-// converting: at one run per wave the waves spent most of their time
-// waiting for a single load.
+// Waves [0, xwaves): one (pair of 16-row tiles, group) each, steps 1-8 for
+// its 2 x 16 x GS elements, one row tile after the other.  Lane l takes row
+// l/4 and, with kq = l%4, the elements of operand lane 16*kq + row (u: k =
+// 16*kq + j, v: k = 64 + 16*kq + j), so a group's maximum is a 4-lane
+// reduction; the wave's stores fill one whole tile pair per level (every
+// store a whole 16-byte lane); the rows' level weights A_max * w_l go to Q_t.
+// Waves [xwaves, ...): one (pair of column tiles, pair of 128-row blocks)
+// each: four 16-byte tiled-weight chunks per lane (column tiles up to the
+// padded width; those beyond N become zeros), all loaded before any is
+// converted in place into operand lane l of its column tile (column blocks
+// of BN), and each block's tile pair stored whole.
 template <int GS>
 __global__ __launch_bounds__(256) void msd_prep_kernel(const uint16_t* __restrict__ x,
                                                        const uint8_t* __restrict__ wt, int M,
@@ -151,122 +146,136 @@ __global__ __launch_bounds__(256) void msd_prep_kernel(const uint16_t* __restric
                                                        int64_t xwaves, uint8_t* __restrict__ a_t,
                                                        float* __restrict__ q_t,
                                                        uint8_t* __restrict__ b_t) {
+  static_assert(GS == 128, "the group-128 path (group size 64 has a kernel of its own)");
   using namespace pf;
   const int G = K / GS;
   const int lane = threadIdx.x & 63;
   const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (wid < xwaves) {
-    const int mt = (int)(wid / G), g = (int)(wid % G);
+    const int mtp = (int)(wid / G), g = (int)(wid % G);
     const int r = lane >> 2, kq = lane & 3;
-    const int m = mt * 16 + r;
-    const bool real = m < M;                         // padding rows decompose zeros
-    const uint16_t* src = x + (real ? (int64_t)m * K + (int64_t)g * GS + 16 * kq : 0);
-    float a[32];
+    const int rb = (2 * mtp) / RT, rt0 = (2 * mtp) % RT;   // rt0 even: the pair's first row tile
+    uint32_t hi0[3][2];                                     // the first row tile's dwords 4-5
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      // c = 0, 1: u (k = 16kq + 8c ..); c = 2, 3: v (k = 64 + 16kq + 8(c-2) ..)
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (c < 2 || GS == 128) v = *reinterpret_cast<const uint4*>(src + (c < 2 ? 8 * c : 64 + 8 * (c - 2)));
-      const uint32_t vw[4] = {real ? v.x : 0u, real ? v.y : 0u, real ? v.z : 0u, real ? v.w : 0u};
+    for (int p = 0; p < 2; ++p) {
+      const int m = (2 * mtp + p) * 16 + r;
+      const bool real = m < M;                       // padding rows decompose zeros
+      const uint16_t* src = x + (real ? (int64_t)m * K + (int64_t)g * GS + 16 * kq : 0);
+      float a[32];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        a[8 * c + 2 * i] = half_bits_to_float(vw[i] & 0xffffu);
-        a[8 * c + 2 * i + 1] = half_bits_to_float(vw[i] >> 16);
+      for (int c = 0; c < 4; ++c) {
+        // c = 0, 1: u (k = 16kq + 8c ..); c = 2, 3: v (k = 64 + 16kq + 8(c-2) ..)
+        const uint4 v = *reinterpret_cast<const uint4*>(src + (c < 2 ? 8 * c : 64 + 8 * (c - 2)));
+        const uint32_t vw[4] = {real ? v.x : 0u, real ? v.y : 0u, real ? v.z : 0u, real ? v.w : 0u};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          a[8 * c + 2 * i] = half_bits_to_float(vw[i] & 0xffffu);
+          a[8 * c + 2 * i + 1] = half_bits_to_float(vw[i] >> 16);
+        }
       }
-    }
-    float mx = 0.0f;
+      float mx = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 32; ++e) mx = fmaxf(mx, fabsf(a[e]));
-    const float amax = group_max<4>(mx);
-    v16f lv[3][2];
+      for (int e = 0; e < 32; ++e) mx = fmaxf(mx, fabsf(a[e]));
+      const float amax = group_max<4>(mx);
+      v16f lv[3][2];
 #pragma unroll
-    for (int l = 0; l < 3; ++l)
+      for (int l = 0; l < 3; ++l)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) lv[l][0][e] = lv[l][1][e] = 0.0f;
-    if (amax > 0.0f) {
-      const float rcp = msd_recip(amax);
+        for (int e = 0; e < 16; ++e) lv[l][0][e] = lv[l][1][e] = 0.0f;
+      if (amax > 0.0f) {
+        const float rcp = msd_recip(amax);
 #pragma unroll
-      for (int e = 0; e < 32; ++e) {
-        if (GS == 64 && e >= 16) break;              // v is zero for GS = 64
-        float r1, r2, r3;
-        msd_expand_f(a[e], amax, rcp, r1, r2, r3);
-        lv[0][e / 16][e % 16] = r1;
-        lv[1][e / 16][e % 16] = r2;
-        lv[2][e / 16][e % 16] = r3;
+        for (int e = 0; e < 32; ++e) {
+          float r1, r2, r3;
+          msd_expand_f(a[e], amax, rcp, r1, r2, r3);
+          lv[0][e / 16][e % 16] = r1;
+          lv[1][e / 16][e % 16] = r2;
+          lv[2][e / 16][e % 16] = r3;
+        }
       }
-    }
-    const int rb = mt / RT, rt = mt % RT;
+      // dwords 0-3 of this row tile's operands now; dwords 4-5 of the pair's
+      // two tiles together, once the second is packed (whole 16-byte lanes)
 #pragma unroll
-    for (int l = 0; l < 3; ++l) {
-      uint8_t* tile = a_t + ((((int64_t)rb * G + g) * 3 + l) * RT + rt) * TILE;
-      store_operand(tile, 16 * kq + r, pack_e2m3(lv[l][0], lv[l][1], 1.0f));
-    }
-    if (kq < 3) {                                    // lanes kq = 0, 1, 2: level weight kq of row m
-      const float w = kq == 0 ? kE1 : (kq == 1 ? kE2 : kE3);
-      q_t[(((int64_t)g * (Mpad / BM) + rb) * 3 + kq) * BM + (m % BM)] = amax * w;
+      for (int l = 0; l < 3; ++l) {
+        uint8_t* pair = a_t + ((((int64_t)rb * G + g) * 3 + l) * RT + rt0) * TILE;
+        const v6i pk = pack_e2m3(lv[l][0], lv[l][1], 1.0f);
+        const int slot = 16 * kq + r;
+        *reinterpret_cast<v4i*>(pair + p * TILE_LO + slot * 16) = v4i{pk[0], pk[1], pk[2], pk[3]};
+        if (p == 0) {
+          hi0[l][0] = (uint32_t)pk[4];
+          hi0[l][1] = (uint32_t)pk[5];
+        } else {
+          *reinterpret_cast<v4i*>(pair + 2 * TILE_LO + slot * 16) =
+              v4i{(int)hi0[l][0], (int)hi0[l][1], pk[4], pk[5]};
+        }
+      }
+      if (kq < 3) {                                  // lanes kq = 0, 1, 2: level weight kq of row m
+        const float w = kq == 0 ? kE1 : (kq == 1 ? kE2 : kE3);
+        q_t[(((int64_t)g * (Mpad / BM) + rb) * 3 + kq) * BM + (m % BM)] = amax * w;
+      }
     }
     return;
   }
-  // tiled weights: chunk t = (nt * KB + kb) * 64 + lane; a wave converts
-  // kPrepWChunks consecutive runs of 64 chunks, all loads issued first
+  // tiled weights: a wave converts the chunks of two adjacent column tiles
+  // for two consecutive 128-row blocks (chunk t = (nt * KB + kb) * 64 + lane),
+  // all four loads issued first, and stores each block's tile pair whole
   const int KB = (K + kTileRows - 1) / kTileRows;
-  const int64_t nchunks = (int64_t)(Npad / kTileCols) * KB * 64;
-  const int64_t t0 = (wid - xwaves) * (kPrepWChunks * 64) + lane;
+  const int KBP = (KB + 1) / 2;
+  const int64_t u = wid - xwaves;
+  const int ctp = (int)(u / KBP), kbp = (int)(u % KBP);
+  if (ctp >= Npad / (2 * kTileCols)) return;
   const int NTR = N / kTileCols;                     // real column tiles
-  uint4 v[kPrepWChunks];
+  uint4 v[2][2];                                      // [block of the pair][column tile of the pair]
 #pragma unroll
-  for (int c = 0; c < kPrepWChunks; ++c) {
-    const int64_t t = t0 + c * 64;
-    const bool ok = t < nchunks && (int)((t >> 6) / KB) < NTR;
-    v[c] = *reinterpret_cast<const uint4*>(wt + (ok ? t : 0) * 16);
-  }
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int nt = 2 * ctp + h, kb = 2 * kbp + i;
+      const bool ok = nt < NTR && kb < KB;
+      v[i][h] = *reinterpret_cast<const uint4*>(wt + (ok ? ((int64_t)nt * KB + kb) * 64 + lane : 0) * 16);
+    }
   __builtin_amdgcn_sched_barrier(0);                 // every load ahead of the first conversion
   const int CT = BN / 16;
+  const int cb = (2 * ctp) / CT, ct0 = (2 * ctp) % CT;   // ct0 even: the pair's first column tile
 #pragma unroll
-  for (int c = 0; c < kPrepWChunks; ++c) {
-    const int64_t t = t0 + c * 64;
-    if (t >= nchunks) break;                          // wave-uniform (runs of 64)
-    const int kb = (int)((t >> 6) % KB);
-    const int nt = (int)((t >> 6) / KB);
-    const bool real = nt < NTR;                       // columns beyond N become zeros
-    const int32_t dw[4] = {real ? (int32_t)v[c].x : 0, real ? (int32_t)v[c].y : 0,
-                           real ? (int32_t)v[c].z : 0, real ? (int32_t)v[c].w : 0};
-    // step s (dwords 2s, 2s+1), element i = 8d + j: dword 2s + d, low nibble of
-    // byte j for j < 4, high nibble of byte j - 4 otherwise
-    v16f w[2];
+  for (int i = 0; i < 2; ++i) {
+    const int kb = 2 * kbp + i;
+    if (kb >= KB) break;                              // wave-uniform
+    v6i pk[2];
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+    for (int h = 0; h < 2; ++h) {
+      const bool real = 2 * ctp + h < NTR;            // columns beyond N become zeros
+      const int32_t dw[4] = {real ? (int32_t)v[i][h].x : 0, real ? (int32_t)v[i][h].y : 0,
+                             real ? (int32_t)v[i][h].z : 0, real ? (int32_t)v[i][h].w : 0};
+      // step s (dwords 2s, 2s+1), element i = 8d + j: dword 2s + d, low nibble of
+      // byte j for j < 4, high nibble of byte j - 4 otherwise
+      v16f w[2];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int j = i % 8;
-        w[st][i] = sfield(dw[2 * st + i / 8], j < 4 ? 8 * j : 8 * (j - 4) + 4, 4);
-      }
-    const int cb = nt / CT, ct = nt % CT;
-    if constexpr (GS == 128) {
-      uint8_t* tile = b_t + (((int64_t)cb * G + kb) * CT + ct) * TILE;
-      store_operand(tile, lane, pack_e2m3(w[0], w[1], 2.0f));
-    } else {
-      v16f zero;
+      for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) zero[i] = 0.0f;
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const int g = 2 * kb + st;
-        if (g >= G) break;                            // padding rows of the last block
-        uint8_t* tile = b_t + (((int64_t)cb * G + g) * CT + ct) * TILE;
-        store_operand(tile, lane, pack_e2m3(w[st], zero, 2.0f));
-      }
+        for (int e = 0; e < 16; ++e) {
+          const int j = e % 8;
+          w[st][e] = sfield(dw[2 * st + e / 8], j < 4 ? 8 * j : 8 * (j - 4) + 4, 4);
+        }
+      pk[h] = pack_e2m3(w[0], w[1], 2.0f);
     }
+    uint8_t* pair = b_t + (((int64_t)cb * G + kb) * CT + ct0) * TILE;
+    *reinterpret_cast<v4i*>(pair + lane * 16) = v4i{pk[0][0], pk[0][1], pk[0][2], pk[0][3]};
+    *reinterpret_cast<v4i*>(pair + TILE_LO + lane * 16) = v4i{pk[1][0], pk[1][1], pk[1][2], pk[1][3]};
+    *reinterpret_cast<v4i*>(pair + 2 * TILE_LO + lane * 16) = v4i{pk[0][4], pk[0][5], pk[1][4], pk[1][5]};
   }
 }
 
 // ---------------------------------------------------------------- GEMM kernel
-// One operand (six dwords) of lane `lane` from an LDS tile, as the MFMA's
-// eight-dword argument (the last two are unused by the FP6 form).
-__device__ __forceinline__ v8i lds_operand(const uint8_t* tile, int lane) {
-  const v4i lo = *reinterpret_cast<const v4i*>(tile + lane * 16);
-  const v2i hi = *reinterpret_cast<const v2i*>(tile + pf::TILE_LO + lane * 8);
-  return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], 0, 0};
+// The two operands (six dwords each) of lane `lane` from an LDS tile pair
+// (address of its first tile), as the MFMA's eight-dword arguments (the last
+// two are unused by the FP6 form): three ds_read_b128.
+__device__ __forceinline__ void lds_operand_pair(const uint8_t* pair, int lane, v8i& op0, v8i& op1) {
+  const v4i lo0 = *reinterpret_cast<const v4i*>(pair + lane * 16);
+  const v4i lo1 = *reinterpret_cast<const v4i*>(pair + pf::TILE_LO + lane * 16);
+  const v4i hi = *reinterpret_cast<const v4i*>(pair + 2 * pf::TILE_LO + lane * 16);
+  op0 = v8i{lo0[0], lo0[1], lo0[2], lo0[3], hi[0], hi[1], 0, 0};
+  op1 = v8i{lo1[0], lo1[1], lo1[2], lo1[3], hi[2], hi[3], 0, 0};
 }
 
 template <int GS, int BN, bool YINT>
@@ -387,20 +396,20 @@ __global__ __launch_bounds__(pf::THREADS, 1) void msd_gemm_kernel(
     }
   };
 
-  // Steps 9-11 for one group from one buffer.  The wave reads its first B
-  // operand and its MT x 3 level operands, then walks its column tiles with
-  // the next column tile's B operand read ahead (two B registers in turn):
-  // per output tile 3 MFMAs, then the combine of the previous output tile (so
-  // the combine never waits for the MFMA it follows).  A register that a
-  // load overwrites was last read by MFMAs issued before that load.
+  // Steps 9-11 for one group from one buffer.  The wave reads its first pair
+  // of B operands and its 2 x 3 level operands (one pair per level), then
+  // walks its column tiles with the next pair of B operands read ahead (two
+  // pairs of B registers in turn): per output tile 3 MFMAs, then the combine
+  // of the previous output tile (so the combine never waits for the MFMA it
+  // follows).  A register that a load overwrites was last read by MFMAs
+  // issued before that load.
+  static_assert(MT == 2 && NT % 2 == 0, "operand tiles are read in pairs");
   auto compute = [&](const uint8_t* sa, const uint8_t* sb, const float* sq, const uint16_t* ss, int g_) {
-    v8i bf[2];
-    bf[0] = lds_operand(sb + (wn * NT) * TILE, lane);
+    v8i bf[2][2];
+    lds_operand_pair(sb + (wn * NT) * TILE, lane, bf[0][0], bf[0][1]);
     v8i af[MT][3];
 #pragma unroll
-    for (int r = 0; r < MT; ++r)
-#pragma unroll
-      for (int l = 0; l < 3; ++l) af[r][l] = lds_operand(sa + (l * RT + wm * MT + r) * TILE, lane);
+    for (int l = 0; l < 3; ++l) lds_operand_pair(sa + (l * RT + wm * MT) * TILE, lane, af[0][l], af[1][l]);
     uint32_t sraw[NT];
     v4f q[MT][3];                // the row tiles' level weights
     if constexpr (!YINT) {
@@ -415,14 +424,16 @@ __global__ __launch_bounds__(pf::THREADS, 1) void msd_gemm_kernel(
     v4f acc[2][3];               // MFMA results of the current and the previous output tile
 #pragma unroll
     for (int c = 0; c < NT; ++c) {
-      if (c + 1 < NT) bf[(c + 1) & 1] = lds_operand(sb + (wn * NT + c + 1) * TILE, lane);
+      const int cp = c / 2;
+      if (c % 2 == 0 && cp + 1 < NT / 2)
+        lds_operand_pair(sb + (wn * NT + c + 2) * TILE, lane, bf[(cp + 1) & 1][0], bf[(cp + 1) & 1][1]);
 #pragma unroll
       for (int r = 0; r < MT; ++r) {
         const int j = c * MT + r, cur = j & 1;
 #pragma unroll
         for (int l = 0; l < 3; ++l)
           acc[cur][l] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              af[r][l], bf[c & 1], v4f{0.f, 0.f, 0.f, 0.f}, 2, 2, 0, kScaleA, 0, kScaleB);
+              af[r][l], bf[cp & 1][c & 1], v4f{0.f, 0.f, 0.f, 0.f}, 2, 2, 0, kScaleA, 0, kScaleB);
         if (j > 0) {
           const int pc = (j - 1) / MT, pr = (j - 1) % MT;
           epilogue(pr, pc, acc[cur ^ 1], q[pr], sraw, g_);
@@ -491,9 +502,8 @@ hipError_t launch_prefill_prep(const void* x, const void* w, int gs, int64_t M, 
                                int64_t N, const PrefillLayout& L, uint8_t* a_t, float* q_t,
                                uint8_t* b_t, hipStream_t stream) {
   if (gs == 64) return launch_prefill64_prep(x, w, M, K, N, L, a_t, q_t, b_t, stream);
-  const int64_t xwaves = (L.mpad / 16) * (K / gs);                // (row tile, group) tasks
-  const int64_t wwaves =                                           // kPrepWChunks x 64 chunks each
-      ((L.npad / kTileCols) * tiled_kblocks(K) + kPrepWChunks - 1) / kPrepWChunks;
+  const int64_t xwaves = (L.mpad / 32) * (K / gs);                // (row tile pair, group) tasks
+  const int64_t wwaves = (L.npad / 32) * ((tiled_kblocks(K) + 1) / 2);   // (column tile pair, block pair)
   const unsigned blocks = (unsigned)((xwaves + wwaves + 3) / 4);
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   const uint8_t* wp = static_cast<const uint8_t*>(w);
