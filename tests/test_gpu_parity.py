@@ -235,6 +235,9 @@ RAGGED = [  # (M, K, N, gs)
     (130, 384, 288, 128), (257, 256, 128, 64),
     # M <= 4 with K split over workgroups and a last chunk that ends inside it
     (1, 4736, 96, 64), (3, 6272, 160, 128),
+    # prefill with columns padded to the GEMM's column block inside a tile pair
+    # range (N = 96: six real 16-column tiles, ten padding tiles at BN = 128)
+    (130, 384, 96, 128),
 ]
 
 
