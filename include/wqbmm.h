@@ -49,9 +49,21 @@
  *     N >= 1, K % group_size == 0, N % 32 == 0, M <= 2^24, K <= 2^20,
  *     N <= 2^20, every pointer 16-byte aligned.
  *   - group_size must be 64 or 128 (other positive values: WQBMM_ERR_UNSUPPORTED).
- *   - The library keeps a per-(device, stream) workspace that it allocates on
- *     first use and grows on demand (hipMalloc; a growth synchronizes that
- *     stream first).  Calls on different streams do not share workspace.
+ *   - Workspace.  The two-kernel paths (decode at 4 < M <= 16, prefill) pass
+ *     operands between their kernels through device memory, and the fused
+ *     decode kernel (M <= 4) with K > 4096 sums its K-splits in accumulators.
+ *     The library keeps that memory per (device, stream): allocated on first
+ *     need and grown on demand with hipMalloc.  Growth never synchronizes and
+ *     never frees: a replaced buffer stays allocated until the process ends
+ *     (a graph captured earlier may still use it), and sizes at least double,
+ *     so the retired buffers of a stream take less than its current one.
+ *     Growth is refused while the stream is being captured into a graph:
+ *     the call returns WQBMM_ERR_CAPTURE and launches nothing.  Make one
+ *     eager call of the largest shape on a stream before capturing on it.
+ *     Calls on different streams never share workspace.  Calls captured on a
+ *     stream use that stream's workspace when their graph is replayed, so a
+ *     replay must not run concurrently with other calls that use the same
+ *     stream's workspace (replay on that stream, or synchronize in between).
  *   - Results are deterministic: the same inputs give bit-identical outputs.
  *   - Only gfx950 (MI355X) is supported: other devices give WQBMM_ERR_UNSUPPORTED.
  *   - Finite inputs are assumed; Inf/NaN inputs give unspecified outputs.
@@ -71,7 +83,8 @@ typedef enum wqbmm_status {
   WQBMM_ERR_INVALID = 2,     /* a shape / alignment rule above is violated       */
   WQBMM_ERR_UNSUPPORTED = 3, /* group_size not 64/128, or the device is not gfx950 */
   WQBMM_ERR_LAUNCH = 4,      /* a HIP call or kernel launch failed               */
-  WQBMM_ERR_ALLOC = 5        /* workspace allocation failed                      */
+  WQBMM_ERR_ALLOC = 5,       /* workspace allocation failed                      */
+  WQBMM_ERR_CAPTURE = 6      /* the workspace would have to grow during graph capture */
 } wqbmm_status;
 
 /* Kernel path selector for the *_path / *_yint entry points. */

@@ -20,6 +20,7 @@ WQBMM_ERR_INVALID = 2
 WQBMM_ERR_UNSUPPORTED = 3
 WQBMM_ERR_LAUNCH = 4
 WQBMM_ERR_ALLOC = 5
+WQBMM_ERR_CAPTURE = 6
 
 WQBMM_PATH_AUTO = 0
 WQBMM_PATH_DECODE = 1

@@ -18,6 +18,7 @@
 #include <map>
 #include <mutex>
 #include <utility>
+#include <vector>
 
 #include "../../include/wqbmm.h"
 #include "msd_launch.hpp"
@@ -65,59 +66,119 @@ wqbmm_status check_device(int* dev_out) {
   return it->second ? WQBMM_OK : WQBMM_ERR_UNSUPPORTED;
 }
 
-// ---- per-(device, stream) workspace, grown on demand
-// Layout: [decode accumulators][scratch].  The decode accumulators must be
-// zero before a decode launch; the kernel re-arms every element it uses, and
-// no other kernel writes that region, so it is zeroed only when allocated.
-// The scratch region holds the prefill operand tiles.
+// ---- scratch memory of one call
+// A call's kernels use up to two regions beside its inputs and outputs:
+//   acc: the split-K accumulators of the fused decode kernel (M <= 4 with K
+//        split over workgroups).  They must be zero before a launch; every
+//        launch that completes leaves the elements it used at zero again, and
+//        no other kernel writes this region, so it is zeroed once, when the
+//        memory is first handed out;
+//   ops: the operands that the two-kernel paths pass from their operand
+//        kernel to their contraction kernel (decode at 4 < M <= 16, prefill).
+struct Buffers {
+  uint64_t* acc = nullptr;
+  size_t acc_bytes = 0;
+  uint8_t* ops = nullptr;
+  size_t ops_bytes = 0;
+};
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Bytes of each region a call needs.
+struct Needs {
+  size_t acc = 0;
+  size_t ops = 0;
+};
+
+size_t prefill_ops_bytes(const wqbmm::PrefillLayout& L) {
+  return round_up(L.a_bytes, 256) + round_up(L.q_bytes, 256) + round_up(L.b_bytes, 256);
+}
+
+Needs needs_of(int path, int64_t gs, int64_t M, int64_t K, int64_t N, int64_t g_begin, int64_t g_end,
+               bool yint) {
+  Needs n;
+  if (path == WQBMM_PATH_DECODE) {
+    if (M > 4) {
+      n.ops = wqbmm::decode_gemv_workspace_bytes((int)gs, K);
+    } else if (!yint) {
+      n.acc = wqbmm::decode_accum_bytes(wqbmm::decode_plan((int)gs, M, K, N, g_begin, g_end), M, N);
+    }
+  } else {
+    n.ops = prefill_ops_bytes(wqbmm::prefill_layout((int)gs, M, K, N));
+  }
+  n.acc = round_up(n.acc, 256);
+  n.ops = round_up(n.ops, 256);
+  return n;
+}
+
+// Whether `stream` is being captured into a graph (an invalidated capture
+// counts as one).  False with *err set if the query fails.
+bool capturing(hipStream_t stream, wqbmm_status* err) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess) {
+    *err = WQBMM_ERR_LAUNCH;
+    return false;
+  }
+  *err = WQBMM_OK;
+  return cs != hipStreamCaptureStatusNone;
+}
+
+// ---- per-(device, stream) workspace of wqbmm_a16w4_msd and friends
+// Grown on demand, never while the stream is being captured (a captured graph
+// would hold the growth's allocation and zeroing only inside the graph), and
+// never freed: a buffer that a larger one replaces is retired but stays
+// allocated until the process ends, because a graph captured earlier may
+// still replay kernels that use it, and because freeing it would have to wait
+// for the stream.  Sizes at least double on growth, so the retired buffers
+// of a stream add up to less than its current one.  The accumulator region
+// of a new buffer is zeroed by a kernel on the stream, ahead of the call's
+// own kernels; nothing synchronizes the host.
 struct Workspace {
   void* base = nullptr;
   size_t acc_bytes = 0;
-  size_t scratch_bytes = 0;
-  // path and shape whose operands the scratch region currently holds
+  size_t ops_bytes = 0;
+  // path and shape whose operands the ops region currently holds
   // (prep_path 0: none, WQBMM_PATH_DECODE or WQBMM_PATH_PREFILL)
   int prep_path = 0;
   int64_t prep_gs = 0, prep_m = -1, prep_k = 0, prep_n = 0;
 };
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+std::vector<void*> g_retired;
 
-size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+size_t grown(size_t have, size_t need) {
+  if (need <= have) return have;
+  return std::max(need + need / 4, 2 * have);
+}
 
-// Returns an accumulator region of at least `acc` bytes (zeroed) and a
-// scratch region of at least `scratch` bytes for launches on `stream`.
-// Growth synchronizes `stream` so that no launch still using the old buffer
-// is pending before it is freed; a new buffer gets its accumulator region
-// zeroed by a kernel enqueued on `stream`.
-wqbmm_status get_workspace(int dev, hipStream_t stream, size_t acc, size_t scratch,
-                           uint64_t** acc_out, uint8_t** scratch_out) {
+wqbmm_status get_workspace(int dev, hipStream_t stream, const Needs& need, Buffers* out) {
+  if (need.acc == 0 && need.ops == 0) {   // e.g. the fused decode kernel without a K split
+    *out = Buffers{};
+    return WQBMM_OK;
+  }
   std::lock_guard<std::mutex> lk(g_mu);
   Workspace& ws = g_ws[std::make_pair(dev, stream)];
-  acc = round_up(acc, 256);
-  scratch = round_up(scratch, 256);
-  if (ws.acc_bytes < acc || ws.scratch_bytes < scratch || !ws.base) {
-    const size_t new_acc = std::max(ws.acc_bytes, acc + acc / 4);
-    const size_t new_scratch = std::max(ws.scratch_bytes, scratch + scratch / 4);
-    if (ws.base) {
-      if (hipStreamSynchronize(stream) != hipSuccess) return WQBMM_ERR_LAUNCH;
-      (void)hipFree(ws.base);
-      ws.base = nullptr;
-      ws.acc_bytes = ws.scratch_bytes = 0;
-    }
+  if (!ws.base || ws.acc_bytes < need.acc || ws.ops_bytes < need.ops) {
+    wqbmm_status st;
+    if (capturing(stream, &st)) return WQBMM_ERR_CAPTURE;
+    if (st != WQBMM_OK) return st;
+    const size_t acc = round_up(grown(ws.acc_bytes, need.acc), 256);
+    const size_t ops = round_up(grown(ws.ops_bytes, need.ops), 256);
     void* p = nullptr;
-    const size_t total = round_up(new_acc, 256) + round_up(new_scratch, 256) + 256;
-    if (hipMalloc(&p, total) != hipSuccess) return WQBMM_ERR_ALLOC;
-    if (wqbmm::launch_zero_words(static_cast<uint32_t*>(p), (int64_t)(round_up(new_acc, 256) / 4),
-                                 stream) != hipSuccess) {
-      (void)hipFree(p);
+    if (hipMalloc(&p, acc + ops + 256) != hipSuccess) return WQBMM_ERR_ALLOC;
+    if (wqbmm::launch_zero_words(static_cast<uint32_t*>(p), (int64_t)(acc / 4), stream) != hipSuccess) {
+      g_retired.push_back(p);
       return WQBMM_ERR_LAUNCH;
     }
+    if (ws.base) g_retired.push_back(ws.base);
     ws.base = p;
-    ws.acc_bytes = round_up(new_acc, 256);
-    ws.scratch_bytes = round_up(new_scratch, 256);
+    ws.acc_bytes = acc;
+    ws.ops_bytes = ops;
     ws.prep_path = 0;
   }
-  *acc_out = static_cast<uint64_t*>(ws.base);
-  *scratch_out = static_cast<uint8_t*>(ws.base) + ws.acc_bytes;
+  out->acc = static_cast<uint64_t*>(ws.base);
+  out->acc_bytes = ws.acc_bytes;
+  out->ops = static_cast<uint8_t*>(ws.base) + ws.acc_bytes;
+  out->ops_bytes = ws.ops_bytes;
   return WQBMM_OK;
 }
 
@@ -129,7 +190,7 @@ int resolve_path(int path, int64_t M, int64_t K, int64_t N, int64_t gs) {
 wqbmm_status launch_status(hipError_t e) { return e == hipSuccess ? WQBMM_OK : WQBMM_ERR_LAUNCH; }
 
 // Records (stage 0 or 1) or checks (stage 2) which path and shape the
-// operands in the scratch region of (dev, stream) belong to.
+// operands in the ops region of (dev, stream) belong to.
 wqbmm_status track_operands(int dev, hipStream_t stream, int path, int stage, int64_t gs, int64_t M,
                             int64_t K, int64_t N) {
   std::lock_guard<std::mutex> lk(g_mu);
@@ -142,76 +203,63 @@ wqbmm_status track_operands(int dev, hipStream_t stream, int path, int stage, in
   return WQBMM_OK;
 }
 
-wqbmm_status run_prefill(int dev, const void* x, const void* w, const void* scale, int64_t gs,
-                         int64_t M, int64_t K, int64_t N, int64_t g_begin, int64_t g_end, void* y,
-                         int32_t* y_int, int stage, hipStream_t stream);
-
 // The decode path.  M <= 4: one fused kernel (stage 1 launches nothing);
 // 4 < M <= 16: the operand kernel (stage 1) and the contraction (stage 2).
-wqbmm_status run_decode(int dev, const void* x, const void* w, const void* scale, int64_t gs,
+// `b` holds at least needs_of(...) bytes in each region.
+wqbmm_status run_decode(const Buffers& b, const void* x, const void* w, const void* scale, int64_t gs,
                         int64_t M, int64_t K, int64_t N, int64_t g_begin, int64_t g_end, void* y,
                         int32_t* y_int, int stage, hipStream_t stream) {
-  uint64_t* accum = nullptr;
-  uint8_t* scratch = nullptr;
-  wqbmm_status st;
-  if (M > 4) {
-    st = get_workspace(dev, stream, 0, wqbmm::decode_gemv_workspace_bytes((int)gs, K), &accum, &scratch);
-    if (st != WQBMM_OK) return st;
-    st = track_operands(dev, stream, WQBMM_PATH_DECODE, stage, gs, M, K, N);
-    if (st != WQBMM_OK) return st;
+  if (M > 4)
     return launch_status(wqbmm::launch_decode_gemv(x, w, scale, (int)gs, M, K, N, g_begin, g_end, y,
-                                                   y_int, scratch, stage, stream));
-  }
+                                                   y_int, b.ops, stage, stream));
   if (stage == 1) return WQBMM_OK;
   const DecodePlan plan = wqbmm::decode_plan((int)gs, M, K, N, g_begin, g_end);
-  const size_t abytes = y_int ? 0 : wqbmm::decode_accum_bytes(plan, M, N);
-  if (abytes) {
-    st = get_workspace(dev, stream, abytes, 0, &accum, &scratch);
-    if (st != WQBMM_OK) return st;
-  }
   return launch_status(wqbmm::launch_decode(x, w, scale, (int)gs, M, K, N, g_begin, g_end, y,
-                                            y_int, accum, plan, stream));
+                                            y_int, b.acc, plan, stream));
 }
 
-// Steps 1-11 (or 1-9 with y_int) on one of the two kernel paths.
-wqbmm_status run(const void* x, const void* w, const void* scale, int64_t gs, int64_t M,
-                 int64_t K, int64_t N, int64_t g_begin, int64_t g_end, void* y, int32_t* y_int,
-                 int path, hipStream_t stream) {
-  int dev = -1;
-  wqbmm_status st = check_device(&dev);
-  if (st != WQBMM_OK) return st;
-  if (path == WQBMM_PATH_DECODE)
-    return run_decode(dev, x, w, scale, gs, M, K, N, g_begin, g_end, y, y_int, 0, stream);
-  // prefill: operand preparation into the workspace, then the MFMA GEMM
-  return run_prefill(dev, x, w, scale, gs, M, K, N, g_begin, g_end, y, y_int, 0, stream);
-}
-
-// The prefill path.  stage 0: both kernels; 1: preparation only; 2: GEMM only,
-// on the operands a previous stage 0/1 call left in this stream's workspace
-// for the same shape (checked).
-wqbmm_status run_prefill(int dev, const void* x, const void* w, const void* scale, int64_t gs,
+// The prefill path.  stage 0: both kernels; 1: preparation only; 2: GEMM only.
+wqbmm_status run_prefill(const Buffers& b, const void* x, const void* w, const void* scale, int64_t gs,
                          int64_t M, int64_t K, int64_t N, int64_t g_begin, int64_t g_end, void* y,
                          int32_t* y_int, int stage, hipStream_t stream) {
   const wqbmm::PrefillLayout L = wqbmm::prefill_layout((int)gs, M, K, N);
-  const size_t a_off = 0;
-  const size_t q_off = round_up(L.a_bytes, 256);
-  const size_t b_off = q_off + round_up(L.q_bytes, 256);
-  const size_t total = b_off + round_up(L.b_bytes, 256);
-  uint64_t* accum = nullptr;
-  uint8_t* scratch = nullptr;
-  wqbmm_status st = get_workspace(dev, stream, 0, total, &accum, &scratch);
-  if (st != WQBMM_OK) return st;
-  uint8_t* a_t = scratch + a_off;
-  float* q_t = reinterpret_cast<float*>(scratch + q_off);
-  uint8_t* b_t = scratch + b_off;
-  st = track_operands(dev, stream, WQBMM_PATH_PREFILL, stage, gs, M, K, N);
-  if (st != WQBMM_OK) return st;
+  uint8_t* a_t = b.ops;
+  float* q_t = reinterpret_cast<float*>(b.ops + round_up(L.a_bytes, 256));
+  uint8_t* b_t = b.ops + round_up(L.a_bytes, 256) + round_up(L.q_bytes, 256);
   if (stage != 2) {
-    st = launch_status(wqbmm::launch_prefill_prep(x, w, (int)gs, M, K, N, L, a_t, q_t, b_t, stream));
+    const wqbmm_status st =
+        launch_status(wqbmm::launch_prefill_prep(x, w, (int)gs, M, K, N, L, a_t, q_t, b_t, stream));
     if (st != WQBMM_OK || stage == 1) return st;
   }
   return launch_status(wqbmm::launch_prefill_gemm(a_t, q_t, b_t, w, scale, (int)gs, M, K, N, L,
                                                   g_begin, g_end, y, y_int, stream));
+}
+
+wqbmm_status run_path(const Buffers& b, int path, const void* x, const void* w, const void* scale,
+                      int64_t gs, int64_t M, int64_t K, int64_t N, int64_t g_begin, int64_t g_end,
+                      void* y, int32_t* y_int, int stage, hipStream_t stream) {
+  if (path == WQBMM_PATH_DECODE)
+    return run_decode(b, x, w, scale, gs, M, K, N, g_begin, g_end, y, y_int, stage, stream);
+  return run_prefill(b, x, w, scale, gs, M, K, N, g_begin, g_end, y, y_int, stage, stream);
+}
+
+// Steps 1-11 (or 1-9 with y_int) on one of the two kernel paths, with this
+// stream's workspace.  Stages as in wqbmm_a16w4_msd_profile_stage (0: all).
+wqbmm_status run(const void* x, const void* w, const void* scale, int64_t gs, int64_t M,
+                 int64_t K, int64_t N, int64_t g_begin, int64_t g_end, void* y, int32_t* y_int,
+                 int path, int stage, hipStream_t stream) {
+  int dev = -1;
+  wqbmm_status st = check_device(&dev);
+  if (st != WQBMM_OK) return st;
+  Buffers b;
+  st = get_workspace(dev, stream, needs_of(path, gs, M, K, N, g_begin, g_end, y_int != nullptr), &b);
+  if (st != WQBMM_OK) return st;
+  const bool two_kernels = path == WQBMM_PATH_PREFILL || M > 4;
+  if (two_kernels) {
+    st = track_operands(dev, stream, path, stage, gs, M, K, N);
+    if (st != WQBMM_OK) return st;
+  }
+  return run_path(b, path, x, w, scale, gs, M, K, N, g_begin, g_end, y, y_int, stage, stream);
 }
 
 }  // namespace
@@ -231,6 +279,9 @@ const char* wqbmm_status_string(int status) {
     case WQBMM_ERR_UNSUPPORTED: return "WQBMM_ERR_UNSUPPORTED: group_size not 64/128 or device not gfx950";
     case WQBMM_ERR_LAUNCH: return "WQBMM_ERR_LAUNCH: a HIP call or kernel launch failed";
     case WQBMM_ERR_ALLOC: return "WQBMM_ERR_ALLOC: workspace allocation failed";
+    case WQBMM_ERR_CAPTURE:
+      return "WQBMM_ERR_CAPTURE: the stream's workspace would have to grow while the stream is "
+             "captured into a graph (make one eager call of the largest shape on it first)";
     default: return "WQBMM_ERR_UNKNOWN: not a wqbmm_status value";
   }
 }
@@ -253,24 +304,45 @@ wqbmm_status wqbmm_a16w4_tile_weights(const void* w_nd, int64_t K, int64_t N, vo
   return launch_status(wqbmm::launch_prepack(w_nd, K, N, w_tiled, static_cast<hipStream_t>(stream)));
 }
 
+}  // extern "C"
+
+namespace {
+
+// Host validation shared by the operator entry points, in the order null
+// pointer -> shape -> support.  `scale`/`y` are checked only when the entry
+// point takes them (y_int stands in for y where Y_int is exported).  On
+// success *p_out is the resolved kernel path.
+wqbmm_status validate_call(const void* x, const void* w_tiled, const void* scale, bool takes_scale,
+                           const void* y, int64_t gs, int64_t M, int64_t K, int64_t N, int path,
+                           int* p_out) {
+  // x and y have no elements when M == 0 and may then be NULL
+  if ((!x && M != 0) || !w_tiled || (takes_scale && !scale) || (!y && M != 0))
+    return WQBMM_ERR_NULLPTR;
+  wqbmm_status st = check_shape(gs, M, K, N);
+  if (st != WQBMM_OK) return st;
+  if (!aligned16(x) || !aligned16(w_tiled) || (takes_scale && !aligned16(scale)) || !aligned16(y))
+    return WQBMM_ERR_INVALID;
+  if (path < WQBMM_PATH_AUTO || path > WQBMM_PATH_PREFILL) return WQBMM_ERR_INVALID;
+  const int p = resolve_path(path, M, K, N, gs);
+  if (p == WQBMM_PATH_DECODE && M > kDecodeMaxM) return WQBMM_ERR_INVALID;
+  st = check_support(gs);
+  if (st != WQBMM_OK) return st;
+  *p_out = p;
+  return WQBMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 wqbmm_status wqbmm_a16w4_msd_path(const void* x, const void* w_tiled,
                                   const void* antiquant_scale, int64_t group_size, int64_t M,
                                   int64_t K, int64_t N, void* y, int path, void* stream) {
-  // x and y have no elements when M == 0 and may then be NULL
-  if ((!x && M != 0) || !w_tiled || !antiquant_scale || (!y && M != 0))
-    return WQBMM_ERR_NULLPTR;
-  wqbmm_status st = check_shape(group_size, M, K, N);
-  if (st != WQBMM_OK) return st;
-  if (!aligned16(x) || !aligned16(w_tiled) || !aligned16(antiquant_scale) || !aligned16(y))
-    return WQBMM_ERR_INVALID;
-  if (path < WQBMM_PATH_AUTO || path > WQBMM_PATH_PREFILL) return WQBMM_ERR_INVALID;
-  const int p = resolve_path(path, M, K, N, group_size);
-  if (p == WQBMM_PATH_DECODE && M > kDecodeMaxM) return WQBMM_ERR_INVALID;
-  st = check_support(group_size);
-  if (st != WQBMM_OK) return st;
-  if (M == 0) return WQBMM_OK;
-  return run(x, w_tiled, antiquant_scale, group_size, M, K, N, 0, K / group_size, y,
-             nullptr, p, static_cast<hipStream_t>(stream));
+  int p = 0;
+  const wqbmm_status st = validate_call(x, w_tiled, antiquant_scale, true, y, group_size, M, K, N, path, &p);
+  if (st != WQBMM_OK || M == 0) return st;
+  return run(x, w_tiled, antiquant_scale, group_size, M, K, N, 0, K / group_size, y, nullptr, p, 0,
+             static_cast<hipStream_t>(stream));
 }
 
 wqbmm_status wqbmm_a16w4_msd(const void* x, const void* w_tiled,
@@ -299,18 +371,12 @@ wqbmm_status wqbmm_a16w4_msd_prepass(const void* x, int64_t group_size, int64_t 
 wqbmm_status wqbmm_a16w4_msd_yint(const void* x, const void* w_tiled, int64_t group_size,
                                   int64_t M, int64_t K, int64_t N, int64_t g_begin,
                                   int64_t g_end, int32_t* y_int, int path, void* stream) {
-  if ((!x && M != 0) || !w_tiled || (!y_int && M != 0)) return WQBMM_ERR_NULLPTR;
-  wqbmm_status st = check_shape(group_size, M, K, N);
+  int p = 0;
+  wqbmm_status st = validate_call(x, w_tiled, nullptr, false, y_int, group_size, M, K, N, path, &p);
   if (st != WQBMM_OK) return st;
-  if (!aligned16(x) || !aligned16(w_tiled) || !aligned16(y_int)) return WQBMM_ERR_INVALID;
   if (g_begin < 0 || g_end > K / group_size || g_begin >= g_end) return WQBMM_ERR_INVALID;
-  if (path < WQBMM_PATH_AUTO || path > WQBMM_PATH_PREFILL) return WQBMM_ERR_INVALID;
-  const int p = resolve_path(path, M, K, N, group_size);
-  if (p == WQBMM_PATH_DECODE && M > kDecodeMaxM) return WQBMM_ERR_INVALID;
-  st = check_support(group_size);
-  if (st != WQBMM_OK) return st;
   if (M == 0) return WQBMM_OK;
-  return run(x, w_tiled, nullptr, group_size, M, K, N, g_begin, g_end, nullptr, y_int, p,
+  return run(x, w_tiled, nullptr, group_size, M, K, N, g_begin, g_end, nullptr, y_int, p, 0,
              static_cast<hipStream_t>(stream));
 }
 
@@ -318,28 +384,13 @@ wqbmm_status wqbmm_a16w4_msd_profile_stage(const void* x, const void* w_tiled,
                                            const void* antiquant_scale, int64_t group_size,
                                            int64_t M, int64_t K, int64_t N, void* y, int path,
                                            int stage, void* stream) {
-  if ((!x && M != 0) || !w_tiled || !antiquant_scale || (!y && M != 0))
-    return WQBMM_ERR_NULLPTR;
-  wqbmm_status st = check_shape(group_size, M, K, N);
+  int p = 0;
+  const wqbmm_status st = validate_call(x, w_tiled, antiquant_scale, true, y, group_size, M, K, N, path, &p);
   if (st != WQBMM_OK) return st;
-  if (!aligned16(x) || !aligned16(w_tiled) || !aligned16(antiquant_scale) || !aligned16(y))
-    return WQBMM_ERR_INVALID;
   if (stage < 1 || stage > 2) return WQBMM_ERR_INVALID;
-  if (path < WQBMM_PATH_AUTO || path > WQBMM_PATH_PREFILL) return WQBMM_ERR_INVALID;
-  const int p = resolve_path(path, M, K, N, group_size);
-  if (p == WQBMM_PATH_DECODE && M > kDecodeMaxM) return WQBMM_ERR_INVALID;
-  st = check_support(group_size);
-  if (st != WQBMM_OK) return st;
   if (M == 0) return WQBMM_OK;
-  int dev = -1;
-  st = check_device(&dev);
-  if (st != WQBMM_OK) return st;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (p == WQBMM_PATH_DECODE)
-    return run_decode(dev, x, w_tiled, antiquant_scale, group_size, M, K, N, 0, K / group_size, y,
-                      nullptr, stage, s);
-  return run_prefill(dev, x, w_tiled, antiquant_scale, group_size, M, K, N, 0, K / group_size, y,
-                     nullptr, stage, s);
+  return run(x, w_tiled, antiquant_scale, group_size, M, K, N, 0, K / group_size, y, nullptr, p,
+             stage, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"
