@@ -84,7 +84,8 @@ typedef enum wqbmm_status {
   WQBMM_ERR_UNSUPPORTED = 3, /* group_size not 64/128, or the device is not gfx950 */
   WQBMM_ERR_LAUNCH = 4,      /* a HIP call or kernel launch failed               */
   WQBMM_ERR_ALLOC = 5,       /* workspace allocation failed                      */
-  WQBMM_ERR_CAPTURE = 6      /* the workspace would have to grow during graph capture */
+  WQBMM_ERR_CAPTURE = 6,     /* the workspace would have to grow during graph capture */
+  WQBMM_ERR_TOO_LARGE = 7    /* the shape exceeds wqbmm_a16w4_msd_noalloc's fixed scratch */
 } wqbmm_status;
 
 /* Kernel path selector for the *_path / *_yint entry points. */
@@ -131,6 +132,32 @@ wqbmm_status wqbmm_a16w4_msd_path(const void* x, const void* w_tiled,
                                   const void* antiquant_scale, int64_t group_size,
                                   int64_t M, int64_t K, int64_t N, void* y,
                                   int path, void* stream);
+
+/*
+ * wqbmm_a16w4_msd without any device allocation, for callers that cannot
+ * allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same operation, arguments, rules and
+ * kernels as wqbmm_a16w4_msd, and bit-identical results.  It calls no
+ * hipMalloc, hipFree or other allocating routine: the memory its kernels
+ * pass between them is one fixed 64 MiB array per device, a static device
+ * variable of the library that the device holds from loading until the
+ * process ends (2 MiB of split-K accumulators for M <= 4 with K > 4096, which
+ * allows M * N up to 262144 there; 62 MiB of operands for the two-kernel
+ * paths, enough for M = 4096 at K = N = 4096 with group size 128).  A shape
+ * that needs more returns WQBMM_ERR_TOO_LARGE before any launch.
+ *   - The first call on a device sets the array up (its device address, and a
+ *     kernel on `stream` that zeroes the accumulators); that first call must
+ *     not be made while `stream` is being captured (WQBMM_ERR_CAPTURE).
+ *   - Every call on a device shares that device's array and leaves the last
+ *     call's operands in it: calls that overlap in time on one device race
+ *     and give wrong results.  Order them (one stream, or synchronize in
+ *     between); a graph holding such calls must not replay concurrently with
+ *     other calls of this entry point on the same device.
+ */
+wqbmm_status wqbmm_a16w4_msd_noalloc(const void* x, const void* w_tiled,
+                                     const void* antiquant_scale, int64_t group_size,
+                                     int64_t M, int64_t K, int64_t N, void* y,
+                                     void* stream);
 
 /*
  * Steps 1-8 alone (WQBMM-Exp page §4.1: A_max, tmp1..tmp3, A1..A3, A_int),

@@ -26,7 +26,7 @@ def test_library_exports_every_header_symbol():
 
 
 def test_status_strings_and_version():
-    for s in range(7):
+    for s in range(8):
         assert L.status_string(s).startswith("WQBMM_")
     assert "UNKNOWN" in L.status_string(99)
     assert L.wqbmm_version() >= 10000

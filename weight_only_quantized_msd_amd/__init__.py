@@ -17,13 +17,15 @@ current HIP stream.  PyTorch supplies device memory and streams.
 """
 from __future__ import annotations
 
-from ._lib import (WQBMM_ERR_ALLOC, WQBMM_ERR_INVALID, WQBMM_ERR_LAUNCH,  # noqa: F401
-                   WQBMM_ERR_NULLPTR, WQBMM_ERR_UNSUPPORTED, WQBMM_OK, WQBMM_PATH_AUTO,
+from ._lib import (WQBMM_ERR_ALLOC, WQBMM_ERR_CAPTURE, WQBMM_ERR_INVALID,  # noqa: F401
+                   WQBMM_ERR_LAUNCH, WQBMM_ERR_NULLPTR, WQBMM_ERR_TOO_LARGE,
+                   WQBMM_ERR_UNSUPPORTED, WQBMM_OK, WQBMM_PATH_AUTO,
                    WQBMM_PATH_DECODE, WQBMM_PATH_PREFILL, WqbmmError, check, lib,
                    status_string, wqbmm_select_path, wqbmm_version)
 
 __all__ = [
-    "wqbmm_a16w4_tile_weights", "wqbmm_a16w4_msd", "wqbmm_a16w4_msd_path", "wqbmm_a16w4_msd_prepass",
+    "wqbmm_a16w4_tile_weights", "wqbmm_a16w4_msd", "wqbmm_a16w4_msd_path", "wqbmm_a16w4_msd_noalloc",
+    "wqbmm_a16w4_msd_prepass",
     "wqbmm_a16w4_msd_yint", "wqbmm_a16w4_msd_profile_stage", "wqbmm_select_path", "wqbmm_status_string", "wqbmm_version",
     "WqbmmError",
 ]
@@ -108,6 +110,25 @@ def wqbmm_a16w4_msd(x, w_tiled, antiquant_scale, group_size: int, y=None, stream
     """The operator; returns y (fp16 [M][N]).  Asynchronous on the current stream."""
     return wqbmm_a16w4_msd_path(x, w_tiled, antiquant_scale, group_size,
                                 WQBMM_PATH_AUTO, y=y, stream=stream)
+
+
+def wqbmm_a16w4_msd_noalloc(x, w_tiled, antiquant_scale, group_size: int, y, stream=None):
+    """The operator without any device allocation (one fixed scratch array per
+    device inside the library); y (fp16 [M][N]) is caller-provided and
+    returned.  Calls that overlap in time on one device race."""
+    import torch
+    _require(x, torch.float16, 2, "x")
+    _require(antiquant_scale, torch.float16, 2, "antiquant_scale")
+    _require(y, torch.float16, 2, "y")
+    M, K = x.shape
+    N = _weight_n(w_tiled, K)
+    if antiquant_scale.shape[1] != N or (
+            group_size > 0 and antiquant_scale.shape[0] * group_size != K) or tuple(y.shape) != (M, N):
+        raise ValueError("inconsistent shapes: x [M][K], tiled w for K x N, scale [K/gs][N], y [M][N]")
+    st = lib().wqbmm_a16w4_msd_noalloc(x.data_ptr(), w_tiled.data_ptr(), antiquant_scale.data_ptr(),
+                                       int(group_size), M, K, N, y.data_ptr(), _stream_ptr(stream))
+    check(st, "wqbmm_a16w4_msd_noalloc")
+    return y
 
 
 def wqbmm_a16w4_msd_prepass(x, group_size: int, stream=None):

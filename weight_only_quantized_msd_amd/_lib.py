@@ -21,6 +21,7 @@ WQBMM_ERR_UNSUPPORTED = 3
 WQBMM_ERR_LAUNCH = 4
 WQBMM_ERR_ALLOC = 5
 WQBMM_ERR_CAPTURE = 6
+WQBMM_ERR_TOO_LARGE = 7
 
 WQBMM_PATH_AUTO = 0
 WQBMM_PATH_DECODE = 1
@@ -36,6 +37,7 @@ SIGNATURES = {
     "wqbmm_a16w4_tile_weights": (_int, [_p, _i64, _i64, _p, _p]),
     "wqbmm_a16w4_msd": (_int, [_p, _p, _p, _i64, _i64, _i64, _i64, _p, _p]),
     "wqbmm_a16w4_msd_path": (_int, [_p, _p, _p, _i64, _i64, _i64, _i64, _p, _int, _p]),
+    "wqbmm_a16w4_msd_noalloc": (_int, [_p, _p, _p, _i64, _i64, _i64, _i64, _p, _p]),
     "wqbmm_a16w4_msd_prepass": (_int, [_p, _i64, _i64, _i64, _p, _p, _p]),
     "wqbmm_a16w4_msd_yint": (_int, [_p, _p, _i64, _i64, _i64, _i64, _i64, _i64, _p, _int, _p]),
     "wqbmm_a16w4_msd_profile_stage": (_int, [_p, _p, _p, _i64, _i64, _i64, _i64, _p, _int, _int, _p]),
@@ -101,6 +103,10 @@ def wqbmm_a16w4_msd_raw(x, w, scale, group_size, M, K, N, y, stream) -> int:
 
 def wqbmm_a16w4_msd_path_raw(x, w, scale, group_size, M, K, N, y, path, stream) -> int:
     return lib().wqbmm_a16w4_msd_path(x, w, scale, group_size, M, K, N, y, path, stream)
+
+
+def wqbmm_a16w4_msd_noalloc_raw(x, w, scale, group_size, M, K, N, y, stream) -> int:
+    return lib().wqbmm_a16w4_msd_noalloc(x, w, scale, group_size, M, K, N, y, stream)
 
 
 def wqbmm_a16w4_msd_prepass_raw(x, group_size, M, K, a_int, a_max, stream) -> int:

@@ -46,24 +46,24 @@ wqbmm_status check_support(int64_t gs) {
   return (gs == 64 || gs == 128) ? WQBMM_OK : WQBMM_ERR_UNSUPPORTED;
 }
 
-// ---- device check (gfx950 only), cached per device
+// ---- device check (gfx950 only), cached per device in a fixed table
+constexpr int kMaxDevices = 64;
 std::mutex g_mu;
-std::map<int, bool> g_arch_ok;
+int g_arch[kMaxDevices];   // 0: not checked yet, 1: gfx950, 2: another device
 
 wqbmm_status check_device(int* dev_out) {
   int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess) return WQBMM_ERR_UNSUPPORTED;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return WQBMM_ERR_UNSUPPORTED;
   std::lock_guard<std::mutex> lk(g_mu);
-  auto it = g_arch_ok.find(dev);
-  if (it == g_arch_ok.end()) {
+  if (g_arch[dev] == 0) {
     hipDeviceProp_t prop;
     bool ok = false;
     if (hipGetDeviceProperties(&prop, dev) == hipSuccess)
       ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
-    it = g_arch_ok.emplace(dev, ok).first;
+    g_arch[dev] = ok ? 1 : 2;
   }
   *dev_out = dev;
-  return it->second ? WQBMM_OK : WQBMM_ERR_UNSUPPORTED;
+  return g_arch[dev] == 1 ? WQBMM_OK : WQBMM_ERR_UNSUPPORTED;
 }
 
 // ---- scratch memory of one call
@@ -182,6 +182,50 @@ wqbmm_status get_workspace(int dev, hipStream_t stream, const Needs& need, Buffe
   return WQBMM_OK;
 }
 
+}  // namespace
+
+// ---- scratch of the allocation-free entry point (wqbmm_a16w4_msd_noalloc)
+// One fixed array per device, loaded with the library: the first 2 MiB hold
+// the fused decode kernel's split-K accumulators (zeroed at set-up, left zero
+// by every completed launch), the rest the two-kernel paths' operands.  In
+// host code `scratch` only names the array's host-side stand-in; its device
+// address on the current device comes from hipGetSymbolAddress, once per
+// device, and only that address is passed to kernels.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr size_t kScratchAccBytes = size_t(2) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+uint8_t* g_scratch_ptr[kMaxDevices];   // device address of `scratch` per device (null: not set up)
+
+// The scratch of device `dev`, set up on its first use: the symbol's device
+// address, and a kernel on `stream` that zeroes the accumulator region.  The
+// set-up is refused while `stream` is being captured (the zeroing would exist
+// only inside the graph).  WQBMM_ERR_TOO_LARGE if the call needs more than
+// the array holds.
+wqbmm_status scratch_buffers(int dev, hipStream_t stream, const Needs& need, Buffers* out) {
+  if (need.acc > kScratchAccBytes || need.ops > kScratchBytes - kScratchAccBytes)
+    return WQBMM_ERR_TOO_LARGE;
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (!g_scratch_ptr[dev]) {
+    wqbmm_status st;
+    if (capturing(stream, &st)) return WQBMM_ERR_CAPTURE;
+    if (st != WQBMM_OK) return st;
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return WQBMM_ERR_LAUNCH;
+    if (wqbmm::launch_zero_words(static_cast<uint32_t*>(p), (int64_t)(kScratchAccBytes / 4), stream) !=
+        hipSuccess)
+      return WQBMM_ERR_LAUNCH;
+    g_scratch_ptr[dev] = static_cast<uint8_t*>(p);
+  }
+  out->acc = reinterpret_cast<uint64_t*>(g_scratch_ptr[dev]);
+  out->acc_bytes = kScratchAccBytes;
+  out->ops = g_scratch_ptr[dev] + kScratchAccBytes;
+  out->ops_bytes = kScratchBytes - kScratchAccBytes;
+  return WQBMM_OK;
+}
+
 int resolve_path(int path, int64_t M, int64_t K, int64_t N, int64_t gs) {
   if (path == WQBMM_PATH_AUTO) return wqbmm_select_path(M, K, N, gs);
   return path;
@@ -279,6 +323,9 @@ const char* wqbmm_status_string(int status) {
     case WQBMM_ERR_UNSUPPORTED: return "WQBMM_ERR_UNSUPPORTED: group_size not 64/128 or device not gfx950";
     case WQBMM_ERR_LAUNCH: return "WQBMM_ERR_LAUNCH: a HIP call or kernel launch failed";
     case WQBMM_ERR_ALLOC: return "WQBMM_ERR_ALLOC: workspace allocation failed";
+    case WQBMM_ERR_TOO_LARGE:
+      return "WQBMM_ERR_TOO_LARGE: the shape needs more than the allocation-free entry point's "
+             "fixed scratch (2 MiB of accumulators, 62 MiB of operands)";
     case WQBMM_ERR_CAPTURE:
       return "WQBMM_ERR_CAPTURE: the stream's workspace would have to grow while the stream is "
              "captured into a graph (make one eager call of the largest shape on it first)";
@@ -350,6 +397,24 @@ wqbmm_status wqbmm_a16w4_msd(const void* x, const void* w_tiled,
                              int64_t K, int64_t N, void* y, void* stream) {
   return wqbmm_a16w4_msd_path(x, w_tiled, antiquant_scale, group_size, M, K, N, y,
                               WQBMM_PATH_AUTO, stream);
+}
+
+wqbmm_status wqbmm_a16w4_msd_noalloc(const void* x, const void* w_tiled,
+                                     const void* antiquant_scale, int64_t group_size, int64_t M,
+                                     int64_t K, int64_t N, void* y, void* stream) {
+  int p = 0;
+  wqbmm_status st = validate_call(x, w_tiled, antiquant_scale, true, y, group_size, M, K, N,
+                                  WQBMM_PATH_AUTO, &p);
+  if (st != WQBMM_OK || M == 0) return st;
+  int dev = -1;
+  st = check_device(&dev);
+  if (st != WQBMM_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  Buffers b;
+  st = scratch_buffers(dev, s, needs_of(p, group_size, M, K, N, 0, K / group_size, false), &b);
+  if (st != WQBMM_OK) return st;
+  return run_path(b, p, x, w_tiled, antiquant_scale, group_size, M, K, N, 0, K / group_size, y,
+                  nullptr, 0, s);
 }
 
 wqbmm_status wqbmm_a16w4_msd_prepass(const void* x, int64_t group_size, int64_t M, int64_t K,
