@@ -3,19 +3,27 @@
 
 One step = one call of the whole operator (steps 1-11: decomposition of x,
 integer contraction on MFMA, fp32 combine/accumulate, fp16 store) on one
-synthetic batch that is already resident in HBM, with weights already in the
-library's tiled layout (converted once per weight, outside the timed region).  Steps cycle through enough distinct buffer sets
-(x, w, scale, y) that their footprint exceeds 512 MiB, twice the 256 MiB
-MALL, so every step streams its weights from HBM.  The K timed steps are
-captured once into a HIP graph and replayed, so the GPU runs them back to
-back without Python launch overhead in between; the kernels are the same as
-in an eager call.
+synthetic batch that is already resident in HBM, with the weights already in
+the library's tiled layout (converted once per weight, outside any timed
+region).  Steps cycle through enough distinct buffer sets (x, w, scale, y)
+that their footprint exceeds 512 MiB, twice the 256 MiB MALL, so every step
+streams its weights from HBM.  The K timed steps are captured once into a HIP
+graph; the headline replays it once between synchronizations.  The steps'
+time is taken with HIP events on the launch stream (ms_per_step); the host
+wall clock around the same replay is reported beside it.
 
-Prints ONE JSON line:  metric / value (effective TOPS = 2*M*N*K per step per
-second) / ms_per_step / roofline of the dominant kernel (HIP events on the
-launch stream) / cpu_baseline (the CPU oracle on the host cores).
+The headline workload is prefill_m2048 (M = 2048, K = N = 4096, group size
+128), the largest configuration of the metric's M = 1..2048 range.  Every
+other workload is measured in the same run and nested under "workloads",
+each with its own step time, the roofline of its dominant kernel (timed
+alone, in its own graph over the same rotating buffer sets) and its
+preparation kernel.  The weight-streaming workloads also carry a plain read
+of the same byte count (the achievable-bandwidth reference).
 
-usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+Prints ONE JSON line.
+
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+                       [--workload NAME] [--only] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -24,6 +32,8 @@ import hashlib
 import json
 import math
 import os
+import platform
+import statistics
 import sys
 import time
 
@@ -33,11 +43,14 @@ sys.path.insert(0, ROOT)
 METRIC = "A16W4 MSD matmul effective TOPS + weight GB/s (% roofline) at M=1..2048"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 I8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, published (5.0 POP/s)
-FP6_PEAK_TOPS = 10100.0      # MI355X dense FP6 MFMA, published (10.1 PFLOP/s): the GEMM's own dtype
+FP6_PEAK_TOPS = 10100.0      # MI355X dense FP6 MFMA, published (10.1 PFLOP/s): the GEMMs' own dtype
 # fp32 vector rate in lane-operations: the published 157.3 TFLOP/s counts an FMA
 # as two flops, i.e. 256 CUs x 4 SIMDs x 32 lanes x 2.4 GHz operations per second
 VALU_F32_OPS_PEAK_T = 256 * 4 * 32 * 2.4e9 / 1e12
 MALL_COLD_BYTES = 512 << 20
+HEADLINE = "prefill_m2048"
+NESTED = ["decode_m1", "decode_m16", "ffn_up_m16", "outlier_m128", "pages_sample_m1", "tiny"]
+REPLAYS = 11                 # extra timed replays of the K-step graph for median / p10 / p90
 
 
 def kernel_sources_sha() -> str:
@@ -54,6 +67,40 @@ def algorithmic(M, K, N, gs):
     w_bytes = K * N // 2
     bytes_total = w_bytes + 2 * G * N + 2 * M * K + 2 * M * N   # W + scale + x + y, once each
     return dict(w_bytes=w_bytes, bytes=bytes_total, eff_ops=2 * M * N * K, exec_i8_ops=6 * M * N * K)
+
+
+def kernels_of(path, M, K, N, gs):
+    """The kernels the library launches for this shape and path: (preparation
+    kernel or None, dominant kernel).  Mirrors the dispatch in msd_api.cpp and
+    the launchers (msd_decode.hip, msd_decode_gemv.hip, msd_prefill*.hip)."""
+    if path == 1:
+        if M <= 4:
+            return None, "msd_decode_kernel"
+        return "msd_decode_operands_kernel", "msd_decode_gemv_kernel"
+    if gs == 128:
+        return "msd_prep_kernel", "msd_gemm_kernel"
+    mblocks = -(-M // 128)
+    return "msd_prep64_kernel", ("msd_gemm64w_kernel" if mblocks <= 2 else "msd_gemm64_kernel")
+
+
+def prefill_prep_bytes(M, K, N, gs):
+    """Algorithmic bytes of the prefill preparation kernel: it reads x and
+    writes the level operand tiles (1536 bytes each: 16 rows x 128 k at group
+    size 128, 32 rows x 64 k at group size 64) and the level weights (fp32,
+    three per row and group); unless the GEMM converts the weights itself (group
+    size 64 with at most two 128-row blocks), it also reads the tiled int4
+    weights and writes their operand tiles (columns padded to the GEMM's
+    column block of 256, or 128 when 256 would give fewer than 256 tiles)."""
+    G = K // gs
+    per = 16 if gs == 128 else 32
+    mpad = -(-M // 128) * 128
+    w_in_gemm = gs == 64 and mpad // 128 <= 2
+    bn = 256 if (not w_in_gemm and (mpad // 128) * -(-N // 256) >= 256) else 128
+    npad = -(-N // bn) * bn
+    b = 2 * M * K + 1536 * (3 * mpad // per) * G + 12 * mpad * G
+    if not w_in_gemm:
+        b += K * N // 2 + 1536 * (npad // per) * G
+    return b
 
 
 def make_sets(torch, W, M, K, N, gs, nsets, seed, dist):
@@ -93,81 +140,96 @@ def make_sets(torch, W, M, K, N, gs, nsets, seed, dist):
     return sets
 
 
-def timed_graph(torch, stream, fn_list, steps, warmup):
-    """Eager warmup, capture `steps` calls (cycling fn_list) into one graph,
-    replay once untimed, then time one replay: wall clock between
-    synchronizations, and HIP events on the launch stream."""
-    with torch.cuda.stream(stream):
-        for i in range(warmup):
-            fn_list[i % len(fn_list)]()
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=stream, capture_error_mode="relaxed"):
-        for i in range(steps):
-            fn_list[i % len(fn_list)]()
-    g.replay()
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    with torch.cuda.stream(stream):
-        e0.record(stream)
-        g.replay()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    return (t1 - t0) * 1e3 / steps, e0.elapsed_time(e1) / steps
+class Timed:
+    """`steps` calls (cycling fn_list) captured into one graph on `stream`
+    after `warmup` eager calls.  replay_ms() times one replay with HIP events
+    on that stream (per call), between synchronizations, and also returns the
+    host wall clock of the same replay."""
+
+    def __init__(self, torch, stream, fn_list, steps, warmup):
+        self.torch, self.stream, self.steps = torch, stream, steps
+        with torch.cuda.stream(stream):
+            for i in range(warmup):
+                fn_list[i % len(fn_list)]()
+        torch.cuda.synchronize()
+        self.g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.g, stream=stream, capture_error_mode="relaxed"):
+            for i in range(steps):
+                fn_list[i % len(fn_list)]()
+        self.g.replay()                       # first replay uploads the graph
+        torch.cuda.synchronize()
+
+    def replay_ms(self):
+        torch = self.torch
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        with torch.cuda.stream(self.stream):
+            e0.record(self.stream)
+            self.g.replay()
+            e1.record(self.stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        return e0.elapsed_time(e1) / self.steps, (t1 - t0) * 1e3 / self.steps
+
+    def spread(self, n):
+        v = sorted(self.replay_ms()[0] for _ in range(n))
+        q = lambda p: v[min(len(v) - 1, max(0, int(round(p * (len(v) - 1)))))]
+        return {"replays": n, "p10_ms": round(q(0.1), 6), "median_ms": round(statistics.median(v), 6),
+                "p90_ms": round(q(0.9), 6)}
 
 
-def prefill_prep_bytes(M, K, N, gs):
-    """Algorithmic bytes of the prefill preparation kernel: it reads x and
-    writes the level operand tiles (1536 bytes each: 16 rows x 128 k at group
-    size 128, 32 rows x 64 k at group size 64) and the level weights (fp32,
-    three per row and group); unless the GEMM converts the weights itself (group
-    size 64 with at most two 128-row blocks), it also reads the tiled int4
-    weights and writes their operand tiles (columns padded to the GEMM's
-    column block of 256, or 128 when 256 would give fewer than 256 tiles)."""
-    G = K // gs
-    per = 16 if gs == 128 else 32
-    mpad = -(-M // 128) * 128
-    w_in_gemm = gs == 64 and mpad // 128 <= 2
-    bn = 256 if (not w_in_gemm and (mpad // 128) * -(-N // 256) >= 256) else 128
-    npad = -(-N // bn) * bn
-    b = 2 * M * K + 1536 * (3 * mpad // per) * G + 12 * mpad * G
-    if not w_in_gemm:
-        b += K * N // 2 + 1536 * (npad // per) * G
-    return b
+def host_cpu():
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"model": model, "machine": platform.machine(), "logical_cpus": os.cpu_count(),
+            "usable_cpus": usable}
 
 
 def cpu_baseline(name, M, K, N, gs, seconds):
+    """The CPU oracle (plain C, OpenMP over rows) on a bounded sample of the
+    workload: a prefix of rows, all of K and N; timed at all usable cores and
+    at one thread, about `seconds` each."""
     import numpy as np
     import oracle
     from weight_only_quantized_msd_amd import datagen
     d = datagen.make_inputs(name)
-    # bounded sample: all rows for small M, else a prefix of rows
-    rows = np.arange(M) if M <= 16 else np.arange(min(M, 8))
-    t0 = time.perf_counter()
-    reps = 0
-    while True:
-        oracle.matmul(d["x"], d["w_packed"], d["scale"], gs, rows=rows)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or reps >= 10000:
-            break
-    ops = 2.0 * len(rows) * N * K * reps
-    cpu = "unknown"
-    try:
-        for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                cpu = line.split(":", 1)[1].strip()
+    rows = np.arange(M) if M <= 16 else np.arange(min(M, 16))
+
+    def run(threads):
+        oracle.set_num_threads(threads)
+        used = oracle.num_threads()
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            oracle.matmul(d["x"], d["w_packed"], d["scale"], gs, rows=rows)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds or reps >= 10000:
                 break
-    except OSError:
-        pass
-    return {"value": ops / el / 1e12, "unit": "TOPS", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"{name}: rows {len(rows)} of {M}, all of K={K}, N={N}; {reps} oracle call(s) in {el:.1f} s",
-            "host_cpu": cpu, "seconds": round(el, 2)}
+        return 2.0 * len(rows) * N * K * reps / el / 1e12, used, reps, el
+
+    cpu = host_cpu()
+    v_all, used_all, reps_all, el_all = run(cpu["usable_cpus"])
+    v_one, _, reps_one, el_one = run(1)
+    oracle.set_num_threads(cpu["usable_cpus"])
+    return {"value": v_all, "unit": "TOPS", "cores": used_all, "kind": "oracle",
+            "sample": (f"{name}: rows {len(rows)} of {M}, all of K={K}, N={N}; "
+                       f"{reps_all} oracle call(s) in {el_all:.1f} s at {used_all} threads"),
+            "one_thread": {"value": v_one, "unit": "TOPS", "cores": 1,
+                           "sample": f"same rows; {reps_one} oracle call(s) in {el_one:.1f} s"},
+            "host_cpu": cpu}
 
 
 def read_traffic(workload, sha):
@@ -180,16 +242,176 @@ def read_traffic(workload, sha):
     return t.get("hbm_bytes_per_launch"), t
 
 
+def plain_read(torch, W, nbytes, steps, warmup):
+    """The achievable-bandwidth reference: a plain streaming read of `nbytes`
+    (wqbmm_probe_stream_read), over rotating buffers of >= 512 MiB in all."""
+    from weight_only_quantized_msd_amd import _lib as L
+    nb = -(-nbytes // 16) * 16
+    nbuf = max(2, min(256, math.ceil(MALL_COLD_BYTES / nb)))
+    bufs = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(nbuf)]
+    for b in bufs:
+        b.fill_(1)
+    sink = torch.empty(2048, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.Stream()
+    sp = int(stream.cuda_stream)
+
+    def call(b):
+        def f():
+            rc = L.wqbmm_probe_stream_read_raw(b.data_ptr(), nb, sink.data_ptr(), sp)
+            if rc:
+                raise RuntimeError(f"wqbmm_probe_stream_read: {rc}")
+        return f
+
+    t = Timed(torch, stream, [call(b) for b in bufs], steps, warmup)
+    ms, _ = t.replay_ms()
+    del bufs
+    return {"kernel": "msd_probe_read_kernel", "bytes": nb, "avg_kernel_us": round(ms * 1e3, 3),
+            "GBps": round(nb / (ms * 1e-3) / 1e9, 1), "frac_of_hbm_peak": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+def measure(torch, W, name, args, path_override=0):
+    """Everything about one workload: step time (event and wall clock, spread,
+    warm-cache), each kernel alone, its roofline."""
+    from weight_only_quantized_msd_amd import datagen
+    wl = datagen.WORKLOADS[name]
+    M, K, N, gs = wl.M, wl.K, wl.N, wl.group_size
+    alg = algorithmic(M, K, N, gs)
+    path = path_override or W.wqbmm_select_path(M, K, N, gs)
+    dist = {"x": wl.x_dist, "w": (wl.w_low, wl.w_high), "scale": wl.scale_dist,
+            "outlier_frac": wl.outlier_frac, "outlier_mult": wl.outlier_mult}
+    nsets = max(2, min(256, math.ceil(MALL_COLD_BYTES / alg["bytes"])))
+    sets = make_sets(torch, W, M, K, N, gs, nsets, wl.seed, dist)
+    stream = torch.cuda.Stream()
+    lib = W.lib()
+    sptr = int(stream.cuda_stream)
+    print(f"[bench] {name}: M={M} K={K} N={N} gs={gs} path={path} sets={nsets}", file=sys.stderr, flush=True)
+
+    def call(st):
+        def f():
+            rc = lib.wqbmm_a16w4_msd_path(st["x"].data_ptr(), st["w"].data_ptr(), st["s"].data_ptr(),
+                                          gs, M, K, N, st["y"].data_ptr(), path, sptr)
+            if rc:
+                raise W.WqbmmError(rc, "wqbmm_a16w4_msd_path")
+        return f
+
+    def stage(st, k):
+        def f():
+            rc = lib.wqbmm_a16w4_msd_profile_stage(st["x"].data_ptr(), st["w"].data_ptr(),
+                                                   st["s"].data_ptr(), gs, M, K, N,
+                                                   st["y"].data_ptr(), path, k, sptr)
+            if rc:
+                raise W.WqbmmError(rc, "wqbmm_a16w4_msd_profile_stage")
+        return f
+
+    steps, warmup = args.steps, args.warmup
+    full = Timed(torch, stream, [call(st) for st in sets], steps, warmup)
+    ev_ms, wall_ms = full.replay_ms()
+    spread = full.spread(REPLAYS)
+    del full
+    warm = Timed(torch, stream, [call(sets[0])], steps, warmup)
+    warm_ms, _ = warm.replay_ms()
+    del warm
+
+    prep_name, main_name = kernels_of(path, M, K, N, gs)
+    prep_ms = None
+    if prep_name:
+        t = Timed(torch, stream, [stage(st, 1) for st in sets], steps, warmup)
+        prep_ms, _ = t.replay_ms()
+        del t
+    t = Timed(torch, stream, [stage(st, 2) for st in sets], steps, warmup)
+    kern_ms, _ = t.replay_ms()
+    del t
+
+    G = K // gs
+    sha = kernel_sources_sha()
+    traffic, tinfo = read_traffic(name, sha)
+    extra = {}
+    if path == 1:
+        if M > 4:
+            # contraction kernel: tiled int4 weights, scales, the 16-row level
+            # operands (three int4 levels) and level weights once, y
+            kb = -(-K // 128)
+            kbytes = alg["w_bytes"] + 2 * G * N + 3 * 1024 * kb + 192 * G + 2 * M * N
+            extra["prep"] = {"kernel": prep_name, "avg_kernel_us": round(prep_ms * 1e3, 3),
+                             "algorithmic_bytes_per_launch": 2 * M * K + 3 * 1024 * kb + 192 * G}
+        else:
+            kbytes = alg["bytes"]
+        achieved = kbytes / (kern_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": main_name, "avg_kernel_us": round(kern_ms * 1e3, 3),
+                "algorithmic_bytes_per_launch": kbytes}
+        if not args.no_plain_read:
+            pr = plain_read(torch, W, alg["bytes"], steps, warmup)
+            pr["note"] = "plain streaming read of the workload's algorithmic bytes (W + scale + x + y)"
+            extra["plain_read_reference"] = pr
+            roof["frac_of_plain_read"] = round(pr["avg_kernel_us"] / (kern_ms * 1e3), 4)
+    else:
+        # The GEMM contracts on FP6 (e2m3) MFMAs, so its roofline peak is the
+        # dense FP6 rate; the fraction of the int8 rate is reported beside it.
+        # It is timed alone over the rotating sets with the operand tiles as
+        # the preparation kernel of the same shape left them (MALL-resident,
+        # as in a full step, where the GEMM follows its preparation kernel).
+        achieved = alg["exec_i8_ops"] / (kern_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP6_PEAK_TOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / FP6_PEAK_TOPS, 4), "traffic": traffic,
+                "kernel": main_name, "mfma_dtype": "fp6 e2m3",
+                "avg_kernel_us": round(kern_ms * 1e3, 3),
+                "algorithmic_ops_per_launch": alg["exec_i8_ops"],
+                "frac_of_i8_peak": round(achieved / I8_PEAK_TOPS, 4),
+                "operands": "MALL-resident operand tiles, as the preparation kernel leaves them"}
+        # The GEMMs spend more SIMD time on the fp32 combine of step 10 than on
+        # the MFMA: 4 fp32 operations per (row, column, group) -- three for
+        # the level weights, one for the scale and the running sum.
+        combine_ops = 4 * M * N * G
+        alu = combine_ops / (kern_ms * 1e-3) / 1e12
+        extra["alu_view"] = {"bound": "alu", "ops_per_launch": combine_ops, "achieved": round(alu, 2),
+                             "peak": round(VALU_F32_OPS_PEAK_T, 2), "unit": "T fp32 op/s",
+                             "frac": round(alu / VALU_F32_OPS_PEAK_T, 4)}
+        prep_bytes = prefill_prep_bytes(M, K, N, gs)
+        extra["prep"] = {"kernel": prep_name, "avg_kernel_us": round(prep_ms * 1e3, 3),
+                         "algorithmic_bytes_per_launch": prep_bytes,
+                         "achieved_GBps": round(prep_bytes / (prep_ms * 1e-3) / 1e9, 1)}
+    if isinstance(tinfo, dict):
+        extra["traffic_detail"] = {k: tinfo[k] for k in tinfo if k not in ("kernel_sources_sha", "commands")}
+    elif isinstance(tinfo, str):
+        extra["traffic_detail"] = tinfo
+    t_s = ev_ms * 1e-3
+    res = {
+        "config": {"workload": f"{name}: M={M} K={K} N={N} group_size={gs}", "M": M, "K": K, "N": N,
+                   "group_size": gs, "path": {1: "decode", 2: "prefill"}[path],
+                   "buffer_sets": nsets, "footprint_MiB": round(nsets * alg["bytes"] / 2 ** 20, 1)},
+        "ms_per_step": round(ev_ms, 6),
+        "wall_ms_per_step": round(wall_ms, 6),
+        "step_spread": spread,
+        "warm_cache_ms_per_step": round(warm_ms, 6),
+        "effective_TOPS": round(alg["eff_ops"] / t_s / 1e12, 3),
+        "weight_GBps": round(alg["w_bytes"] / t_s / 1e9, 1),
+        "weight_GBps_frac_of_hbm": round(alg["w_bytes"] / t_s / 1e9 / HBM_PEAK_GBS, 4),
+        "hbm_algorithmic_GBps": round(alg["bytes"] / t_s / 1e9, 1),
+        "exec_i8_TOPS": round(alg["exec_i8_ops"] / t_s / 1e12, 2),
+        "step_frac_of_i8_peak": round(alg["exec_i8_ops"] / t_s / 1e12 / I8_PEAK_TOPS, 4),
+        "roofline": roof,
+    }
+    res.update(extra)
+    del sets
+    torch.cuda.synchronize()
+    return res
+
+
 def main():
     from weight_only_quantized_msd_amd import datagen
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode_m16", choices=sorted(datagen.WORKLOADS))
-    ap.add_argument("--path", type=int, default=0, help="0 auto, 1 decode, 2 prefill")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(datagen.WORKLOADS),
+                    help="the headline workload (default prefill_m2048)")
+    ap.add_argument("--only", action="store_true", help="measure the headline workload alone")
+    ap.add_argument("--path", type=int, default=0, help="0 auto, 1 decode, 2 prefill (headline only)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-plain-read", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -203,20 +425,7 @@ def main():
 
     import torch
     import weight_only_quantized_msd_amd as W
-
-    wl = datagen.WORKLOADS[args.workload]
-    M, K, N, gs = wl.M, wl.K, wl.N, wl.group_size
-    alg = algorithmic(M, K, N, gs)
-    path = args.path or W.wqbmm_select_path(M, K, N, gs)
-    dist = {"x": wl.x_dist, "w": (wl.w_low, wl.w_high), "scale": wl.scale_dist,
-            "outlier_frac": wl.outlier_frac, "outlier_mult": wl.outlier_mult}
-    set_bytes = alg["bytes"]
-    nsets = max(2, min(256, math.ceil(MALL_COLD_BYTES / set_bytes)))
     torch.cuda.init()
-    sets = make_sets(torch, W, M, K, N, gs, nsets, wl.seed, dist)
-    stream = torch.cuda.Stream()
-    lib = W.lib()
-    sptr = int(stream.cuda_stream)
 
     if args.calib_copy_mib:
         src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
@@ -226,115 +435,44 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    def call(st):
-        def f():
-            rc = lib.wqbmm_a16w4_msd_path(st["x"].data_ptr(), st["w"].data_ptr(), st["s"].data_ptr(),
-                                          gs, M, K, N, st["y"].data_ptr(), path, sptr)
-            if rc:
-                raise W.WqbmmError(rc, "wqbmm_a16w4_msd_path")
-        return f
+    head = measure(torch, W, args.workload, args, args.path)
+    nested = {}
+    if not args.only:
+        for name in NESTED + ([HEADLINE] if args.workload != HEADLINE else []):
+            if name != args.workload:
+                nested[name] = measure(torch, W, name, args)
 
-    ms_step, ev_step = timed_graph(torch, stream, [call(st) for st in sets], args.steps, args.warmup)
-    t_s = ms_step * 1e-3
-    value = alg["eff_ops"] / t_s / 1e12
-
-    extra = {}
-    sha = kernel_sources_sha()
-    traffic, tinfo = read_traffic(args.workload, sha)
-
-    # The path's kernels timed alone, each in its own graph over the rotating
-    # sets (MALL-cold): stage 1 = the operand kernel, stage 2 = the
-    # contraction on the operands the last stage 1 left in this stream's
-    # workspace (rotating scale, y and, for the weights, w).  The fused decode
-    # kernel (M <= 4) is stage 2 alone.
-    def stage(st, k):
-        def f():
-            rc = lib.wqbmm_a16w4_msd_profile_stage(st["x"].data_ptr(), st["w"].data_ptr(),
-                                                   st["s"].data_ptr(), gs, M, K, N,
-                                                   st["y"].data_ptr(), path, k, sptr)
-            if rc:
-                raise W.WqbmmError(rc, "wqbmm_a16w4_msd_profile_stage")
-        return f
-
-    G = K // gs
-    two_kernels = path == 2 or M > 4
-    prep_ms = None
-    if two_kernels:
-        _, prep_ms = timed_graph(torch, stream, [stage(st, 1) for st in sets], args.steps, args.warmup)
-    _, kern_ms = timed_graph(torch, stream, [stage(st, 2) for st in sets], args.steps, args.warmup)
-    if path == 1:
-        if M > 4:
-            # contraction kernel: tiled int4 weights, scales, the 16-row level
-            # operands (three int4 levels) and level weights once, y
-            kb = -(-K // 128)
-            kbytes = alg["w_bytes"] + 2 * G * N + 3 * 1024 * kb + 192 * G + 2 * M * N
-            kname = "msd_decode_gemv_kernel"
-            extra["prep"] = {"kernel": "msd_decode_operands_kernel", "avg_kernel_us": round(prep_ms * 1e3, 3),
-                             "algorithmic_bytes_per_launch": 2 * M * K + 3 * 1024 * kb + 192 * G}
-        else:
-            kbytes = alg["bytes"]
-            kname = "msd_decode_kernel"
-        achieved = kbytes / (kern_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": kname, "avg_kernel_us": round(kern_ms * 1e3, 3),
-                "algorithmic_bytes_per_launch": kbytes}
-    else:
-        # The GEMM contracts on FP6 (e2m3) MFMAs, so its roofline peak is the
-        # dense FP6 rate; the fraction of the int8 rate is reported beside it.
-        achieved = alg["exec_i8_ops"] / (kern_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP6_PEAK_TOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / FP6_PEAK_TOPS, 4), "traffic": traffic,
-                "kernel": "msd_gemm_kernel", "mfma_dtype": "fp6 e2m3",
-                "avg_kernel_us": round(kern_ms * 1e3, 3),
-                "algorithmic_ops_per_launch": alg["exec_i8_ops"],
-                "frac_of_i8_peak": round(achieved / I8_PEAK_TOPS, 4)}
-        # The GEMM spends more SIMD time on the fp32 combine of step 10 than on
-        # the MFMA (and the two do not overlap): 4 fp32 operations per (row,
-        # column, group) -- three for the level weights, one for the scale and
-        # the running sum.
-        combine_ops = 4 * M * N * G
-        alu = combine_ops / (kern_ms * 1e-3) / 1e12
-        extra["alu_view"] = {"bound": "alu", "ops_per_launch": combine_ops, "achieved": round(alu, 2),
-                             "peak": round(VALU_F32_OPS_PEAK_T, 2), "unit": "T fp32 op/s",
-                             "frac": round(alu / VALU_F32_OPS_PEAK_T, 4)}
-        prep_bytes = prefill_prep_bytes(M, K, N, gs)
-        extra["prep"] = {"kernel": "msd_prep_kernel", "avg_kernel_us": round(prep_ms * 1e3, 3),
-                         "achieved_GBps": round(prep_bytes / (prep_ms * 1e-3) / 1e9, 1)}
-    if tinfo is not None and not isinstance(tinfo, str):
-        extra["traffic_detail"] = {k: tinfo[k] for k in tinfo if k != "kernel_sources_sha"}
-    elif isinstance(tinfo, str):
-        extra["traffic_detail"] = tinfo
-
+    wl = datagen.WORKLOADS[args.workload]
+    alg = algorithmic(wl.M, wl.K, wl.N, wl.group_size)
     out = {
         "metric": METRIC,
-        "value": round(value, 3),
+        "value": head["effective_TOPS"],
         "unit": "TOPS",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 6),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "i8" if path == 1 else "fp6",
+        "dtype": "i8" if head["config"]["path"] == "decode" else "fp6",
         "data": "synthetic",
-        "config": {"workload": f"{args.workload}: M={M} K={K} N={N} group_size={gs}",
-                   "M": M, "K": K, "N": N, "group_size": gs,
-                   "path": {1: "decode", 2: "prefill"}[path],
-                   "buffer_sets": nsets, "footprint_MiB": round(nsets * set_bytes / 2 ** 20, 1),
-                   "submission": "captured HIP graph of the K steps"},
-        "weight_GBps": round(alg["w_bytes"] / t_s / 1e9, 1),
-        "weight_GBps_frac_of_hbm": round(alg["w_bytes"] / t_s / 1e9 / HBM_PEAK_GBS, 4),
-        "hbm_algorithmic_GBps": round(alg["bytes"] / t_s / 1e9, 1),
-        "exec_i8_TOPS": round(alg["exec_i8_ops"] / t_s / 1e12, 2),
-        "event_ms_per_step": round(ev_step, 6),
-        "roofline": roof,
-        "kernel_sources_sha": sha,
+        "config": dict(head["config"], submission="captured HIP graph of the K steps; ms_per_step from "
+                       "HIP events on the launch stream, wall_ms_per_step from the host clock"),
+        "timing": {"ms_per_step": "HIP events around one replay of the K-step graph, per step",
+                   "wall_ms_per_step": "host clock around the same replay, between synchronizations",
+                   "step_spread": f"per-step time of {REPLAYS} further replays: p10 / median / p90",
+                   "warm_cache_ms_per_step": "K steps on one buffer set (weights MALL-resident), labelled warm"},
+        "kernel_sources_sha": kernel_sources_sha(),
     }
-    out.update(extra)
+    for k, v in head.items():
+        if k not in ("config", "ms_per_step"):
+            out[k] = v
+    out["value"] = round(alg["eff_ops"] / (head["ms_per_step"] * 1e-3) / 1e12, 3)
+    if nested:
+        out["workloads"] = nested
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(args.workload, M, K, N, gs, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(args.workload, wl.M, wl.K, wl.N, wl.group_size, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

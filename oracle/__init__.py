@@ -45,6 +45,8 @@ def _load():
     lib.msd_oracle_matmul.argtypes = [_p, _p, _p, _i64, _i64, _i64, _i64, _p, _i64, _p, _p]
     lib.msd_oracle_num_threads.restype = ctypes.c_int
     lib.msd_oracle_num_threads.argtypes = []
+    lib.msd_oracle_set_num_threads.restype = None
+    lib.msd_oracle_set_num_threads.argtypes = [ctypes.c_int]
     _lib = lib
     return lib
 
@@ -61,6 +63,11 @@ def _check(rc, what):
 
 def num_threads() -> int:
     return int(_load().msd_oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Thread count of later oracle calls (OpenMP)."""
+    _load().msd_oracle_set_num_threads(int(n))
 
 
 def half_to_float(bits: int) -> float:

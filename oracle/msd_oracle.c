@@ -260,3 +260,11 @@ int msd_oracle_num_threads(void) {
     return 1;
 #endif
 }
+
+void msd_oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

@@ -56,6 +56,10 @@ int msd_oracle_matmul(const uint16_t* x, const uint8_t* w_packed,
  * without OpenMP). */
 int msd_oracle_num_threads(void);
 
+/* Sets the number of OpenMP threads for later calls (n > 0; ignored without
+ * OpenMP).  Used to time the oracle at one thread and at all cores. */
+void msd_oracle_set_num_threads(int n);
+
 #ifdef __cplusplus
 }
 #endif

@@ -12,7 +12,8 @@ import re
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libwqbmm.so")
-HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "wqbmm.h")
+INCLUDE_DIR = os.path.join(os.path.dirname(_HERE), "include")
+HEADER_PATH = os.path.join(INCLUDE_DIR, "wqbmm.h")
 
 WQBMM_OK = 0
 WQBMM_ERR_NULLPTR = 1
@@ -44,6 +45,8 @@ SIGNATURES = {
     "wqbmm_select_path": (_int, [_i64, _i64, _i64, _i64]),
     "wqbmm_status_string": (ctypes.c_char_p, [_int]),
     "wqbmm_version": (_int, []),
+    # include/wqbmm_probe.h (measurement helper)
+    "wqbmm_probe_stream_read": (_int, [_p, _i64, _p, _p]),
 }
 
 _lib = None
@@ -72,10 +75,14 @@ def lib():
 
 
 def header_functions() -> list[str]:
-    """Names of the functions include/wqbmm.h declares."""
-    text = open(HEADER_PATH).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(wqbmm_\w+)\s*\(", text)))
+    """Names of the functions the headers in include/ declare."""
+    names = set()
+    for h in sorted(os.listdir(INCLUDE_DIR)):
+        if h.endswith(".h"):
+            text = open(os.path.join(INCLUDE_DIR, h)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(wqbmm_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def status_string(status: int) -> str:
@@ -119,6 +126,10 @@ def wqbmm_a16w4_msd_yint_raw(x, w, group_size, M, K, N, g_begin, g_end, y_int, p
 
 def wqbmm_a16w4_msd_profile_stage_raw(x, w, scale, group_size, M, K, N, y, path, stage, stream) -> int:
     return lib().wqbmm_a16w4_msd_profile_stage(x, w, scale, group_size, M, K, N, y, path, stage, stream)
+
+
+def wqbmm_probe_stream_read_raw(src, nbytes, sink, stream) -> int:
+    return lib().wqbmm_probe_stream_read(src, nbytes, sink, stream)
 
 
 def wqbmm_select_path(M, K, N, group_size) -> int:

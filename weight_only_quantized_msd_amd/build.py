@@ -16,7 +16,7 @@ CSRC = os.path.join(_HERE, "csrc")
 BUILD_DIR = os.path.join(_HERE, "_build")
 LIB_PATH = os.path.join(_HERE, "libwqbmm.so")
 SOURCES = ["msd_api.cpp", "msd_prepack.hip", "msd_prepass.hip", "msd_prefill.hip", "msd_prefill64.hip",
-           "msd_decode.hip", "msd_decode_gemv.hip"]
+           "msd_decode.hip", "msd_decode_gemv.hip", "msd_probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CFLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -1,0 +1,58 @@
+// msd_probe.hip -- measurement helper, not part of the operator: a plain
+// streaming read of a byte range, the achievable-bandwidth reference that the
+// weight-streaming (decode) kernels are compared with.  It reads every byte
+// once with 16-byte nontemporal loads (the loads the decode kernels use for
+// their weights), four in flight per lane, and stores one XOR per workgroup
+// so that the loads cannot be dropped.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/wqbmm_probe.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(kThreads) void msd_probe_read_kernel(const u32x4* __restrict__ src,
+                                                                  int64_t chunks,
+                                                                  uint32_t* __restrict__ sink) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  uint32_t h = 0;
+  for (; i + (kUnroll - 1) * stride < chunks; i += kUnroll * stride) {
+    u32x4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) h ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < chunks; i += stride) {
+    const u32x4 v = __builtin_nontemporal_load(src + i);
+    h ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  __shared__ uint32_t red[kThreads];
+  red[threadIdx.x] = h;
+  __syncthreads();
+  for (int s = kThreads / 2; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s) red[threadIdx.x] ^= red[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) sink[blockIdx.x] = red[0];
+}
+
+}  // namespace
+
+extern "C" int wqbmm_probe_stream_read(const void* src, int64_t bytes, void* sink, void* stream) {
+  if (!src || !sink) return 1;
+  if (bytes <= 0 || bytes % 16 != 0 || (reinterpret_cast<uintptr_t>(src) & 15u) != 0) return 2;
+  const int64_t chunks = bytes / 16;
+  int64_t grid = (chunks + (int64_t)kThreads * kUnroll - 1) / ((int64_t)kThreads * kUnroll);
+  if (grid > WQBMM_PROBE_SINK_WORDS) grid = WQBMM_PROBE_SINK_WORDS;
+  hipLaunchKernelGGL(msd_probe_read_kernel, dim3((unsigned)grid), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const u32x4*>(src), chunks,
+                     static_cast<uint32_t*>(sink));
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
