@@ -16,13 +16,15 @@
 extern "C" {
 #endif
 
-/* Workgroups of the read kernel at most, and so the uint32 words of `sink`. */
-#define WQBMM_PROBE_SINK_WORDS 2048
+/* Workgroups of the read kernel at most (it loops over larger ranges). */
+#define WQBMM_PROBE_MAX_GRID 2048
 
 /*
- * Reads `bytes` bytes at `src` once, with 16-byte nontemporal loads, and
- * stores one XOR of the words read per workgroup into `sink` (uint32
- * [WQBMM_PROBE_SINK_WORDS], device memory; only the first words are written).
+ * Reads `bytes` bytes at `src` once, with 16-byte nontemporal loads.  Each
+ * lane folds its words by XOR and stores the result to `sink` (one uint32 of
+ * device memory) only if it equals 0x9E3779B9, which keeps the loads alive;
+ * with data whose words cancel (e.g. a byte pattern repeated over aligned
+ * 64-byte runs, such as a constant fill) nothing is written.
  * src: device memory, 16-byte aligned; bytes > 0 and a multiple of 16.
  * Asynchronous on `stream` (a hipStream_t; NULL = the legacy default stream).
  * Returns 0 on success, 1 if a pointer is NULL, 2 if `bytes` or the alignment

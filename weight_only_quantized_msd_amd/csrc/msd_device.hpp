@@ -15,6 +15,7 @@
 namespace wqbmm {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 // Expansion factors (WQBMM-Exp page §4.1, fp32 as the page's kernel keeps them).
 constexpr float kF1 = 7.49f;
@@ -53,56 +54,86 @@ __device__ __forceinline__ float msd_div(float t, float d, float y) {
   return __builtin_fmaf(__builtin_fmaf(-q0, d, t), y, q0);
 }
 
-// WQBMM-Exp page §4.1 steps 2-7 for one element of a group whose maximum
-// |x| is amax > 0 (rcp = msd_recip(amax)): tmp1 = 7.49*a/A_max, A1 =
-// round(tmp1), tmp2 = (tmp1-A1)*14.98, A2 = round(tmp2), tmp3 =
-// (tmp2-A2)*14.98, A3 = round(tmp3).  Every operation is one IEEE fp32
-// rounding in this order (no contraction; the division is correctly
-// rounded, see msd_div), round is half-to-even (v_rndne_f32).  |A_l| <= 7
-// follows from 7.49 < 7.5 and |residual| <= 0.5.  msd_expand_f returns the
-// levels as (integral) floats, msd_expand as ints.
-__device__ __forceinline__ void msd_expand_f(float a, float amax, float rcp, float& r1, float& r2,
-                                             float& r3) {
-#pragma clang fp contract(off)
-  const float t1 = msd_div(kF1 * a, amax, rcp);
-  r1 = __builtin_rintf(t1);
-  const float t2 = (t1 - r1) * kF2;
-  r2 = __builtin_rintf(t2);
-  const float t3 = (t2 - r2) * kF2;
-  r3 = __builtin_rintf(t3);
-}
-
-__device__ __forceinline__ void msd_expand(float a, float amax, float rcp, int& A1, int& A2, int& A3) {
-  float r1, r2, r3;
-  msd_expand_f(a, amax, rcp, r1, r2, r3);
-  A1 = (int)r1;
-  A2 = (int)r2;
-  A3 = (int)r3;
-}
-
-// Maximum over WIDTH (4, 8 or 16) consecutive, aligned lanes, with DPP lane
-// permutations (no LDS traffic): exchange within quads (xor 1, xor 2), then
-// mirror within each half-row of 8 lanes, then within each row of 16.  max is
-// exact, so the order does not matter.  Every lane of the wave must call it.
-template <int WIDTH>
-__device__ __forceinline__ float group_max(float v) {
-  static_assert(WIDTH == 4 || WIDTH == 8 || WIDTH == 16, "group of 4, 8 or 16 lanes");
-  auto dpp = [](float x, auto ctrl) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), decltype(ctrl)::value, 0xf, 0xf, false));
-  };
-  v = fmaxf(v, dpp(v, std::integral_constant<int, 0xB1>{}));   // quad_perm [1,0,3,2]: lane ^ 1
-  v = fmaxf(v, dpp(v, std::integral_constant<int, 0x4E>{}));   // quad_perm [2,3,0,1]: lane ^ 2
-  if constexpr (WIDTH >= 8) v = fmaxf(v, dpp(v, std::integral_constant<int, 0x141>{}));  // row_half_mirror
-  if constexpr (WIDTH == 16) v = fmaxf(v, dpp(v, std::integral_constant<int, 0x140>{}));  // row_mirror
-  return v;
-}
-
 // Round half to even of |t| < 2^22 with the 1.5*2^23 trick: u = t + kMagic
 // lands where the float spacing is 1, so the (round-to-nearest-even) sum
 // holds rint(t) in its low mantissa bits -- its low byte is rint(t) as a
 // two's-complement int8 -- and u - kMagic is rint(t) exactly (kMagic is even,
 // so ties go to the even integer as with rintf).
 constexpr float kMagic = 12582912.0f;
+
+// ---- WQBMM-Exp page §4.1 steps 1-8: the one decomposition every kernel uses
+//
+// Step 1 (A_max = rowMax(|A_group|)) is exact: the maximum is taken over the
+// fp16 magnitudes' bit patterns as unsigned integers (for non-negative finite
+// values the order of the patterns is the order of the values, and an integer
+// max needs no NaN handling) and widened once.  A kernel takes the maximum of
+// its lane-local elements with chunk_max_bits, reduces it over the lanes that
+// share the group (group_max_bits, or a shuffle), and forms the divisor's
+// reciprocal with msd_group_scale.  Steps 2-7 then run per element in
+// msd_levels.  A zero group (A_max = 0, so every element is +-0) takes a zero
+// reciprocal, which makes every quotient 0 and so every level 0, as the
+// definition's guard requires.
+
+// Largest fp16 magnitude bit pattern among the 8 values of a 16-byte chunk.
+__device__ __forceinline__ uint32_t chunk_max_bits(const uint4 xv) {
+  const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+  const u16x2 m01 = __builtin_elementwise_max(__builtin_bit_cast(u16x2, xw[0] & 0x7fff7fffu),
+                                              __builtin_bit_cast(u16x2, xw[1] & 0x7fff7fffu));
+  const u16x2 m23 = __builtin_elementwise_max(__builtin_bit_cast(u16x2, xw[2] & 0x7fff7fffu),
+                                              __builtin_bit_cast(u16x2, xw[3] & 0x7fff7fffu));
+  const u16x2 mh = __builtin_elementwise_max(m01, m23);
+  return max((uint32_t)mh.x, (uint32_t)mh.y);
+}
+
+// A_max (exact) and the refined reciprocal of step 2's divisor, from the
+// group's largest magnitude bit pattern; rcp = 0 for a zero group.
+__device__ __forceinline__ void msd_group_scale(uint32_t max_bits, float& amax, float& rcp) {
+  amax = half_bits_to_float(max_bits);
+  rcp = amax > 0.0f ? msd_recip(amax) : 0.0f;
+}
+
+// Steps 2-7 for one element (fp16 bit pattern h) of a group with maximum amax
+// and reciprocal rcp: tmp1 = 7.49*a/A_max, A1 = round(tmp1), tmp2 =
+// (tmp1-A1)*14.98, A2 = round(tmp2), tmp3 = (tmp2-A2)*14.98, A3 =
+// round(tmp3).  Every operation is one IEEE fp32 rounding in this order (no
+// contraction; tmp = 7.49*a is one fused multiply-add with a zero addend
+// straight from the fp16 value: exact widening, one rounding of the product;
+// the division is correctly rounded, see msd_div); round is half to even,
+// done by the kMagic sum.  Out: the sums u_l = A_l + kMagic (their low byte
+// is A_l as int8) and the levels r_l = A_l as floats (a kernel uses either).
+// |A_l| <= 7 follows from 7.49 < 7.5 and |residual| <= 0.5.
+__device__ __forceinline__ void msd_levels(uint32_t h, float amax, float rcp, float (&u)[3],
+                                           float (&r)[3]) {
+#pragma clang fp contract(off)
+  const _Float16 a = __builtin_bit_cast(_Float16, (uint16_t)h);
+  const float t1 = msd_div(__builtin_fmaf((float)a, kF1, 0.0f), amax, rcp);
+  u[0] = t1 + kMagic;
+  r[0] = u[0] - kMagic;
+  const float t2 = (t1 - r[0]) * kF2;
+  u[1] = t2 + kMagic;
+  r[1] = u[1] - kMagic;
+  const float t3 = (t2 - r[1]) * kF2;
+  u[2] = t3 + kMagic;
+  r[2] = u[2] - kMagic;
+}
+
+// Maximum over WIDTH (4, 8 or 16) consecutive, aligned lanes of non-negative
+// float bit patterns, as unsigned integers, with DPP lane permutations (no
+// LDS traffic): exchange within quads (xor 1, xor 2), then mirror within each
+// half-row of 8 lanes, then within each row of 16.  max is exact, so the
+// order does not matter.  Every lane of the wave must call it.
+template <int WIDTH>
+__device__ __forceinline__ uint32_t group_max_bits(uint32_t v) {
+  static_assert(WIDTH == 4 || WIDTH == 8 || WIDTH == 16, "group of 4, 8 or 16 lanes");
+  auto dpp = [](uint32_t x, auto ctrl) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, decltype(ctrl)::value, 0xf, 0xf, false);
+  };
+  v = max(v, dpp(v, std::integral_constant<int, 0xB1>{}));    // lane ^ 1
+  v = max(v, dpp(v, std::integral_constant<int, 0x4E>{}));    // lane ^ 2
+  if constexpr (WIDTH >= 8) v = max(v, dpp(v, std::integral_constant<int, 0x141>{}));   // row_half_mirror
+  if constexpr (WIDTH == 16) v = max(v, dpp(v, std::integral_constant<int, 0x140>{}));  // row_mirror
+  return v;
+}
 
 // Low bytes of four dwords -> one dword (byte j from x_j): three v_perm_b32
 // (selector 0x0c gives a zero byte).
@@ -112,62 +143,23 @@ __device__ __forceinline__ uint32_t pack_low_bytes(uint32_t x0, uint32_t x1, uin
   return __builtin_amdgcn_perm(p23, p01, 0x05040100u);               // x0.b0 x1.b0 x2.b0 x3.b0
 }
 
-// Maximum over WIDTH (8 or 16) consecutive, aligned lanes of non-negative
-// float bit patterns, as unsigned integers (for non-negative finite floats the
-// order of the bit patterns is the order of the values, and an integer max
-// needs no NaN canonicalisation): DPP exchanges as in group_max.
-template <int WIDTH>
-__device__ __forceinline__ uint32_t group_max_bits(uint32_t v) {
-  static_assert(WIDTH == 8 || WIDTH == 16, "group of 8 or 16 lanes");
-  auto dpp = [](uint32_t x, auto ctrl) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, decltype(ctrl)::value, 0xf, 0xf, false);
-  };
-  v = max(v, dpp(v, std::integral_constant<int, 0xB1>{}));    // lane ^ 1
-  v = max(v, dpp(v, std::integral_constant<int, 0x4E>{}));    // lane ^ 2
-  v = max(v, dpp(v, std::integral_constant<int, 0x141>{}));   // row_half_mirror
-  if constexpr (WIDTH == 16) v = max(v, dpp(v, std::integral_constant<int, 0x140>{}));  // row_mirror
-  return v;
-}
-
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-
-// Steps 1-8 for 8 consecutive elements of one row (one 16-byte fp16 chunk).
-// The group's GS elements are held by GS/8 consecutive, aligned lanes; every
-// lane of the wave must call this (the max is a cross-lane reduction).
-// Out: the 8 levels of each of A1..A3 packed as int8 bytes in two dwords each,
-// and the group's A_max (step 1: rowMax(|A_group|), exact: the maximum is
-// taken over the fp16 magnitudes' bit patterns and widened once).  The
-// arithmetic is msd_expand_f's, with each rint done by the kMagic sum;
-// tmp = 7.49*a is one fused multiply-add with a zero addend straight from
-// the fp16 value (v_fma_mix_f32: exact widening, one rounding of the
-// product).  A zero group (A_max = 0, so every a is +-0) takes a zero
-// reciprocal, which makes every quotient 0 and every level 0, as the guard
-// of the definition requires.
+// Steps 1-8 for 8 consecutive elements of one row (one 16-byte fp16 chunk)
+// whose group's GS elements are held by GS/8 consecutive, aligned lanes;
+// every lane of the wave must call this (the max is a cross-lane reduction).
+// Out: the 8 levels of each of A1..A3 packed as int8 bytes in two dwords
+// each, and the group's A_max.
 template <int GS>
 __device__ __forceinline__ void msd_decompose8(const uint4 xv, uint32_t (&lv)[3][2], float& amax) {
   const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
-  const u16x2 m01 = __builtin_elementwise_max(__builtin_bit_cast(u16x2, xw[0] & 0x7fff7fffu),
-                                              __builtin_bit_cast(u16x2, xw[1] & 0x7fff7fffu));
-  const u16x2 m23 = __builtin_elementwise_max(__builtin_bit_cast(u16x2, xw[2] & 0x7fff7fffu),
-                                              __builtin_bit_cast(u16x2, xw[3] & 0x7fff7fffu));
-  const u16x2 mh = __builtin_elementwise_max(m01, m23);
-  const uint32_t mb = group_max_bits<GS / 8>(max((uint32_t)mh.x, (uint32_t)mh.y));
-  amax = half_bits_to_float(mb);
-  const float rcp = amax > 0.0f ? msd_recip(amax) : 0.0f;
+  float rcp;
+  msd_group_scale(group_max_bits<GS / 8>(chunk_max_bits(xv)), amax, rcp);
   uint32_t u[3][8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-#pragma clang fp contract(off)
-    const _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)(i & 1 ? xw[i >> 1] >> 16 : xw[i >> 1] & 0xffffu));
-    const float t1 = msd_div(__builtin_fmaf((float)h, kF1, 0.0f), amax, rcp);
-    const float u1 = t1 + kMagic;
-    const float t2 = (t1 - (u1 - kMagic)) * kF2;
-    const float u2 = t2 + kMagic;
-    const float t3 = (t2 - (u2 - kMagic)) * kF2;
-    const float u3 = t3 + kMagic;
-    u[0][i] = __float_as_uint(u1);
-    u[1][i] = __float_as_uint(u2);
-    u[2][i] = __float_as_uint(u3);
+    float uf[3], rf[3];
+    msd_levels(i & 1 ? xw[i >> 1] >> 16 : xw[i >> 1] & 0xffffu, amax, rcp, uf, rf);
+#pragma unroll
+    for (int l = 0; l < 3; ++l) u[l][i] = __float_as_uint(uf[l]);
   }
 #pragma unroll
   for (int l = 0; l < 3; ++l) {

@@ -161,36 +161,29 @@ __global__ __launch_bounds__(256) void msd_prep_kernel(const uint16_t* __restric
       const int m = (2 * mtp + p) * 16 + r;
       const bool real = m < M;                       // padding rows decompose zeros
       const uint16_t* src = x + (real ? (int64_t)m * K + (int64_t)g * GS + 16 * kq : 0);
-      float a[32];
+      uint4 xv[4];
+      uint32_t mb = 0;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         // c = 0, 1: u (k = 16kq + 8c ..); c = 2, 3: v (k = 64 + 16kq + 8(c-2) ..)
         const uint4 v = *reinterpret_cast<const uint4*>(src + (c < 2 ? 8 * c : 64 + 8 * (c - 2)));
-        const uint32_t vw[4] = {real ? v.x : 0u, real ? v.y : 0u, real ? v.z : 0u, real ? v.w : 0u};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          a[8 * c + 2 * i] = half_bits_to_float(vw[i] & 0xffffu);
-          a[8 * c + 2 * i + 1] = half_bits_to_float(vw[i] >> 16);
-        }
+        xv[c] = real ? v : make_uint4(0u, 0u, 0u, 0u);
+        mb = max(mb, chunk_max_bits(xv[c]));
       }
-      float mx = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 32; ++e) mx = fmaxf(mx, fabsf(a[e]));
-      const float amax = group_max<4>(mx);
+      // steps 1-8 (msd_device.hpp): the group is the 4 lanes of this row
+      float amax, rcp;
+      msd_group_scale(group_max_bits<4>(mb), amax, rcp);
       v16f lv[3][2];
 #pragma unroll
-      for (int l = 0; l < 3; ++l)
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t vw[4] = {xv[c].x, xv[c].y, xv[c].z, xv[c].w};
 #pragma unroll
-        for (int e = 0; e < 16; ++e) lv[l][0][e] = lv[l][1][e] = 0.0f;
-      if (amax > 0.0f) {
-        const float rcp = msd_recip(amax);
+        for (int j = 0; j < 8; ++j) {
+          const int e = 8 * c + j;
+          float u[3], rl[3];
+          msd_levels(j & 1 ? vw[j >> 1] >> 16 : vw[j >> 1] & 0xffffu, amax, rcp, u, rl);
 #pragma unroll
-        for (int e = 0; e < 32; ++e) {
-          float r1, r2, r3;
-          msd_expand_f(a[e], amax, rcp, r1, r2, r3);
-          lv[0][e / 16][e % 16] = r1;
-          lv[1][e / 16][e % 16] = r2;
-          lv[2][e / 16][e % 16] = r3;
+          for (int l = 0; l < 3; ++l) lv[l][e / 16][e % 16] = rl[l];
         }
       }
       // dwords 0-3 of this row tile's operands now; dwords 4-5 of the pair's

@@ -161,31 +161,28 @@ __global__ __launch_bounds__(256) void msd_prep64_kernel(const uint16_t* __restr
     const int m = mt * 32 + (lane & 31);
     const bool real = m < M;
     const uint16_t* src = x + (real ? (int64_t)m * K + (int64_t)g * 64 + 32 * h : 0);
-    float a[32];
+    uint4 xv[4];
+    uint32_t mb = 0;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (real) v = *reinterpret_cast<const uint4*>(src + 8 * c);
-      const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        a[8 * c + 2 * i] = half_bits_to_float(vw[i] & 0xffffu);
-        a[8 * c + 2 * i + 1] = half_bits_to_float(vw[i] >> 16);
-      }
+      xv[c] = make_uint4(0u, 0u, 0u, 0u);
+      if (real) xv[c] = *reinterpret_cast<const uint4*>(src + 8 * c);
+      mb = max(mb, chunk_max_bits(xv[c]));
     }
-    float mx = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 32; ++e) mx = fmaxf(mx, fabsf(a[e]));
-    const float amax = fmaxf(mx, __shfl_xor(mx, 32));   // exact: max of the two halves
+    // steps 1-8 (msd_device.hpp): the group is lanes l and l^32
+    float amax, rcp;
+    msd_group_scale(max(mb, (uint32_t)__shfl_xor((int)mb, 32)), amax, rcp);
     float lv[3][32];
 #pragma unroll
-    for (int l = 0; l < 3; ++l)
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t vw[4] = {xv[c].x, xv[c].y, xv[c].z, xv[c].w};
 #pragma unroll
-      for (int e = 0; e < 32; ++e) lv[l][e] = 0.0f;
-    if (amax > 0.0f) {
-      const float rcp = msd_recip(amax);
+      for (int j = 0; j < 8; ++j) {
+        float u[3], rl[3];
+        msd_levels(j & 1 ? vw[j >> 1] >> 16 : vw[j >> 1] & 0xffffu, amax, rcp, u, rl);
 #pragma unroll
-      for (int e = 0; e < 32; ++e) msd_expand_f(a[e], amax, rcp, lv[0][e], lv[1][e], lv[2][e]);
+        for (int l = 0; l < 3; ++l) lv[l][8 * c + j] = rl[l];
+      }
     }
     const int rb = mt / RT, rt = mt % RT;
 #pragma unroll

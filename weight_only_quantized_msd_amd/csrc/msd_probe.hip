@@ -2,8 +2,10 @@
 // streaming read of a byte range, the achievable-bandwidth reference that the
 // weight-streaming (decode) kernels are compared with.  It reads every byte
 // once with 16-byte nontemporal loads (the loads the decode kernels use for
-// their weights), four in flight per lane, and stores one XOR per workgroup
-// so that the loads cannot be dropped.
+// their weights): a wave's load covers 1 KB, four loads in flight per lane.
+// Each lane folds what it read into one word and stores it only if it equals
+// a value the caller's data never produces, so the loads cannot be dropped
+// and the kernel writes nothing in practice.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -33,14 +35,7 @@ __global__ __launch_bounds__(kThreads) void msd_probe_read_kernel(const u32x4* _
     const u32x4 v = __builtin_nontemporal_load(src + i);
     h ^= v.x ^ v.y ^ v.z ^ v.w;
   }
-  __shared__ uint32_t red[kThreads];
-  red[threadIdx.x] = h;
-  __syncthreads();
-  for (int s = kThreads / 2; s > 0; s >>= 1) {
-    if ((int)threadIdx.x < s) red[threadIdx.x] ^= red[threadIdx.x + s];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) sink[blockIdx.x] = red[0];
+  if (h == 0x9E3779B9u) sink[0] = h;
 }
 
 }  // namespace
@@ -50,7 +45,7 @@ extern "C" int wqbmm_probe_stream_read(const void* src, int64_t bytes, void* sin
   if (bytes <= 0 || bytes % 16 != 0 || (reinterpret_cast<uintptr_t>(src) & 15u) != 0) return 2;
   const int64_t chunks = bytes / 16;
   int64_t grid = (chunks + (int64_t)kThreads * kUnroll - 1) / ((int64_t)kThreads * kUnroll);
-  if (grid > WQBMM_PROBE_SINK_WORDS) grid = WQBMM_PROBE_SINK_WORDS;
+  if (grid > WQBMM_PROBE_MAX_GRID) grid = WQBMM_PROBE_MAX_GRID;
   hipLaunchKernelGGL(msd_probe_read_kernel, dim3((unsigned)grid), dim3(kThreads), 0,
                      static_cast<hipStream_t>(stream), static_cast<const u32x4*>(src), chunks,
                      static_cast<uint32_t*>(sink));
