@@ -49,7 +49,8 @@ FP6_PEAK_TOPS = 10100.0      # MI355X dense FP6 MFMA, published (10.1 PFLOP/s): 
 VALU_F32_OPS_PEAK_T = 256 * 4 * 32 * 2.4e9 / 1e12
 MALL_COLD_BYTES = 512 << 20
 HEADLINE = "prefill_m2048"
-NESTED = ["decode_m1", "decode_m16", "ffn_up_m16", "outlier_m128", "pages_sample_m1", "tiny"]
+NESTED = ["decode_m1", "decode_m16", "ffn_up_m16", "mid_m64", "mid_m256", "outlier_m128",
+          "pages_sample_m1", "tiny"]
 REPLAYS = 11                 # extra timed replays of the K-step graph for median / p10 / p90
 
 
@@ -406,6 +407,74 @@ def measure(torch, W, name, args, path_override=0):
     return res
 
 
+SWEEP_M = [8, 12, 16, 24, 32, 48, 64, 96, 128]
+SWEEP_SHAPES = [("K4096_N4096_g128", 4096, 4096, 128), ("K8192_N28672_g64", 8192, 28672, 64)]
+
+
+def sweep(torch, W, args):
+    """Decode-vs-prefill split: the step time of each kernel path at
+    M = 8..128 on the decode shape (K = N = 4096, group size 128) and the
+    outlier shape (K = 8192, N = 28672, group size 64), MALL-cold as above,
+    with each path's kernels timed alone.  Returns a list of rows."""
+    from weight_only_quantized_msd_amd import datagen  # noqa: F401
+    rows = []
+    lib = W.lib()
+    for label, K, N, gs in SWEEP_SHAPES:
+        for M in SWEEP_M:
+            alg = algorithmic(M, K, N, gs)
+            nsets = max(2, min(64, math.ceil(MALL_COLD_BYTES / alg["bytes"])))
+            dist = {"x": "normal", "w": (-8, 7), "scale": ("uniform", 0.005, 0.02)}
+            sets = make_sets(torch, W, M, K, N, gs, nsets, 7, dist)
+            stream = torch.cuda.Stream()
+            sptr = int(stream.cuda_stream)
+            for path in (1, 2):
+                st0 = sets[0]
+                rc = lib.wqbmm_a16w4_msd_path(st0["x"].data_ptr(), st0["w"].data_ptr(), st0["s"].data_ptr(),
+                                              gs, M, K, N, st0["y"].data_ptr(), path, sptr)
+                if rc == W.WQBMM_ERR_INVALID:      # the decode path's row limit
+                    continue
+                if rc:
+                    raise W.WqbmmError(rc, "sweep")
+                def call(st, k=0):
+                    def f():
+                        if k == 0:
+                            rc = lib.wqbmm_a16w4_msd_path(st["x"].data_ptr(), st["w"].data_ptr(),
+                                                          st["s"].data_ptr(), gs, M, K, N,
+                                                          st["y"].data_ptr(), path, sptr)
+                        else:
+                            rc = lib.wqbmm_a16w4_msd_profile_stage(st["x"].data_ptr(), st["w"].data_ptr(),
+                                                                   st["s"].data_ptr(), gs, M, K, N,
+                                                                   st["y"].data_ptr(), path, k, sptr)
+                        if rc:
+                            raise W.WqbmmError(rc, "sweep")
+                    return f
+                print(f"[sweep] {label} M={M} path={path}", file=sys.stderr, flush=True)
+                t = Timed(torch, stream, [call(st) for st in sets], args.steps, args.warmup)
+                step_ms = t.spread(5)["median_ms"]
+                del t
+                prep_name, main_name = kernels_of(path, M, K, N, gs)
+                prep_ms = None
+                if prep_name:
+                    t = Timed(torch, stream, [call(st, 1) for st in sets], args.steps, args.warmup)
+                    prep_ms = t.replay_ms()[0]
+                    del t
+                t = Timed(torch, stream, [call(st, 2) for st in sets], args.steps, args.warmup)
+                main_ms = t.replay_ms()[0]
+                del t
+                rows.append({"shape": label, "M": M, "K": K, "N": N, "group_size": gs,
+                             "path": {1: "decode", 2: "prefill"}[path],
+                             "selected": W.wqbmm_select_path(M, K, N, gs) == path,
+                             "step_us": round(step_ms * 1e3, 3),
+                             "effective_TOPS": round(alg["eff_ops"] / (step_ms * 1e-3) / 1e12, 2),
+                             "weight_GBps": round(alg["w_bytes"] / (step_ms * 1e-3) / 1e9, 1),
+                             "prep_kernel": prep_name,
+                             "prep_us": None if prep_ms is None else round(prep_ms * 1e3, 3),
+                             "main_kernel": main_name, "main_us": round(main_ms * 1e3, 3)})
+            del sets
+            torch.cuda.synchronize()
+    return rows
+
+
 def main():
     from weight_only_quantized_msd_amd import datagen
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -419,6 +488,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-plain-read", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the bench line: the decode-vs-prefill M sweep (one JSON line)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -441,6 +512,11 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    if args.sweep:
+        print(json.dumps({"sweep": sweep(torch, W, args), "steps": args.steps,
+                          "kernel_sources_sha": kernel_sources_sha()}), flush=True)
+        return
 
     head = measure(torch, W, args.workload, args, args.path)
     nested = {}

@@ -16,6 +16,20 @@ FAKE = 0x1000          # 16-byte aligned, never dereferenced: validation fails f
 MIS = 0x1008           # misaligned
 
 
+@pytest.fixture(autouse=True)
+def no_device_visible():
+    """These checks pass pointers that are never valid device memory.  They
+    run only where no GPU is visible: there a call that validation wrongly
+    let through stops at the device check (WQBMM_ERR_UNSUPPORTED) instead of
+    launching kernels on the fake pointers."""
+    try:
+        import torch
+        if torch.cuda.is_available():
+            pytest.skip("fake-pointer validation checks run only without a visible GPU")
+    except ImportError:
+        pass
+
+
 def test_library_exports_every_header_symbol():
     names = L.header_functions()
     assert {"wqbmm_a16w4_msd", "wqbmm_a16w4_msd_prepass", "wqbmm_a16w4_msd_yint"} <= set(names)
@@ -35,7 +49,8 @@ def test_status_strings_and_version():
 def test_select_path():
     assert L.wqbmm_select_path(1, 4096, 4096, 128) == L.WQBMM_PATH_DECODE
     assert L.wqbmm_select_path(16, 4096, 11008, 128) == L.WQBMM_PATH_DECODE
-    assert L.wqbmm_select_path(17, 4096, 4096, 128) == L.WQBMM_PATH_PREFILL
+    assert L.wqbmm_select_path(64, 4096, 4096, 128) == L.WQBMM_PATH_DECODE
+    assert L.wqbmm_select_path(65, 4096, 4096, 128) == L.WQBMM_PATH_PREFILL
     assert L.wqbmm_select_path(2048, 4096, 4096, 128) == L.WQBMM_PATH_PREFILL
 
 
@@ -76,7 +91,7 @@ def test_msd_validation(name, over, want):
 @pytest.mark.parametrize("path,M,want", [
     (3, 4, L.WQBMM_ERR_INVALID),            # unknown path
     (-1, 4, L.WQBMM_ERR_INVALID),
-    (L.WQBMM_PATH_DECODE, 17, L.WQBMM_ERR_INVALID),   # decode kernel covers M <= 16
+    (L.WQBMM_PATH_DECODE, 65, L.WQBMM_ERR_INVALID),   # decode kernels cover M <= 64
     (L.WQBMM_PATH_DECODE, 0, L.WQBMM_OK),
     (L.WQBMM_PATH_PREFILL, 0, L.WQBMM_OK),
 ])
@@ -107,7 +122,7 @@ def test_prepass_validation(over, want):
     (dict(ge=5), L.WQBMM_ERR_INVALID),          # K/gs = 4 groups
     (dict(gb=2, ge=2), L.WQBMM_ERR_INVALID),    # empty range
     (dict(gb=3, ge=1), L.WQBMM_ERR_INVALID),
-    (dict(path=L.WQBMM_PATH_DECODE, M=32), L.WQBMM_ERR_INVALID),
+    (dict(path=L.WQBMM_PATH_DECODE, M=65), L.WQBMM_ERR_INVALID),
     (dict(M=0), L.WQBMM_OK),
 ])
 def test_yint_validation(over, want):
@@ -128,7 +143,7 @@ def test_yint_validation(over, want):
     (dict(gs=96, K=192), L.WQBMM_ERR_UNSUPPORTED),
     (dict(path=3), L.WQBMM_ERR_INVALID),
     (dict(path=-1), L.WQBMM_ERR_INVALID),
-    (dict(path=L.WQBMM_PATH_DECODE, M=17), L.WQBMM_ERR_INVALID),
+    (dict(path=L.WQBMM_PATH_DECODE, M=65), L.WQBMM_ERR_INVALID),
     (dict(M=0, x=0, y=0), L.WQBMM_OK),
 ])
 def test_profile_stage_validation(over, want):

@@ -99,7 +99,7 @@ def sample_rows(M, n, seed):
 
 
 ALL = ["tiny", "decode_m1", "decode_m16", "ffn_up_m16", "prefill_m2048", "outlier_m128",
-       "pages_sample_m1"]
+       "pages_sample_m1", "mid_m64", "mid_m256"]
 
 
 # ------------------------------------------------------------------ weight tiling
@@ -186,6 +186,8 @@ YINT_CASES = [
     ("outlier_m128", PREFILL, (0, 2)), ("outlier_m128", PREFILL, (64, 65)),
     ("outlier_m128", PREFILL, (_O_SEEDED, _O_SEEDED + 1)), ("outlier_m128", PREFILL, (126, 128)),
     ("pages_sample_m1", DECODE, (0, 64)),
+    ("mid_m64", DECODE, None), ("mid_m64", PREFILL, (13, 19)),
+    ("mid_m256", PREFILL, (0, 32)),
 ]
 
 
@@ -217,6 +219,8 @@ Y_CASES = [
     ("prefill_m2048", AUTO, None),
     ("outlier_m128", AUTO, None),
     ("pages_sample_m1", AUTO, None),
+    ("mid_m64", AUTO, None), ("mid_m64", DECODE, None), ("mid_m64", PREFILL, None),
+    ("mid_m256", AUTO, None),
 ]
 
 
@@ -242,6 +246,7 @@ def test_y_within_tolerance(torch_dev, name, path, nrows):
 RAGGED = [  # (M, K, N, gs)
     (1, 64, 32, 64), (2, 128, 96, 128), (3, 192, 160, 64), (4, 640, 288, 128),
     (5, 576, 4128, 64), (13, 1024, 416, 128), (16, 2560, 544, 128), (17, 512, 160, 64),
+    (40, 1152, 224, 128), (64, 704, 96, 64), (65, 512, 160, 128),
     (130, 384, 288, 128), (257, 256, 128, 64),
     # M <= 4 with K split over workgroups and a last chunk that ends inside it
     (1, 4736, 96, 64), (3, 6272, 160, 128),
@@ -262,7 +267,7 @@ def test_ragged_shapes(torch_dev, M, K, N, gs):
     ra, _ = oracle.decompose(d["x"], gs)
     G = K // gs
     ref_yi = oracle.yint(ra, d["w"], gs, 0, G)
-    paths = (DECODE, PREFILL) if M <= 16 else (PREFILL,)
+    paths = (DECODE, PREFILL) if M <= 64 else (PREFILL,)
     bound = elementwise_bound(d)
     for p in paths:
         announce(f"ragged M={M} K={K} N={N} gs={gs} path={p}")
@@ -274,13 +279,17 @@ def test_ragged_shapes(torch_dev, M, K, N, gs):
         assert np.array_equal(yi.cpu().numpy(), ref_yi), f"path {p} Y_int"
 
 
-# The decode contraction for 4 < M <= 16 (operand kernel + full-K contraction):
-# K beyond 4096 (several load rounds per wave), a single 128-row block, K not
-# a multiple of 128 at group size 64, and Y_int over group ranges that start
-# and end inside a 128-row block.
+# The decode contraction for 4 < M <= 64 (operand kernel + full-K contraction,
+# rows in slices of 16): K beyond 4096 (several load rounds per wave), a
+# single 128-row block, K not a multiple of 128 at group size 64, Y_int over
+# group ranges that start and end inside a 128-row block, and every slice
+# count with full and ragged last slices (M = 17, 31, 32, 33, 48, 63, 64).
 GEMV_CASES = [  # (M, K, N, gs, g_begin, g_end)
     (16, 8192, 512, 128, 0, 64), (8, 12288, 256, 128, 37, 91), (16, 8192, 384, 64, 5, 118),
     (5, 64, 96, 64, 0, 1), (9, 128, 64, 128, 0, 1), (12, 320, 160, 64, 1, 4),
+    (17, 4096, 512, 128, 0, 32), (31, 2048, 256, 64, 3, 29), (32, 8192, 384, 128, 11, 60),
+    (33, 1024, 288, 128, 0, 8), (48, 4096, 256, 64, 0, 64), (63, 640, 160, 64, 1, 9),
+    (64, 4096, 512, 128, 0, 32), (64, 12288, 128, 64, 90, 150),
 ]
 
 
@@ -415,7 +424,7 @@ def test_profile_stages_compose_to_path(torch_dev, name, path):
     with pytest.raises(W.WqbmmError):
         W.wqbmm_a16w4_msd_profile_stage(x[: max(1, d["M"] // 2)].contiguous(), w, s, gs, 2, path=path)
     other = PREFILL if path == DECODE else DECODE
-    if d["M"] <= 16:   # operands of the other path are not these
+    if d["M"] <= 64:   # operands of the other path are not these
         W.wqbmm_a16w4_msd_profile_stage(x, w, s, gs, 1, path=other)
         with pytest.raises(W.WqbmmError):
             W.wqbmm_a16w4_msd_profile_stage(x, w, s, gs, 2, path=path)

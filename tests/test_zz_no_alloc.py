@@ -80,16 +80,31 @@ def test_noalloc_back_to_back_and_repeat(torch_dev):
 
 
 def test_noalloc_rejects_too_large_before_launch(torch_dev):
+    """Real device buffers of the stated shapes (uninitialised: nothing reads
+    them when the size check works), so that no call can reach a kernel with
+    an invalid pointer."""
     import weight_only_quantized_msd_amd as W
     from weight_only_quantized_msd_amd import _lib as L
-    FAKE = 0x1000   # never dereferenced: the size check fails first
+    torch = torch_dev
     announce("noalloc too large")
+
+    def bufs(M, K, N, gs):
+        x = torch.empty((M, K), dtype=torch.float16, device="cuda")
+        w = torch.empty((N // 16, (K + 127) // 128 * 1024), dtype=torch.uint8, device="cuda")
+        s = torch.empty((K // gs, N), dtype=torch.float16, device="cuda")
+        y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        return x, w, s, y
+
+    def call(M, K, N, gs, null_x=False):
+        x, w, s, y = bufs(M, K, N, gs)
+        rc = L.wqbmm_a16w4_msd_noalloc_raw(0 if null_x else x.data_ptr(), w.data_ptr(), s.data_ptr(), gs,
+                                           M, K, N, y.data_ptr(), None)
+        torch.cuda.synchronize()
+        return rc
+
     # prefill operands beyond 62 MiB
-    assert L.wqbmm_a16w4_msd_noalloc_raw(FAKE, FAKE, FAKE, 128, 16384, 4096, 4096, FAKE, None) \
-        == W.WQBMM_ERR_TOO_LARGE
+    assert call(16384, 4096, 4096, 128) == W.WQBMM_ERR_TOO_LARGE
     # split-K accumulators beyond 2 MiB (M = 4, K > 4096, N = 131072)
-    assert L.wqbmm_a16w4_msd_noalloc_raw(FAKE, FAKE, FAKE, 128, 4, 8192, 131072, FAKE, None) \
-        == W.WQBMM_ERR_TOO_LARGE
+    assert call(4, 8192, 131072, 128) == W.WQBMM_ERR_TOO_LARGE
     # the usual validation still comes first
-    assert L.wqbmm_a16w4_msd_noalloc_raw(0, FAKE, FAKE, 128, 4, 256, 256, FAKE, None) \
-        == W.WQBMM_ERR_NULLPTR
+    assert call(4, 256, 256, 128, null_x=True) == W.WQBMM_ERR_NULLPTR

@@ -30,7 +30,7 @@ using wqbmm::DecodePlan;
 constexpr int64_t kMaxM = int64_t(1) << 24;
 constexpr int64_t kMaxK = int64_t(1) << 20;
 constexpr int64_t kMaxN = int64_t(1) << 20;
-constexpr int kDecodeMaxM = 16;
+constexpr int kDecodeMaxM = 64;
 
 // NULL counts as aligned: it is only accepted where the array is empty (M == 0).
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -99,7 +99,7 @@ Needs needs_of(int path, int64_t gs, int64_t M, int64_t K, int64_t N, int64_t g_
   Needs n;
   if (path == WQBMM_PATH_DECODE) {
     if (M > 4) {
-      n.ops = wqbmm::decode_gemv_workspace_bytes((int)gs, K);
+      n.ops = wqbmm::decode_gemv_workspace_bytes((int)gs, M, K);
     } else if (!yint) {
       n.acc = wqbmm::decode_accum_bytes(wqbmm::decode_plan((int)gs, M, K, N, g_begin, g_end), M, N);
     }

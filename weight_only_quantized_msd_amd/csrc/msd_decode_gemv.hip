@@ -1,4 +1,4 @@
-// msd_decode_gemv.hip -- the MSD matmul for 4 < M <= 16 as two kernels: x is
+// msd_decode_gemv.hip -- the MSD matmul for 4 < M <= 64 as two kernels: x is
 // decomposed ONCE into int4-packed MFMA operands, then a GEMV-shaped
 // contraction streams the weights with every workgroup covering whole K.
 //
@@ -19,18 +19,24 @@
 //   wave      = a contiguous run of 128-row blocks (WK waves split K),
 //   reduction = the WK waves' fp32 sums added in LDS in a fixed order.
 //
+// Rows of x come in slices of 16 (R = ceil(M/16) <= 4 slices): each weight
+// chunk a wave loads is the MFMA operand of all R slices, so the weights are
+// streamed once whatever M is, while the level operands (every row of x, for
+// every column tile) grow with R.
+//
 // Level operands.  Every level value lies in [-7, 7] (7.49 < 7.5 and a
 // residual is at most 1/2), so the levels are stored as 4-bit two's
 // complement in exactly the nibble arrangement of the tiled weights: chunk
-// (128-row block kb, level l, lane) is 16 bytes at ((kb*3 + l)*64 + lane)*16;
-// the lane holds row m = lane%16 at k = 128kb + 64s + 16(lane/16) + 8d + j
-// (low nibble of byte 4d + j of step s's 8 bytes) and k + 4 (high nibble).
+// (128-row block kb, slice r, level l, lane) is 16 bytes at
+// (((kb*R + r)*3 + l)*64 + lane)*16; the lane holds row m = 16r + lane%16 at
+// k = 128kb + 64s + 16(lane/16) + 8d + j (low nibble of byte 4d + j of step
+// s's 8 bytes) and k + 4 (high nibble).
 // The same two masks that turn a weight chunk into the i8 MFMA's B operand
 // (16*w per byte) turn a level chunk into its A operand (16*a per byte), so
 // each product is 256*a*w, exact in int32 (|sum| <= 256*7*8*128 < 2^21).
 // Rows m >= M and rows k >= K hold 0.  Beside them the operand kernel stores
-// each group's step-10 level weights A_max * w_l as fp32 [G][level][16 rows]
-// (rows >= M: 0), so that the contraction does not form them once per
+// each group's step-10 level weights A_max * w_l as fp32 [G][slice][level][16
+// rows] (rows >= M: 0), so that the contraction does not form them once per
 // column tile.
 #include "msd_device.hpp"
 #include "msd_launch.hpp"
@@ -45,34 +51,37 @@ constexpr float kD2 = kC2 * 0.0625f;
 constexpr float kD3 = kC3 * 0.0625f;
 
 // ---- steps 1-8: x fp16 [M][K] -> level chunks + group maxima ---------------
-// One workgroup per 128-row block; thread t = 16m + 8s + 2q + d decomposes the
-// 8 elements of row m at k = 128kb + 64s + 16q + 8d + (0..7), which is one
-// dword of each level chunk (lane m + 16q, step s, dword d).  A group is
-// GS/8 consecutive, aligned threads (16 at GS = 128: all (s, q, d) of a row;
-// 8 at GS = 64: all (q, d) of a row and step), as msd_decompose8 requires.
+// One workgroup per (128-row block kb, slice r); thread t = 16m + 8s + 2q + d
+// decomposes the 8 elements of row 16r + m at k = 128kb + 64s + 16q + 8d +
+// (0..7), which is one dword of each level chunk (lane m + 16q, step s, dword
+// d).  A group is GS/8 consecutive, aligned threads (16 at GS = 128: all (s,
+// q, d) of a row; 8 at GS = 64: all (q, d) of a row and step), as
+// msd_decompose8 requires.
 template <int GS>
 __global__ __launch_bounds__(256) void msd_decode_operands_kernel(
-    const uint16_t* __restrict__ x, int M, int K, uint32_t* __restrict__ lvl,
+    const uint16_t* __restrict__ x, int M, int K, int R, uint32_t* __restrict__ lvl,
     float* __restrict__ qt) {
   const int kb = blockIdx.x;
+  const int r = blockIdx.y;
   const int t = threadIdx.x;
   const int m = t >> 4, s = (t >> 3) & 1, q = (t >> 1) & 3, d = t & 1;
+  const int row = 16 * r + m;
   const int k = kb * kTileRows + 64 * s + 16 * q + 8 * d;
-  const bool ok = m < M && k < K;
-  const uint4 v = *reinterpret_cast<const uint4*>(x + (ok ? (int64_t)m * K + k : 0));
+  const bool ok = row < M && k < K;
+  const uint4 v = *reinterpret_cast<const uint4*>(x + (ok ? (int64_t)row * K + k : 0));
   const uint4 xv = ok ? v : make_uint4(0u, 0u, 0u, 0u);
   uint32_t lv[3][2];
   float amax;
   msd_decompose8<GS>(xv, lv, amax);
-  const int64_t base = ((int64_t)kb * 3 * 64 + m + 16 * q) * 4 + 2 * s + d;   // dword index, level 0
+  const int64_t base = (((int64_t)kb * R + r) * 3 * 64 + m + 16 * q) * 4 + 2 * s + d;   // level 0
 #pragma unroll
   for (int l = 0; l < 3; ++l)   // byte j: element j (low nibble), element j + 4 (high nibble)
     lvl[base + (int64_t)l * 64 * 4] = (lv[l][0] & 0x0F0F0F0Fu) | ((lv[l][1] & 0x0F0F0F0Fu) << 4);
   if ((t & (GS / 8 - 1)) == 0 && k < K) {   // the group's level weights A_max * w_l (step 10)
-    float* q = qt + (int64_t)((kb * kTileRows + 64 * s) / GS) * 48 + m;
-    q[0] = amax * kD1;
-    q[16] = amax * kD2;
-    q[32] = amax * kD3;
+    float* qq = qt + ((int64_t)((kb * kTileRows + 64 * s) / GS) * R + r) * 48 + m;
+    qq[0] = amax * kD1;
+    qq[16] = amax * kD2;
+    qq[32] = amax * kD3;
   }
 }
 
@@ -85,21 +94,22 @@ __global__ __launch_bounds__(256) void msd_decode_operands_kernel(
 //     two loads and keeps them in its own LDS slice: per block, per lane
 //     loads of them would cost three 4-byte and one 8-byte access of 64 lanes
 //     for 48 and 32 distinct bytes;
-//   - keeps two blocks of weight and level chunks in flight: the loads of
-//     block j+2 are issued after the compute of block j;
-//   - per 64-row step runs one v_mfma_i32_16x16x64_i8 per level with the
-//     weight chunk as the A operand (MFMA row = output column) and the level
-//     chunk as the B operand (MFMA column = row m of x): D^T = W^T . A_l^T.
+//   - keeps D blocks of weight and level chunks in flight: the loads of
+//     block j+D are issued after the compute of block j;
+//   - per 64-row step runs one v_mfma_i32_16x16x64_i8 per slice and level
+//     with the weight chunk as the A operand (MFMA row = output column) and
+//     the level chunk as the B operand (MFMA column = row of x): D^T = W^T .
+//     A_l^T.
 // Every load is unconditional and its result unmodified (a block past the
 // wave's range reads the round's first block again and its groups are
 // dropped by a zero scale; a load under a branch, or a select on its result,
-// makes the compiler wait for it right there).  Lane l holds row m = l%16 of
-// x for the four consecutive columns 16nt + 4(l/16) + r (element r).  Per
-// completed group the three level sums combine with A_max*w_l and the scale
-// (step 10) into the lane's fp32 sums (step 11, groups ascending within the
-// wave).  The waves' sums are then added in LDS, wave 0 first, and wave 0
-// stores y, 8 bytes per lane.
-template <int GS, int WK, int KBW, bool YINT>
+// makes the compiler wait for it right there).  Lane l holds row 16r + l%16
+// of x (slice r) for the four consecutive columns 16nt + 4(l/16) + c
+// (element c).  Per completed group the three level sums combine with
+// A_max*w_l and the scale (step 10) into the lane's fp32 sums (step 11,
+// groups ascending within the wave).  The waves' sums are then added in LDS,
+// wave 0 first, and wave 0 stores y, 8 bytes per lane and slice.
+template <int GS, int WK, int KBW, int R, bool YINT>
 __global__ __launch_bounds__(64 * WK) void msd_decode_gemv_kernel(
     const uint8_t* __restrict__ lvl, const float* __restrict__ qt,
     const uint8_t* __restrict__ wt, const uint16_t* __restrict__ scale, int M, int K, int N,
@@ -107,13 +117,14 @@ __global__ __launch_bounds__(64 * WK) void msd_decode_gemv_kernel(
     int32_t* __restrict__ y_int) {
   constexpr int GPB = kTileRows / GS;            // groups per block
   constexpr int RG = KBW * GPB;                  // groups per round
-  constexpr int QF = RG * 48 / 64;               // staged level weights per lane
+  constexpr int QG = 48 * R;                     // level weights per group: [slice][level][16 rows]
+  constexpr int QF = RG * QG / 64;               // staged level weights per lane
   constexpr int SV = RG * 16 / 64;               // staged scales per lane
-  constexpr int D = 2;                           // blocks in flight
-  static_assert(QF * 64 == RG * 48 && SV * 64 == RG * 16 && (SV == 1 || SV == 2), "round shape");
-  static_assert(48 % QF == 0, "a lane's staged level weights lie in one group");
-  __shared__ float4 sRed[WK > 1 ? WK - 1 : 1][64];
-  __shared__ float sQ[YINT ? 1 : WK][YINT ? 1 : RG * 48];                // [group][level][row]
+  constexpr int D = R <= 2 ? 2 : 1;              // blocks in flight
+  static_assert(QF * 64 == RG * QG && SV * 64 == RG * 16 && (SV == 1 || SV == 2), "round shape");
+  static_assert(QG % QF == 0, "a lane's staged level weights lie in one group");
+  __shared__ float4 sRed[WK > 1 ? WK - 1 : 1][R][64];
+  __shared__ float sQ[YINT ? 1 : WK][YINT ? 1 : RG * QG];                // [group][slice][level][row]
   __shared__ __attribute__((aligned(8))) uint16_t sS[YINT ? 1 : WK][YINT ? 4 : RG * 16];   // [group][col]
 
   const int lane = threadIdx.x & 63;
@@ -121,12 +132,16 @@ __global__ __launch_bounds__(64 * WK) void msd_decode_gemv_kernel(
   const int nt = blockIdx.x;
   const int KB = (K + kTileRows - 1) / kTileRows;
   const int G = K / GS;
-  const int m = lane & 15;                       // this lane's row of x
+  const int m = lane & 15;                       // this lane's row of x within its slice
   const int n0 = nt * kTileCols + 4 * (lane >> 4);   // first of its 4 columns
   const int wb_lo = kb_lo + wk * kbw;
   const int wb_hi = min(wb_lo + kbw, kb_hi);
 
-  float yacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float yacc[R][4];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) yacc[r][c] = 0.0f;
   const uint8_t* wcol = wt + (int64_t)nt * KB * 1024 + lane * 16;
   // staging: lane covers level weights [QF*lane, QF*lane + QF) of the round
   // and scales of group sgi, columns sc0 .. sc0 + SV - 1
@@ -134,12 +149,12 @@ __global__ __launch_bounds__(64 * WK) void msd_decode_gemv_kernel(
   const int sc0 = SV * (lane % (16 / SV));
 
   for (int kb0 = wb_lo; kb0 < wb_hi; kb0 += KBW) {
-    v4i av[KBW][3], wv[KBW];
+    v4i av[KBW][R][3], wv[KBW];
     float qst[QF];
     uint32_t sst = 0;
     if constexpr (!YINT) {
       const int g0 = kb0 * GPB;
-      const int qo = min(g0 * 48 + QF * lane, G * 48 - QF);   // past G: any valid floats
+      const int qo = min(g0 * QG + QF * lane, G * QG - QF);   // past G: any valid floats
 #pragma unroll
       for (int i = 0; i < QF; ++i) qst[i] = qt[qo + i];
       const int gc = min(g0 + sgi, G - 1);
@@ -152,8 +167,10 @@ __global__ __launch_bounds__(64 * WK) void msd_decode_gemv_kernel(
       const int kbc = kb < wb_hi ? kb : kb0;
       wv[j] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wcol + (int64_t)kbc * 1024));
 #pragma unroll
-      for (int l = 0; l < 3; ++l)
-        av[j][l] = *reinterpret_cast<const v4i*>(lvl + (((int64_t)kbc * 3 + l) * 64 + lane) * 16);
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int l = 0; l < 3; ++l)
+          av[j][r][l] = *reinterpret_cast<const v4i*>(lvl + ((((int64_t)kbc * R + r) * 3 + l) * 64 + lane) * 16);
     };
     auto stage = [&]() __attribute__((always_inline)) {
       if constexpr (!YINT) {
@@ -167,42 +184,55 @@ __global__ __launch_bounds__(64 * WK) void msd_decode_gemv_kernel(
       }
     };
     auto compute_block = [&](int j) __attribute__((always_inline)) {
-      v4i acc[3];
+      v4i acc[R][3];
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         if ((64 * st) % GS == 0) {
 #pragma unroll
-          for (int l = 0; l < 3; ++l) acc[l] = v4i{0, 0, 0, 0};
+          for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int l = 0; l < 3; ++l) acc[r][l] = v4i{0, 0, 0, 0};
         }
         const uint32_t w0 = (uint32_t)wv[j][2 * st], w1 = (uint32_t)wv[j][2 * st + 1];
         const v4i b = v4i{(int)lo16(w0), (int)hi16(w0), (int)lo16(w1), (int)hi16(w1)};
 #pragma unroll
-        for (int l = 0; l < 3; ++l) {
-          const uint32_t a0 = (uint32_t)av[j][l][2 * st], a1 = (uint32_t)av[j][l][2 * st + 1];
-          const v4i a = v4i{(int)lo16(a0), (int)hi16(a0), (int)lo16(a1), (int)hi16(a1)};
-          acc[l] = mfma_i8(b, a, acc[l]);
-        }
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int l = 0; l < 3; ++l) {
+            const uint32_t a0 = (uint32_t)av[j][r][l][2 * st], a1 = (uint32_t)av[j][r][l][2 * st + 1];
+            const v4i a = v4i{(int)lo16(a0), (int)hi16(a0), (int)lo16(a1), (int)hi16(a1)};
+            acc[r][l] = mfma_i8(b, a, acc[r][l]);
+          }
         if ((64 * st + 64) % GS != 0) continue;                      // group not complete
         const int gl = (64 * st) / GS;
         if constexpr (YINT) {
           const int g = (kb0 + j) * GPB + gl;
-          if (kb0 + j >= wb_hi || g < g_begin || g >= g_end || m >= M) continue;
+          if (kb0 + j >= wb_hi || g < g_begin || g >= g_end) continue;
           const int64_t gi = g - g_begin;
 #pragma unroll
-          for (int l = 0; l < 3; ++l)
-            *reinterpret_cast<v4i*>(y_int + ((gi * 3 + l) * M + m) * (int64_t)N + n0) = acc[l] >> 8;
+          for (int r = 0; r < R; ++r) {
+            const int row = 16 * r + m;
+            if (row >= M) continue;
+#pragma unroll
+            for (int l = 0; l < 3; ++l)
+              *reinterpret_cast<v4i*>(y_int + ((gi * 3 + l) * M + row) * (int64_t)N + n0) = acc[r][l] >> 8;
+          }
         } else {
           const int gi = j * GPB + gl;
-          const float q0 = sQ[wk][gi * 48 + m], q1 = sQ[wk][gi * 48 + 16 + m], q2 = sQ[wk][gi * 48 + 32 + m];
           const uint2 sv = *reinterpret_cast<const uint2*>(&sS[wk][gi * 16 + 4 * (lane >> 4)]);
           const float sc[4] = {half_bits_to_float(sv.x & 0xffffu), half_bits_to_float(sv.x >> 16),
                                half_bits_to_float(sv.y & 0xffffu), half_bits_to_float(sv.y >> 16)};
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float tt = (float)acc[0][r] * q0;
-            tt = __builtin_fmaf((float)acc[1][r], q1, tt);
-            tt = __builtin_fmaf((float)acc[2][r], q2, tt);
-            yacc[r] = __builtin_fmaf(tt, sc[r], yacc[r]);
+          for (int r = 0; r < R; ++r) {
+            const float* qg = &sQ[wk][gi * QG + r * 48];
+            const float q0 = qg[m], q1 = qg[16 + m], q2 = qg[32 + m];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              float tt = (float)acc[r][0][c] * q0;
+              tt = __builtin_fmaf((float)acc[r][1][c], q1, tt);
+              tt = __builtin_fmaf((float)acc[r][2][c], q2, tt);
+              yacc[r][c] = __builtin_fmaf(tt, sc[c], yacc[r][c]);
+            }
           }
         }
       }
@@ -228,45 +258,61 @@ __global__ __launch_bounds__(64 * WK) void msd_decode_gemv_kernel(
 
   // ---- the WK waves' sums, added in wave order; wave 0 stores y
   if constexpr (WK > 1) {
-    if (wk > 0) sRed[wk - 1][lane] = make_float4(yacc[0], yacc[1], yacc[2], yacc[3]);
+    if (wk > 0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) sRed[wk - 1][r][lane] = make_float4(yacc[r][0], yacc[r][1], yacc[r][2], yacc[r][3]);
+    }
     __syncthreads();
     if (wk != 0) return;
 #pragma unroll
-    for (int v = 0; v < WK - 1; ++v) {
-      const float4 p = sRed[v][lane];
-      yacc[0] += p.x; yacc[1] += p.y; yacc[2] += p.z; yacc[3] += p.w;
-    }
+    for (int v = 0; v < WK - 1; ++v)
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float4 p = sRed[v][r][lane];
+        yacc[r][0] += p.x; yacc[r][1] += p.y; yacc[r][2] += p.z; yacc[r][3] += p.w;
+      }
   }
-  if (m < M) {
-    const uint32_t lo = (uint32_t)float_to_half_bits(yacc[0]) | ((uint32_t)float_to_half_bits(yacc[1]) << 16);
-    const uint32_t hi = (uint32_t)float_to_half_bits(yacc[2]) | ((uint32_t)float_to_half_bits(yacc[3]) << 16);
-    *reinterpret_cast<uint2*>(y + (int64_t)m * N + n0) = make_uint2(lo, hi);
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int row = 16 * r + m;
+    if (row < M) {
+      const uint32_t lo = (uint32_t)float_to_half_bits(yacc[r][0]) | ((uint32_t)float_to_half_bits(yacc[r][1]) << 16);
+      const uint32_t hi = (uint32_t)float_to_half_bits(yacc[r][2]) | ((uint32_t)float_to_half_bits(yacc[r][3]) << 16);
+      *reinterpret_cast<uint2*>(y + (int64_t)row * N + n0) = make_uint2(lo, hi);
+    }
   }
 }
 
 namespace dg {
 constexpr int WK = 8;    // waves per workgroup (K split within the workgroup)
 constexpr int KBW = 4;   // 128-row blocks per wave and load round
+constexpr int kMaxSlices = 4;
 }  // namespace dg
 
-size_t decode_gemv_workspace_bytes(int gs, int64_t K) {
+int decode_gemv_slices(int64_t M) { return (int)((M + 15) / 16); }
+
+size_t decode_gemv_workspace_bytes(int gs, int64_t M, int64_t K) {
   const int64_t KB = (K + kTileRows - 1) / kTileRows;
-  return (size_t)KB * 3 * 1024 + (size_t)(K / gs) * 48 * sizeof(float);
+  const int64_t R = decode_gemv_slices(M);
+  return (size_t)(KB * R) * 3 * 1024 + (size_t)(K / gs) * (size_t)R * 48 * sizeof(float);
 }
 
 hipError_t launch_decode_gemv(const void* x, const void* w, const void* scale, int gs, int64_t M,
                               int64_t K, int64_t N, int64_t g_begin, int64_t g_end, void* y,
                               int32_t* y_int, uint8_t* ws, int stage, hipStream_t stream) {
-  if (M < 1 || M > 16 || N % kTileCols != 0 || stage < 0 || stage > 2) return hipErrorInvalidValue;
+  const int R = decode_gemv_slices(M);
+  if (M < 1 || R > dg::kMaxSlices || N % kTileCols != 0 || stage < 0 || stage > 2)
+    return hipErrorInvalidValue;
   const int KB = (int)((K + kTileRows - 1) / kTileRows);
   uint32_t* lvl = reinterpret_cast<uint32_t*>(ws);
-  float* qt = reinterpret_cast<float*>(ws + (size_t)KB * 3 * 1024);
+  float* qt = reinterpret_cast<float*>(ws + (size_t)KB * R * 3 * 1024);
   if (stage != 2) {
     const uint16_t* xp = static_cast<const uint16_t*>(x);
+    const dim3 og((unsigned)KB, (unsigned)R);
     if (gs == 64)
-      hipLaunchKernelGGL(msd_decode_operands_kernel<64>, dim3(KB), dim3(256), 0, stream, xp, (int)M, (int)K, lvl, qt);
+      hipLaunchKernelGGL(msd_decode_operands_kernel<64>, og, dim3(256), 0, stream, xp, (int)M, (int)K, R, lvl, qt);
     else
-      hipLaunchKernelGGL(msd_decode_operands_kernel<128>, dim3(KB), dim3(256), 0, stream, xp, (int)M, (int)K, lvl, qt);
+      hipLaunchKernelGGL(msd_decode_operands_kernel<128>, og, dim3(256), 0, stream, xp, (int)M, (int)K, R, lvl, qt);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || stage == 1) return e;
   }
@@ -280,14 +326,24 @@ hipError_t launch_decode_gemv(const void* x, const void* w, const void* scale, i
   const uint16_t* sp = static_cast<const uint16_t*>(scale);
   uint16_t* yp = static_cast<uint16_t*>(y);
   const int m = (int)M, k = (int)K, n = (int)N, gb = (int)g_begin, ge = (int)g_end;
-#define WQBMM_GEMV_LAUNCH(GS_, Y_)                                                                   \
-  hipLaunchKernelGGL((msd_decode_gemv_kernel<GS_, dg::WK, dg::KBW, Y_>), grid, dim3(64 * dg::WK), 0, stream, lp, \
-                     qt, wp, sp, m, k, n, gb, ge, kb_lo, kb_hi, kbw, yp, y_int)
+#define WQBMM_GEMV_LAUNCH(GS_, R_, Y_)                                                              \
+  hipLaunchKernelGGL((msd_decode_gemv_kernel<GS_, dg::WK, dg::KBW, R_, Y_>), grid, dim3(64 * dg::WK), 0,   \
+                     stream, lp, qt, wp, sp, m, k, n, gb, ge, kb_lo, kb_hi, kbw, yp, y_int)
+#define WQBMM_GEMV_R(GS_, Y_)                                                                       \
+  do {                                                                                              \
+    switch (R) {                                                                                    \
+      case 1: WQBMM_GEMV_LAUNCH(GS_, 1, Y_); break;                                                 \
+      case 2: WQBMM_GEMV_LAUNCH(GS_, 2, Y_); break;                                                 \
+      case 3: WQBMM_GEMV_LAUNCH(GS_, 3, Y_); break;                                                 \
+      default: WQBMM_GEMV_LAUNCH(GS_, 4, Y_); break;                                                \
+    }                                                                                               \
+  } while (0)
   if (gs == 64) {
-    if (y_int) WQBMM_GEMV_LAUNCH(64, true); else WQBMM_GEMV_LAUNCH(64, false);
+    if (y_int) WQBMM_GEMV_R(64, true); else WQBMM_GEMV_R(64, false);
   } else {
-    if (y_int) WQBMM_GEMV_LAUNCH(128, true); else WQBMM_GEMV_LAUNCH(128, false);
+    if (y_int) WQBMM_GEMV_R(128, true); else WQBMM_GEMV_R(128, false);
   }
+#undef WQBMM_GEMV_R
 #undef WQBMM_GEMV_LAUNCH
   return hipGetLastError();
 }

@@ -85,12 +85,13 @@ hipError_t launch_decode(const void* x, const void* w, const void* scale, int gs
                          int64_t K, int64_t N, int64_t g_begin, int64_t g_end, void* y,
                          int32_t* y_int, uint64_t* accum, const DecodePlan& plan, hipStream_t stream);
 
-// Decode for 4 < M <= 16 (msd_decode_gemv.hip): an operand kernel decomposes
-// x once into int4-packed level operands and level weights in `ws`
-// (decode_gemv_workspace_bytes), then a contraction kernel covers all of K
-// per 16-column tile (no K-split hand-off).  stage 0: both kernels; 1: the
-// operand kernel only; 2: the contraction only, on the operands in `ws`.
-size_t decode_gemv_workspace_bytes(int gs, int64_t K);
+// Decode for 4 < M <= 64 (msd_decode_gemv.hip): an operand kernel decomposes
+// x once into int4-packed level operands (slices of 16 rows) and level
+// weights in `ws` (decode_gemv_workspace_bytes), then a contraction kernel
+// covers all of K per 16-column tile (no K-split hand-off).  stage 0: both
+// kernels; 1: the operand kernel only; 2: the contraction only, on the
+// operands in `ws`.
+size_t decode_gemv_workspace_bytes(int gs, int64_t M, int64_t K);
 hipError_t launch_decode_gemv(const void* x, const void* w, const void* scale, int gs, int64_t M,
                               int64_t K, int64_t N, int64_t g_begin, int64_t g_end, void* y,
                               int32_t* y_int, uint8_t* ws, int stage, hipStream_t stream);

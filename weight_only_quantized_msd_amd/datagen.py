@@ -47,7 +47,8 @@ class Workload:
         return self.K // self.group_size
 
 
-# The five measured workloads plus the page's own sample shape (§4.3).
+# The five measured workloads, two points in the middle of the M range and
+# the page's own sample shape (§4.3).
 WORKLOADS = {
     "tiny": Workload("tiny", 4, 256, 256, 64, seed=0,
                      note="smallest parity case, several groups and tiles"),
@@ -63,6 +64,12 @@ WORKLOADS = {
                              scale_dist=("lognormal", -4.5, 0.3),
                              outlier_frac=0.01, outlier_mult=50.0,
                              note="1% of K channels x50; lognormal scales"),
+    # The middle of the M = 1..2048 range at the decode shape (same
+    # distributions as decode_m16): where the kernel paths meet.
+    "mid_m64": Workload("mid_m64", 64, 4096, 4096, 128, seed=7,
+                        note="64 rows, K = N = 4096: the row-sliced decode contraction"),
+    "mid_m256": Workload("mid_m256", 256, 4096, 4096, 128, seed=8,
+                         note="256 rows, K = N = 4096: two 128-row blocks of the prefill GEMM"),
     # The page's sample: M=1, N=12288, K=8192, groupSize=128, x ~ U[-3,3],
     # w in [-7,7], scale ~ U[-3,3] (negative scales allowed).
     "pages_sample_m1": Workload("pages_sample_m1", 1, 8192, 12288, 128, seed=6,
