@@ -49,6 +49,8 @@ def test_status_strings_and_version():
 def test_select_path():
     assert L.wqbmm_select_path(1, 4096, 4096, 128) == L.WQBMM_PATH_DECODE
     assert L.wqbmm_select_path(16, 4096, 11008, 128) == L.WQBMM_PATH_DECODE
+    assert L.wqbmm_select_path(48, 8192, 28672, 64) == L.WQBMM_PATH_DECODE
+    assert L.wqbmm_select_path(49, 8192, 28672, 64) == L.WQBMM_PATH_PREFILL
     assert L.wqbmm_select_path(64, 4096, 4096, 128) == L.WQBMM_PATH_DECODE
     assert L.wqbmm_select_path(65, 4096, 4096, 128) == L.WQBMM_PATH_PREFILL
     assert L.wqbmm_select_path(2048, 4096, 4096, 128) == L.WQBMM_PATH_PREFILL

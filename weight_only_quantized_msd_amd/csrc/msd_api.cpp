@@ -310,9 +310,20 @@ wqbmm_status run(const void* x, const void* w, const void* scale, int64_t gs, in
 
 extern "C" {
 
+// The split between the two kernel paths, from the M sweep of both paths
+// (MALL-cold step time, one MI355X):
+//   K = N = 4096, group size 128: decode 7.9 / 9.8 / 11.8 / 13.4 us at
+//     M = 16 / 32 / 48 / 64 against the prefill path's 53-54 us at every M
+//     up to 128 (one 128-row block);
+//   K = 8192, N = 28672, group size 64: decode 42.3 / 62.2 / 84.2 / 129.6 us
+//     at M = 16 / 32 / 48 / 64 against prefill 111-113 us.
+// Decode up to 48 rows everywhere; from 49 to 64 rows only at group size
+// 128 (at group size 64 the four-slice contraction, 3 waves per SIMD, loses).
 int wqbmm_select_path(int64_t M, int64_t K, int64_t N, int64_t group_size) {
-  (void)K; (void)N; (void)group_size;
-  return M <= kDecodeMaxM ? WQBMM_PATH_DECODE : WQBMM_PATH_PREFILL;
+  (void)K; (void)N;
+  if (M <= 48) return WQBMM_PATH_DECODE;
+  if (M <= kDecodeMaxM && group_size == 128) return WQBMM_PATH_DECODE;
+  return WQBMM_PATH_PREFILL;
 }
 
 const char* wqbmm_status_string(int status) {
