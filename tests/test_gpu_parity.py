@@ -315,6 +315,40 @@ def test_decode_contraction_shapes(torch_dev, M, K, N, gs, gb, ge):
     assert np.array_equal(got, ref), f"{np.count_nonzero(got != ref)} words differ"
 
 
+# The group-128 GEMM with few tiles splits K over workgroups and adds the
+# splits' fp32 partial sums in split order: single and ragged row blocks,
+# ragged columns, split counts from 2 to 8 (uneven last split), and Y_int
+# over odd group ranges (each split stores its own groups).
+SPLITK_CASES = [  # (M, K, N, gs, g_begin, g_end)
+    (1, 1024, 160, 128, 3, 8), (65, 2304, 416, 128, 0, 18), (130, 1024, 288, 128, 1, 8),
+    (300, 4096, 544, 128, 5, 30), (97, 4096, 4096, 128, 0, 32),
+]
+
+
+@pytest.mark.parametrize("M,K,N,gs,gb,ge", SPLITK_CASES,
+                         ids=[f"M{c[0]}K{c[1]}N{c[2]}r{c[4]}-{c[5]}" for c in SPLITK_CASES])
+def test_prefill_splitk_shapes(torch_dev, M, K, N, gs, gb, ge):
+    import weight_only_quantized_msd_amd as W
+    torch = torch_dev
+    d = datagen.random_case(M, K, N, gs, seed=M * 7 + K + N)
+    if K >= 4 * gs:
+        d["x"] = adversarial_x(M + K + 3, M, K, gs)
+    x, w, s = to_dev(torch, d)
+    announce(f"prefill split-K M={M} K={K} N={N} gs={gs} groups=[{gb},{ge})")
+    y = W.wqbmm_a16w4_msd_path(x, w, s, gs, PREFILL)
+    y2 = W.wqbmm_a16w4_msd_path(x, w, s, gs, PREFILL)
+    yi = W.wqbmm_a16w4_msd_yint(x, w, gs, gb, ge, path=PREFILL)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    y32, _ = oracle.matmul(d["x"], d["w_packed"], d["scale"], gs)
+    check_y(y.cpu().numpy(), y32, "prefill split-K")
+    check_y_elementwise(y.cpu().numpy(), y32, elementwise_bound(d), "prefill split-K")
+    ra, _ = oracle.decompose(d["x"], gs)
+    ref = oracle.yint(ra, d["w"], gs, gb, ge)
+    got = yi.cpu().numpy()
+    assert np.array_equal(got, ref), f"{np.count_nonzero(got != ref)} words differ"
+
+
 # Group size 64 with many row blocks: the weights are converted by the
 # preparation kernel and the GEMM runs 128 x 256 tiles (at least 256 of them);
 # K = 192 leaves a last stage of one group.  Sampled rows against the oracle.

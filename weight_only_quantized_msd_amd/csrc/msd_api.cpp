@@ -91,7 +91,8 @@ struct Needs {
 };
 
 size_t prefill_ops_bytes(const wqbmm::PrefillLayout& L) {
-  return round_up(L.a_bytes, 256) + round_up(L.q_bytes, 256) + round_up(L.b_bytes, 256);
+  return round_up(L.a_bytes, 256) + round_up(L.q_bytes, 256) + round_up(L.b_bytes, 256) +
+         round_up(L.part_bytes, 256);
 }
 
 Needs needs_of(int path, int64_t gs, int64_t M, int64_t K, int64_t N, int64_t g_begin, int64_t g_end,
@@ -270,13 +271,14 @@ wqbmm_status run_prefill(const Buffers& b, const void* x, const void* w, const v
   uint8_t* a_t = b.ops;
   float* q_t = reinterpret_cast<float*>(b.ops + round_up(L.a_bytes, 256));
   uint8_t* b_t = b.ops + round_up(L.a_bytes, 256) + round_up(L.q_bytes, 256);
+  float* part = reinterpret_cast<float*>(b_t + round_up(L.b_bytes, 256));
   if (stage != 2) {
     const wqbmm_status st =
         launch_status(wqbmm::launch_prefill_prep(x, w, (int)gs, M, K, N, L, a_t, q_t, b_t, stream));
     if (st != WQBMM_OK || stage == 1) return st;
   }
   return launch_status(wqbmm::launch_prefill_gemm(a_t, q_t, b_t, w, scale, (int)gs, M, K, N, L,
-                                                  g_begin, g_end, y, y_int, stream));
+                                                  g_begin, g_end, y, y_int, part, stream));
 }
 
 wqbmm_status run_path(const Buffers& b, int path, const void* x, const void* w, const void* scale,

@@ -40,6 +40,8 @@ struct PrefillLayout {
   size_t q_bytes;      // level weights, [group][row block][level][128] fp32
   size_t b_bytes;      // weight tiles: (npad/16) * G tiles of 1536 bytes (0 if w_in_gemm)
   bool w_in_gemm;      // the GEMM converts the tiled int4 weights itself (few row blocks)
+  int64_t splits = 1;  // K-splits of the GEMM (few tiles); > 1: fp32 partial sums + a reduction
+  size_t part_bytes = 0;   // splits * M * N fp32 partial sums (0 without a split)
 };
 PrefillLayout prefill_layout(int gs, int64_t M, int64_t K, int64_t N);
 
@@ -48,12 +50,14 @@ hipError_t launch_prefill_prep(const void* x, const void* w, int gs, int64_t M, 
                                uint8_t* b_t, hipStream_t stream);
 
 // y_int == nullptr: groups [g_begin, g_end) are combined into y (fp16 [M][N]);
-// otherwise they are stored as int32 Y_int.
+// otherwise they are stored as int32 Y_int.  With L.splits > 1 the GEMM
+// splits the group range and writes fp32 partial sums to `part`
+// (L.part_bytes), which a second kernel adds in split order into y.
 hipError_t launch_prefill_gemm(const uint8_t* a_t, const float* q_t, const uint8_t* b_t,
                                const void* w_tiled,
                                const void* scale, int gs, int64_t M, int64_t K, int64_t N,
                                const PrefillLayout& L, int64_t g_begin, int64_t g_end, void* y,
-                               int32_t* y_int, hipStream_t stream);
+                               int32_t* y_int, float* part, hipStream_t stream);
 
 // Group size 64 (msd_prefill64.hip): the same roles on the 32x32x64 FP6 MFMA
 // (one group per instruction); the launchers above dispatch to these.

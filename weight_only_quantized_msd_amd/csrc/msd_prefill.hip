@@ -73,6 +73,8 @@
 // bands of 4 row blocks (column-major within a band), so that the tiles an
 // XCD runs together share 4 A runs and few B runs in its L2.  The mapping
 // affects speed only.
+#include <algorithm>
+
 #include "msd_device.hpp"
 #include "msd_launch.hpp"
 
@@ -275,8 +277,8 @@ template <int GS, int BN, bool YINT>
 __global__ __launch_bounds__(pf::THREADS, 1) void msd_gemm_kernel(
     const uint8_t* __restrict__ a_t, const float* __restrict__ q_t,
     const uint8_t* __restrict__ b_t, const uint16_t* __restrict__ scale, int M, int Mpad, int K,
-    int N, int g_begin, int g_end, int mblocks, int nblocks, uint16_t* __restrict__ y,
-    int32_t* __restrict__ y_int) {
+    int N, int g_begin, int g_end, int mblocks, int nblocks, int splits, int gps,
+    uint16_t* __restrict__ y, int32_t* __restrict__ y_int, float* __restrict__ part) {
   using namespace pf;
   constexpr int CT = BN / 16;                          // column tiles per block
   constexpr int NT = CT / WAVES_N;                     // column tiles per wave: 8 or 4
@@ -310,9 +312,16 @@ __global__ __launch_bounds__(pf::THREADS, 1) void msd_gemm_kernel(
   // Tile order: XCD x (= id % 8) runs the contiguous range of tiles
   // [x * total/8, (x+1) * total/8); tiles are numbered in bands of BAND row
   // blocks, column-major within a band.
-  const int total = mblocks * nblocks;
+  const int tiles = mblocks * nblocks;
+  const int total = tiles * splits;
   int t = blockIdx.x;
   if (total % NXCD == 0) t = (blockIdx.x % NXCD) * (total / NXCD) + blockIdx.x / NXCD;
+  // K-split (few tiles): split sp takes groups [g_lo, g_hi) of the range and,
+  // unless Y_int is exported, leaves an fp32 partial sum for the reduction
+  const int sp = t / tiles;
+  t %= tiles;
+  const int g_lo = g_begin + sp * gps;
+  const int g_hi = min(g_end, g_lo + gps);
   const int band_tiles = BAND * nblocks;
   const int band = t / band_tiles;
   const int in_band = t % band_tiles;
@@ -441,16 +450,16 @@ __global__ __launch_bounds__(pf::THREADS, 1) void msd_gemm_kernel(
   // ones.  While a group is computed from one buffer, the next group is
   // copied into the other; each wave waits for its own copies, and the
   // barrier then publishes all of them and frees the buffer just read.
-  dma(g_begin, sA0, sB0, sQ0, sS0);
+  dma(g_lo, sA0, sB0, sQ0, sS0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int g = g_begin; g < g_end; g += 2) {
-    if (g + 1 < g_end) dma(g + 1, sA1, sB1, sQ1, sS1);
+  for (int g = g_lo; g < g_hi; g += 2) {
+    if (g + 1 < g_hi) dma(g + 1, sA1, sB1, sQ1, sS1);
     compute(sA0, sB0, sQ0, sS0, g);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (g + 1 >= g_end) break;
-    if (g + 2 < g_end) dma(g + 2, sA0, sB0, sQ0, sS0);
+    if (g + 1 >= g_hi) break;
+    if (g + 2 < g_hi) dma(g + 2, sA0, sB0, sQ0, sS0);
     compute(sA1, sB1, sQ1, sS1, g + 1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -466,13 +475,47 @@ __global__ __launch_bounds__(pf::THREADS, 1) void msd_gemm_kernel(
 #pragma unroll
         for (int c = 0; c < NT; ++c) {
           const int n = n0 + wn * WN + c * 16 + (lane & 15);
-          if (n < N) y[(int64_t)m * N + n] = float_to_half_bits(yacc[r][c][i]);
+          if (n >= N) continue;
+          if (splits > 1) part[((int64_t)sp * M + m) * N + n] = yacc[r][c][i];
+          else y[(int64_t)m * N + n] = float_to_half_bits(yacc[r][c][i]);
         }
       }
   }
 }
 
+// ------------------------------------------------------- split-K reduction
+// y[m][n] = fp16_rne(sum over splits s = 0, 1, .. of part[s][m][n]), the
+// splits added in ascending order (each split holds its groups' sum, groups
+// ascending), so the result is the same on every run.  Four consecutive
+// outputs per thread (N % 4 == 0).
+__global__ __launch_bounds__(256) void msd_splitk_reduce_kernel(const float* __restrict__ part,
+                                                                int splits, int64_t MN,
+                                                                uint16_t* __restrict__ y) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= MN) return;
+  float4 acc = *reinterpret_cast<const float4*>(part + i);
+  for (int s = 1; s < splits; ++s) {
+    const float4 p = *reinterpret_cast<const float4*>(part + (int64_t)s * MN + i);
+    acc.x += p.x; acc.y += p.y; acc.z += p.z; acc.w += p.w;
+  }
+  const uint32_t lo = (uint32_t)float_to_half_bits(acc.x) | ((uint32_t)float_to_half_bits(acc.y) << 16);
+  const uint32_t hi = (uint32_t)float_to_half_bits(acc.z) | ((uint32_t)float_to_half_bits(acc.w) << 16);
+  *reinterpret_cast<uint2*>(y + i) = make_uint2(lo, hi);
+}
+
 // ---------------------------------------------------------------- launchers
+
+// K-split of the GEMM when its tiles alone would leave CUs idle: enough
+// splits to bring the workgroups to about one per CU (the GEMM holds one
+// workgroup per CU), each split at least two groups long.  The splits' fp32
+// partial sums [splits][M][N] follow the operand tiles in the workspace.
+void set_splits(PrefillLayout& L, int64_t tiles, int64_t G, int64_t M, int64_t N) {
+  int64_t s = tiles >= 256 ? 1 : 256 / tiles;
+  s = std::min<int64_t>(s, std::max<int64_t>(1, G / 2));
+  const int64_t gps = (G + s - 1) / s;
+  L.splits = (G + gps - 1) / gps;
+  L.part_bytes = L.splits > 1 ? (size_t)L.splits * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
 
 // Column blocks of 256 when that still gives at least one workgroup per CU
 // (256 workgroups), else of 128.
@@ -488,6 +531,7 @@ PrefillLayout prefill_layout(int gs, int64_t M, int64_t K, int64_t N) {
   L.q_bytes = (size_t)(G * (L.mpad / pf::BM)) * pf::Q_GROUP;
   L.b_bytes = (size_t)((L.npad / 16) * G) * pf::TILE;
   L.w_in_gemm = false;
+  set_splits(L, (L.mpad / pf::BM) * (L.npad / L.bn), G, M, N);
   return L;
 }
 
@@ -509,20 +553,28 @@ hipError_t launch_prefill_prep(const void* x, const void* w, int gs, int64_t M, 
 hipError_t launch_prefill_gemm(const uint8_t* a_t, const float* q_t, const uint8_t* b_t,
                                const void* w_tiled, const void* scale, int gs, int64_t M, int64_t K, int64_t N,
                                const PrefillLayout& L, int64_t g_begin, int64_t g_end, void* y,
-                               int32_t* y_int, hipStream_t stream) {
+                               int32_t* y_int, float* part, hipStream_t stream) {
   if (gs == 64)
     return launch_prefill64_gemm(a_t, q_t, b_t, w_tiled, scale, M, K, N, L, g_begin, g_end, y, y_int,
                                  stream);
   if (L.bn != 128 && L.bn != 256) return hipErrorInvalidValue;
   const int mblocks = (int)(L.mpad / pf::BM);
   const int nblocks = (int)(L.npad / L.bn);
-  const dim3 grid((unsigned)(mblocks * nblocks));
+  // the layout's split count over this group range (a Y_int export needs no
+  // partial sums: each split stores its own groups)
+  const int64_t range = g_end - g_begin;
+  int64_t splits = std::min<int64_t>(L.splits, range);
+  const int64_t gps = (range + splits - 1) / splits;
+  splits = (range + gps - 1) / gps;
+  if (splits > 1 && !y_int && (!part || splits > L.splits)) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(mblocks * nblocks * splits));
   const uint16_t* sp = static_cast<const uint16_t*>(scale);
   uint16_t* yp = static_cast<uint16_t*>(y);
   const int m = (int)M, mp = (int)L.mpad, k = (int)K, n = (int)N, gb = (int)g_begin, ge = (int)g_end;
+  const int S = (int)splits, GPS = (int)gps;
 #define WQBMM_GEMM_LAUNCH(GS_, BN_, Y_)                                                          \
   hipLaunchKernelGGL((msd_gemm_kernel<GS_, BN_, Y_>), grid, dim3(pf::THREADS), 0, stream, a_t,  \
-                     q_t, b_t, sp, m, mp, k, n, gb, ge, mblocks, nblocks, yp, y_int)
+                     q_t, b_t, sp, m, mp, k, n, gb, ge, mblocks, nblocks, S, GPS, yp, y_int, part)
 #define WQBMM_GEMM_BN(GS_, Y_)                                                                   \
   do {                                                                                           \
     if (L.bn == 256) WQBMM_GEMM_LAUNCH(GS_, 256, Y_); else WQBMM_GEMM_LAUNCH(GS_, 128, Y_);       \
@@ -530,6 +582,11 @@ hipError_t launch_prefill_gemm(const uint8_t* a_t, const float* q_t, const uint8
   if (y_int) WQBMM_GEMM_BN(128, true); else WQBMM_GEMM_BN(128, false);
 #undef WQBMM_GEMM_BN
 #undef WQBMM_GEMM_LAUNCH
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || y_int || S == 1) return e;
+  const int64_t MN = M * N;
+  hipLaunchKernelGGL(msd_splitk_reduce_kernel, dim3((unsigned)((MN / 4 + 255) / 256)), dim3(256), 0, stream,
+                     part, S, MN, yp);
   return hipGetLastError();
 }
 
