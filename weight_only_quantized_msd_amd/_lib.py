@@ -11,7 +11,9 @@ import os
 import re
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libwqbmm.so")
+# WQBMM_LIB selects another build of the same library (the host-sanitized
+# build for the sanitizer runs of the boundary tests); default: the product.
+LIB_PATH = os.environ.get("WQBMM_LIB") or os.path.join(_HERE, "libwqbmm.so")
 INCLUDE_DIR = os.path.join(os.path.dirname(_HERE), "include")
 HEADER_PATH = os.path.join(INCLUDE_DIR, "wqbmm.h")
 

@@ -52,5 +52,35 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+def build_host_sanitized(verbose: bool = False) -> str:
+    """libwqbmm_san.so: the library with its host code (msd_api.cpp: argument
+    validation, dispatch, workspace bookkeeping) built with AddressSanitizer
+    and UndefinedBehaviorSanitizer; device code and the kernel objects are the
+    normal ones (build() must have run).  The process that loads it must
+    preload clang's ASan runtime.  The sanitizers apply to host code only."""
+    objs = [os.path.join(BUILD_DIR, os.path.splitext(s)[0] + ".o") for s in SOURCES if s != "msd_api.cpp"]
+    for o in objs:
+        if not os.path.exists(o):
+            raise RuntimeError(f"{o} missing: run build() first")
+    api_obj = os.path.join(BUILD_DIR, "msd_api_san.o")
+    cmd = [HIPCC, "-x", "hip"] + CFLAGS + ["-g", "-Xarch_host", "-fsanitize=address",
+                                             "-Xarch_host", "-fsanitize=undefined",
+                                             "-Xarch_host", "-fno-sanitize-recover=all",
+                                             "-c", os.path.join(CSRC, "msd_api.cpp"), "-o", api_obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on msd_api.cpp (sanitized):\n{r.stdout}\n{r.stderr}")
+    out = os.path.join(_HERE, "libwqbmm_san.so")
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address",
+           "-Xarch_host", "-fsanitize=undefined", "-shared-libsan", "-o", out + ".tmp", api_obj] + objs
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
