@@ -351,12 +351,14 @@ def measure(torch, W, name, args, path_override=0):
     extra = {}
     if path == 1:
         if M > 4:
-            # contraction kernel: tiled int4 weights, scales, the 16-row level
-            # operands (three int4 levels) and level weights once, y
+            # contraction kernel: tiled int4 weights, scales, the level operands
+            # (three int4 levels per row slice) and level weights once, y
+            # R = ceil(M/16) slices of 16 rows, each three int4 levels of every k
             kb = -(-K // 128)
-            kbytes = alg["w_bytes"] + 2 * G * N + 3 * 1024 * kb + 192 * G + 2 * M * N
+            R = -(-M // 16)
+            kbytes = alg["w_bytes"] + 2 * G * N + R * (3 * 1024 * kb + 192 * G) + 2 * M * N
             extra["prep"] = {"kernel": prep_name, "avg_kernel_us": round(prep_ms * 1e3, 3),
-                             "algorithmic_bytes_per_launch": 2 * M * K + 3 * 1024 * kb + 192 * G}
+                             "algorithmic_bytes_per_launch": 2 * M * K + R * (3 * 1024 * kb + 192 * G)}
         else:
             kbytes = alg["bytes"]
         achieved = kbytes / (kern_ms * 1e-3) / 1e9
