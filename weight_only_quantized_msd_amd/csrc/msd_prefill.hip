@@ -466,20 +466,60 @@ __global__ __launch_bounds__(pf::THREADS, 1) void msd_gemm_kernel(
   }
 
   if constexpr (!YINT) {
+    // y (or a split's fp32 partial sum) through LDS (the operand buffers are
+    // free: every wave passed the barrier after its last group and no copy
+    // is in flight): each wave writes its 32 x WN tile in rows of stride YS
+    // bytes (68 dwords: the four row groups of an MFMA result land on
+    // distinct banks), then stores whole 16-byte runs of consecutive
+    // columns instead of one 2- or 4-byte store per output.
+    constexpr int YS = 272;
+    static_assert(4 * WM * YS <= A_GROUP && WN * 2 <= YS - 16, "staging fits the A buffers");
+    uint8_t* st = (wave < 4 ? sA0 : sA1) + (wave % 4) * (WM * YS);
+    if (splits > 1) {
+      if constexpr (BN == 128) {                         // a split GEMM has 128-column blocks
+        static_assert(WN * 4 <= YS - 16, "fp32 rows fit the stride");
+#pragma unroll
+        for (int r = 0; r < MT; ++r)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = r * 16 + (lane >> 4) * 4 + i;
+#pragma unroll
+            for (int c = 0; c < NT; ++c)
+              *reinterpret_cast<float*>(st + row * YS + (c * 16 + (lane & 15)) * 4) = yacc[r][c][i];
+          }
+        __syncthreads();
+        constexpr int RUNS = WN / 4;                     // 16-byte runs of 4 floats per row
+#pragma unroll
+        for (int j = 0; j < WM * RUNS / 64; ++j) {
+          const int run = j * 64 + lane;
+          const int row = run / RUNS, col = (run % RUNS) * 4;
+          const int m = m0 + wm * WM + row, n = n0 + wn * WN + col;
+          const v4i v = *reinterpret_cast<const v4i*>(st + row * YS + col * 4);
+          if (m < M && n < N) *reinterpret_cast<v4i*>(part + ((int64_t)sp * M + m) * N + n) = v;
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int r = 0; r < MT; ++r)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int m = m0 + wm * WM + r * 16 + (lane >> 4) * 4 + i;
-        if (m >= M) continue;
+        const int row = r * 16 + (lane >> 4) * 4 + i;
 #pragma unroll
-        for (int c = 0; c < NT; ++c) {
-          const int n = n0 + wn * WN + c * 16 + (lane & 15);
-          if (n >= N) continue;
-          if (splits > 1) part[((int64_t)sp * M + m) * N + n] = yacc[r][c][i];
-          else y[(int64_t)m * N + n] = float_to_half_bits(yacc[r][c][i]);
-        }
+        for (int c = 0; c < NT; ++c)
+          *reinterpret_cast<uint16_t*>(st + row * YS + (c * 16 + (lane & 15)) * 2) =
+              float_to_half_bits(yacc[r][c][i]);
       }
+    __syncthreads();
+    constexpr int RUNS = WN / 8;                         // 16-byte runs per row
+#pragma unroll
+    for (int j = 0; j < WM * RUNS / 64; ++j) {
+      const int run = j * 64 + lane;
+      const int row = run / RUNS, col = (run % RUNS) * 8;
+      const int m = m0 + wm * WM + row, n = n0 + wn * WN + col;
+      const v4i v = *reinterpret_cast<const v4i*>(st + row * YS + col * 2);
+      if (m < M && n < N) *reinterpret_cast<v4i*>(y + (int64_t)m * N + n) = v;
+    }
   }
 }
 
@@ -566,7 +606,9 @@ hipError_t launch_prefill_gemm(const uint8_t* a_t, const float* q_t, const uint8
   int64_t splits = std::min<int64_t>(L.splits, range);
   const int64_t gps = (range + splits - 1) / splits;
   splits = (range + gps - 1) / gps;
-  if (splits > 1 && !y_int && (!part || splits > L.splits)) return hipErrorInvalidValue;
+  // (a split GEMM stages its fp32 partial sums for 128-column blocks only;
+  // the layout splits only below 256 tiles, where the blocks are 128 wide)
+  if (splits > 1 && !y_int && (!part || splits > L.splits || L.bn != 128)) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(mblocks * nblocks * splits));
   const uint16_t* sp = static_cast<const uint16_t*>(scale);
   uint16_t* yp = static_cast<uint16_t*>(y);

@@ -695,18 +695,32 @@ __global__ __launch_bounds__(1024, 1) void msd_gemm64w_kernel(
   }
 
   if constexpr (!YINT) {
-    const int m = m0 + wm * 32 + (lane & 31);
-    if (m < M) {
+    // y through LDS (free after the last barrier: no copy, load or
+    // conversion is in flight): the workgroup's 128 x 128 tile as fp16 rows
+    // of stride YS bytes, then whole 16-byte runs of 8 consecutive columns
+    // (two per thread) instead of one 8-byte store per lane and 4 columns
+    constexpr int YS = 272;
+    static_assert(BM * YS <= X_STAGE && BN * 2 <= YS - 16, "staging fits an x buffer");
+    uint8_t* st = sX0;
+    const int row = wm * 32 + (lane & 31);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int n = n0 + wn * 32 + 8 * r + 4 * (lane >> 5);   // 4 consecutive columns
-        if (n >= N) continue;
-        const uint32_t lo = (uint32_t)float_to_half_bits(yacc[4 * r]) |
-                            ((uint32_t)float_to_half_bits(yacc[4 * r + 1]) << 16);
-        const uint32_t hi = (uint32_t)float_to_half_bits(yacc[4 * r + 2]) |
-                            ((uint32_t)float_to_half_bits(yacc[4 * r + 3]) << 16);
-        *reinterpret_cast<uint2*>(y + (int64_t)m * N + n) = make_uint2(lo, hi);
-      }
+    for (int r = 0; r < 4; ++r) {
+      const int col = wn * 32 + 8 * r + 4 * (lane >> 5);   // 4 consecutive columns
+      const uint32_t lo = (uint32_t)float_to_half_bits(yacc[4 * r]) |
+                          ((uint32_t)float_to_half_bits(yacc[4 * r + 1]) << 16);
+      const uint32_t hi = (uint32_t)float_to_half_bits(yacc[4 * r + 2]) |
+                          ((uint32_t)float_to_half_bits(yacc[4 * r + 3]) << 16);
+      *reinterpret_cast<uint2*>(st + row * YS + col * 2) = make_uint2(lo, hi);
+    }
+    __syncthreads();
+    constexpr int RUNS = BN / 8;                        // 16-byte runs per row
+#pragma unroll
+    for (int j = 0; j < BM * RUNS / 1024; ++j) {
+      const int run = j * 1024 + tid;
+      const int rr = run / RUNS, cc = (run % RUNS) * 8;
+      const int m = m0 + rr, n = n0 + cc;
+      const v4i v = *reinterpret_cast<const v4i*>(st + rr * YS + cc * 2);
+      if (m < M && n < N) *reinterpret_cast<v4i*>(y + (int64_t)m * N + n) = v;
     }
   }
 }
