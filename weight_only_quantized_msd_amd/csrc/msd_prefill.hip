@@ -130,18 +130,21 @@ __device__ __forceinline__ v6i pack_e2m3(const v16f& u, const v16f& v, float div
 }
 
 // ---------------------------------------------------------------- prep kernel
-// Waves [0, xwaves): one (pair of 16-row tiles, group) each, steps 1-8 for
-// its 2 x 16 x GS elements, one row tile after the other.  Lane l takes row
+// Waves [0, xwaves): one (TPW 16-row tiles, group) each, steps 1-8 for its
+// TPW x 16 x GS elements, one row tile after the other.  Lane l takes row
 // l/4 and, with kq = l%4, the elements of operand lane 16*kq + row (u: k =
 // 16*kq + j, v: k = 64 + 16*kq + j), so a group's maximum is a 4-lane
-// reduction; the wave's stores fill one whole tile pair per level (every
-// store a whole 16-byte lane); the rows' level weights A_max * w_l go to Q_t.
+// reduction; the rows' level weights A_max * w_l go to Q_t.  TPW = 2: the
+// wave's stores fill one whole tile pair per level (every store a whole
+// 16-byte lane).  TPW = 1 (few rows, where a wave's latency rather than the
+// bytes sets the time): a wave per row tile, whose dwords 4-5 are an 8-byte
+// store beside those of the other tile of its pair.
 // Waves [xwaves, ...): one (pair of column tiles, pair of 128-row blocks)
 // each: four 16-byte tiled-weight chunks per lane (column tiles up to the
 // padded width; those beyond N become zeros), all loaded before any is
 // converted in place into operand lane l of its column tile (column blocks
 // of BN), and each block's tile pair stored whole.
-template <int GS>
+template <int GS, int TPW>
 __global__ __launch_bounds__(256) void msd_prep_kernel(const uint16_t* __restrict__ x,
                                                        const uint8_t* __restrict__ wt, int M,
                                                        int Mpad, int K, int N, int Npad, int BN,
@@ -149,18 +152,21 @@ __global__ __launch_bounds__(256) void msd_prep_kernel(const uint16_t* __restric
                                                        float* __restrict__ q_t,
                                                        uint8_t* __restrict__ b_t) {
   static_assert(GS == 128, "the group-128 path (group size 64 has a kernel of its own)");
+  static_assert(TPW == 1 || TPW == 2, "one row tile or a pair per wave");
   using namespace pf;
   const int G = K / GS;
   const int lane = threadIdx.x & 63;
   const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (wid < xwaves) {
-    const int mtp = (int)(wid / G), g = (int)(wid % G);
+    const int tt = (int)(wid / G), g = (int)(wid % G);
     const int r = lane >> 2, kq = lane & 3;
-    const int rb = (2 * mtp) / RT, rt0 = (2 * mtp) % RT;   // rt0 even: the pair's first row tile
-    uint32_t hi0[3][2];                                     // the first row tile's dwords 4-5
+    const int t0 = TPW * tt;                                // the wave's first row tile
+    const int rb = t0 / RT, rt0 = (t0 & ~1) % RT;          // rt0 even: the pair's first row tile
+    uint32_t hi0[3][2];                                     // TPW = 2: the first row tile's dwords 4-5
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int m = (2 * mtp + p) * 16 + r;
+    for (int pp = 0; pp < TPW; ++pp) {
+      const int p = (t0 + pp) & 1;                         // position within the pair
+      const int m = (t0 + pp) * 16 + r;
       const bool real = m < M;                       // padding rows decompose zeros
       const uint16_t* src = x + (real ? (int64_t)m * K + (int64_t)g * GS + 16 * kq : 0);
       uint4 xv[4];
@@ -196,7 +202,9 @@ __global__ __launch_bounds__(256) void msd_prep_kernel(const uint16_t* __restric
         const v6i pk = pack_e2m3(lv[l][0], lv[l][1], 1.0f);
         const int slot = 16 * kq + r;
         *reinterpret_cast<v4i*>(pair + p * TILE_LO + slot * 16) = v4i{pk[0], pk[1], pk[2], pk[3]};
-        if (p == 0) {
+        if constexpr (TPW == 1) {
+          *reinterpret_cast<v2i*>(pair + 2 * TILE_LO + slot * 16 + p * 8) = v2i{pk[4], pk[5]};
+        } else if (p == 0) {
           hi0[l][0] = (uint32_t)pk[4];
           hi0[l][1] = (uint32_t)pk[5];
         } else {
@@ -579,14 +587,21 @@ hipError_t launch_prefill_prep(const void* x, const void* w, int gs, int64_t M, 
                                int64_t N, const PrefillLayout& L, uint8_t* a_t, float* q_t,
                                uint8_t* b_t, hipStream_t stream) {
   if (gs == 64) return launch_prefill64_prep(x, w, M, K, N, L, a_t, q_t, b_t, stream);
-  const int64_t xwaves = (L.mpad / 32) * (K / gs);                // (row tile pair, group) tasks
+  // up to 4 row blocks: one row tile per x wave (twice the waves, each half
+  // as long); beyond, a tile pair per wave
+  const int tpw = L.mpad <= 4 * pf::BM ? 1 : 2;
+  const int64_t xwaves = (L.mpad / (16 * tpw)) * (K / gs);          // (row tile(s), group) tasks
   const int64_t wwaves = (L.npad / 32) * ((tiled_kblocks(K) + 1) / 2);   // (column tile pair, block pair)
   const unsigned blocks = (unsigned)((xwaves + wwaves + 3) / 4);
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   const uint8_t* wp = static_cast<const uint8_t*>(w);
   const int m = (int)M, mp = (int)L.mpad, k = (int)K, n = (int)N, np = (int)L.npad, bn = (int)L.bn;
-  hipLaunchKernelGGL(msd_prep_kernel<128>, dim3(blocks), dim3(256), 0, stream, xp, wp, m, mp, k,
-                     n, np, bn, xwaves, a_t, q_t, b_t);
+  if (tpw == 1)
+    hipLaunchKernelGGL((msd_prep_kernel<128, 1>), dim3(blocks), dim3(256), 0, stream, xp, wp, m, mp,
+                       k, n, np, bn, xwaves, a_t, q_t, b_t);
+  else
+    hipLaunchKernelGGL((msd_prep_kernel<128, 2>), dim3(blocks), dim3(256), 0, stream, xp, wp, m, mp,
+                       k, n, np, bn, xwaves, a_t, q_t, b_t);
   return hipGetLastError();
 }
 
