@@ -322,6 +322,8 @@ def test_decode_contraction_shapes(torch_dev, M, K, N, gs, gb, ge):
 SPLITK_CASES = [  # (M, K, N, gs, g_begin, g_end)
     (1, 1024, 160, 128, 3, 8), (65, 2304, 416, 128, 0, 18), (130, 1024, 288, 128, 1, 8),
     (300, 4096, 544, 128, 5, 30), (97, 4096, 4096, 128, 0, 32),
+    # 32 splits: more than the GEMM finishes itself, so the separate reduction runs
+    (1, 8192, 128, 128, 10, 50),
 ]
 
 
