@@ -315,6 +315,35 @@ def test_decode_contraction_shapes(torch_dev, M, K, N, gs, gb, ge):
     assert np.array_equal(got, ref), f"{np.count_nonzero(got != ref)} words differ"
 
 
+# More column tiles than CUs (N/16 > 256): the decode contraction's workgroups
+# each cover a run of column tiles with the level chunks held in registers.
+# One and two row slices, both group sizes, up to 4 and up to 8 blocks per
+# wave, waves without blocks (K = 640), and a last workgroup with fewer tiles
+# (one, for the odd-count path).
+MULTI_CASES = [  # (M, K, N, gs)
+    (16, 4096, 4128, 128), (9, 8192, 5152, 64), (32, 4096, 6144, 128), (20, 2048, 8224, 64),
+    (5, 640, 4640, 128), (16, 8192, 4160, 128),
+]
+
+
+@pytest.mark.parametrize("M,K,N,gs", MULTI_CASES, ids=[f"M{c[0]}K{c[1]}N{c[2]}g{c[3]}" for c in MULTI_CASES])
+def test_decode_multi_tile_shapes(torch_dev, M, K, N, gs):
+    import weight_only_quantized_msd_amd as W
+    torch = torch_dev
+    d = datagen.random_case(M, K, N, gs, seed=M * 17 + K + N)
+    if K >= 4 * gs:
+        d["x"] = adversarial_x(M + K + 5, M, K, gs)
+    x, w, s = to_dev(torch, d)
+    announce(f"decode multi-tile M={M} K={K} N={N} gs={gs}")
+    y = W.wqbmm_a16w4_msd_path(x, w, s, gs, DECODE)
+    y2 = W.wqbmm_a16w4_msd_path(x, w, s, gs, DECODE)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    y32, _ = oracle.matmul(d["x"], d["w_packed"], d["scale"], gs)
+    check_y(y.cpu().numpy(), y32, "decode multi-tile")
+    check_y_elementwise(y.cpu().numpy(), y32, elementwise_bound(d), "decode multi-tile")
+
+
 # The group-128 GEMM with few tiles splits K over workgroups and adds the
 # splits' fp32 partial sums in split order: single and ragged row blocks,
 # ragged columns, split counts from 2 to 8 (uneven last split), and Y_int
