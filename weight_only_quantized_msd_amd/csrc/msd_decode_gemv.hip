@@ -376,14 +376,18 @@ __global__ __launch_bounds__(64 * WK) void msd_decode_gemv_multi_kernel(
     for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int c = 0; c < 4; ++c) yacc[r][c] = 0.0f;
-    // the level chunks count as redefined per tile, so that their unpacked
-    // MFMA operands (twice the registers) are formed per tile, not kept
+    // Beyond 4 blocks of one slice the level chunks count as redefined per
+    // tile, so that their unpacked MFMA operands (twice the registers) are
+    // formed per tile; at 4 blocks and one slice they fit, and the compiler
+    // keeps them unpacked across the tiles.
+    if constexpr (KBR > 4 || R > 1) {
 #pragma unroll
-    for (int j = 0; j < KBR; ++j)
+      for (int j = 0; j < KBR; ++j)
 #pragma unroll
-      for (int r = 0; r < R; ++r)
+        for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int l = 0; l < 3; ++l) asm volatile("" : "+v"(av[j][r][l]));
+          for (int l = 0; l < 3; ++l) asm volatile("" : "+v"(av[j][r][l]));
+    }
     if (has) {
 #pragma unroll
       for (int j = 0; j < KBR; ++j) {
