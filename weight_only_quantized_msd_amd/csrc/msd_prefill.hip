@@ -36,12 +36,14 @@
 //   are packed by the same instruction from the same k assignment, so the
 //   MFMA pairs equal k (whatever its own slot order).  Tiles are stored in
 //   pairs (tile 2j, 2j+1; 3072 bytes): [lane][dwords 0-3 of tile 2j] (1 KB),
-//   [lane][dwords 0-3 of tile 2j+1] (1 KB), then [lane][dwords 4-5 of tile
-//   2j, dwords 4-5 of tile 2j+1] (1 KB), so that a pair is read by three
-//   conflict-free ds_read_b128 (on gfx950 a ds_read_b64 moves half the bytes
-//   per cycle of a ds_read_b128: 128 against about 230 bytes per cycle and
-//   CU, measured).  The pairs are the two row tiles of a level that one
-//   GEMM wave holds, and two adjacent column tiles.
+//   [lane][dwords 0-3 of tile 2j+1] (1 KB), [lane][dwords 4-5 of tile 2j]
+//   (512 bytes), [lane][dwords 4-5 of tile 2j+1] (512 bytes).  A lane's two
+//   operands are then one ds_read_b128 and one ds_read_b64 each, read into
+//   registers that already form the six-dword operand (a 16-byte read of the
+//   two tiles' dwords 4-5 together, which moves more bytes per cycle, needs
+//   two register moves per operand pair to split it).  The pairs are the two
+//   row tiles of a level that one GEMM wave holds, and two adjacent column
+//   tiles.
 //   A_t: [row block of 128][group][level][row tile 0..7][tile]
 //   B_t: [column block of BN][group][column tile 0..BN/16-1][tile]
 //   Q_t: [group][row block][level][128 rows] fp32: A_max * w_l, the row's
@@ -90,6 +92,7 @@ constexpr int MT = WM / 16;    // 2 row tiles per wave
 constexpr int RT = BM / 16;    // 8 row tiles per block
 constexpr int TILE = 1536;     // bytes of one operand tile (16 x 128 k, e2m3)
 constexpr int TILE_LO = 1024;  // its [lane][dwords 0-3] part
+constexpr int TILE_HI = 512;   // its [lane][dwords 4-5] part
 constexpr int A_GROUP = 3 * RT * TILE;   // one group of a row block: 36 KB
 constexpr int Q_GROUP = 3 * BM * 4;      // level weights of a row block: 1.5 KB
 constexpr int NXCD = 8;
@@ -162,7 +165,6 @@ __global__ __launch_bounds__(256) void msd_prep_kernel(const uint16_t* __restric
     const int r = lane >> 2, kq = lane & 3;
     const int t0 = TPW * tt;                                // the wave's first row tile
     const int rb = t0 / RT, rt0 = (t0 & ~1) % RT;          // rt0 even: the pair's first row tile
-    uint32_t hi0[3][2];                                     // TPW = 2: the first row tile's dwords 4-5
 #pragma unroll
     for (int pp = 0; pp < TPW; ++pp) {
       const int p = (t0 + pp) & 1;                         // position within the pair
@@ -194,23 +196,14 @@ __global__ __launch_bounds__(256) void msd_prep_kernel(const uint16_t* __restric
           for (int l = 0; l < 3; ++l) lv[l][e / 16][e % 16] = rl[l];
         }
       }
-      // dwords 0-3 of this row tile's operands now; dwords 4-5 of the pair's
-      // two tiles together, once the second is packed (whole 16-byte lanes)
+      // this row tile's dwords 0-3 and 4-5 in their parts of the pair
 #pragma unroll
       for (int l = 0; l < 3; ++l) {
         uint8_t* pair = a_t + ((((int64_t)rb * G + g) * 3 + l) * RT + rt0) * TILE;
         const v6i pk = pack_e2m3(lv[l][0], lv[l][1], 1.0f);
         const int slot = 16 * kq + r;
         *reinterpret_cast<v4i*>(pair + p * TILE_LO + slot * 16) = v4i{pk[0], pk[1], pk[2], pk[3]};
-        if constexpr (TPW == 1) {
-          *reinterpret_cast<v2i*>(pair + 2 * TILE_LO + slot * 16 + p * 8) = v2i{pk[4], pk[5]};
-        } else if (p == 0) {
-          hi0[l][0] = (uint32_t)pk[4];
-          hi0[l][1] = (uint32_t)pk[5];
-        } else {
-          *reinterpret_cast<v4i*>(pair + 2 * TILE_LO + slot * 16) =
-              v4i{(int)hi0[l][0], (int)hi0[l][1], pk[4], pk[5]};
-        }
+        *reinterpret_cast<v2i*>(pair + 2 * TILE_LO + p * TILE_HI + slot * 8) = v2i{pk[4], pk[5]};
       }
       if (kq < 3) {                                  // lanes kq = 0, 1, 2: level weight kq of row m
         const float w = kq == 0 ? kE1 : (kq == 1 ? kE2 : kE3);
@@ -265,7 +258,8 @@ __global__ __launch_bounds__(256) void msd_prep_kernel(const uint16_t* __restric
     uint8_t* pair = b_t + (((int64_t)cb * G + kb) * CT + ct0) * TILE;
     *reinterpret_cast<v4i*>(pair + lane * 16) = v4i{pk[0][0], pk[0][1], pk[0][2], pk[0][3]};
     *reinterpret_cast<v4i*>(pair + TILE_LO + lane * 16) = v4i{pk[1][0], pk[1][1], pk[1][2], pk[1][3]};
-    *reinterpret_cast<v4i*>(pair + 2 * TILE_LO + lane * 16) = v4i{pk[0][4], pk[0][5], pk[1][4], pk[1][5]};
+    *reinterpret_cast<v2i*>(pair + 2 * TILE_LO + lane * 8) = v2i{pk[0][4], pk[0][5]};
+    *reinterpret_cast<v2i*>(pair + 2 * TILE_LO + TILE_HI + lane * 8) = v2i{pk[1][4], pk[1][5]};
   }
 }
 
@@ -273,12 +267,19 @@ __global__ __launch_bounds__(256) void msd_prep_kernel(const uint16_t* __restric
 // The two operands (six dwords each) of lane `lane` from an LDS tile pair
 // (address of its first tile), as the MFMA's eight-dword arguments (the last
 // two are unused by the FP6 form): three ds_read_b128.
+// The 8-byte reads are volatile: the compiler would otherwise merge two of
+// them (of this pair or of two pairs) into one read of four registers and
+// then move two of those into place.
 __device__ __forceinline__ void lds_operand_pair(const uint8_t* pair, int lane, v8i& op0, v8i& op1) {
   const v4i lo0 = *reinterpret_cast<const v4i*>(pair + lane * 16);
   const v4i lo1 = *reinterpret_cast<const v4i*>(pair + pf::TILE_LO + lane * 16);
-  const v4i hi = *reinterpret_cast<const v4i*>(pair + 2 * pf::TILE_LO + lane * 16);
-  op0 = v8i{lo0[0], lo0[1], lo0[2], lo0[3], hi[0], hi[1], 0, 0};
-  op1 = v8i{lo1[0], lo1[1], lo1[2], lo1[3], hi[2], hi[3], 0, 0};
+  typedef const volatile __attribute__((address_space(3))) v2i lds_v2i;
+  typedef const __attribute__((address_space(3))) uint8_t lds_u8;
+  lds_u8* lp = (lds_u8*)pair;
+  const v2i hi0 = *(lds_v2i*)(lp + 2 * pf::TILE_LO + lane * 8);
+  const v2i hi1 = *(lds_v2i*)(lp + 2 * pf::TILE_LO + pf::TILE_HI + lane * 8);
+  op0 = v8i{lo0[0], lo0[1], lo0[2], lo0[3], hi0[0], hi0[1], 0, 0};
+  op1 = v8i{lo1[0], lo1[1], lo1[2], lo1[3], hi1[0], hi1[1], 0, 0};
 }
 
 template <int GS, int BN, bool YINT>
