@@ -77,6 +77,11 @@ def kernels_of(path, M, K, N, gs):
     if path == 1:
         if M <= 4:
             return None, "msd_decode_kernel"
+        # more column tiles than CUs: workgroups of several tiles (one or two
+        # row slices, at most 8 or 4 blocks of 128 rows per wave)
+        R, kbw = -(-M // 16), -(-(-(-K // 128)) // 8)
+        if N // 16 > 256 and ((R == 1 and kbw <= 8) or (R == 2 and kbw <= 4)):
+            return "msd_decode_operands_kernel", "msd_decode_gemv_multi_kernel"
         return "msd_decode_operands_kernel", "msd_decode_gemv_kernel"
     if gs == 128:
         return "msd_prep_kernel", ("msd_gemm_kernel" if prefill_splits(M, K, N) == 1
