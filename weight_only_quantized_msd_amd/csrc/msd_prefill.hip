@@ -137,11 +137,11 @@ __device__ __forceinline__ v6i pack_e2m3(const v16f& u, const v16f& v, float div
 // TPW x 16 x GS elements, one row tile after the other.  Lane l takes row
 // l/4 and, with kq = l%4, the elements of operand lane 16*kq + row (u: k =
 // 16*kq + j, v: k = 64 + 16*kq + j), so a group's maximum is a 4-lane
-// reduction; the rows' level weights A_max * w_l go to Q_t.  TPW = 2: the
-// wave's stores fill one whole tile pair per level (every store a whole
-// 16-byte lane).  TPW = 1 (few rows, where a wave's latency rather than the
-// bytes sets the time): a wave per row tile, whose dwords 4-5 are an 8-byte
-// store beside those of the other tile of its pair.
+// reduction; the rows' level weights A_max * w_l go to Q_t.  Per row tile
+// and level a wave stores dwords 0-3 (16 bytes per lane) and dwords 4-5 (8
+// bytes per lane) into their parts of the tile pair.  TPW = 2 (many rows): a
+// wave per tile pair; TPW = 1 (up to four row blocks, where a wave's latency
+// rather than the bytes sets the time): a wave per row tile.
 // Waves [xwaves, ...): one (pair of column tiles, pair of 128-row blocks)
 // each: four 16-byte tiled-weight chunks per lane (column tiles up to the
 // padded width; those beyond N become zeros), all loaded before any is
@@ -266,7 +266,8 @@ __global__ __launch_bounds__(256) void msd_prep_kernel(const uint16_t* __restric
 // ---------------------------------------------------------------- GEMM kernel
 // The two operands (six dwords each) of lane `lane` from an LDS tile pair
 // (address of its first tile), as the MFMA's eight-dword arguments (the last
-// two are unused by the FP6 form): three ds_read_b128.
+// two are unused by the FP6 form): per operand one ds_read_b128 and one
+// ds_read_b64.
 // The 8-byte reads are volatile: the compiler would otherwise merge two of
 // them (of this pair or of two pairs) into one read of four registers and
 // then move two of those into place.
