@@ -6,8 +6,8 @@ makes two calls in a row on the entry point's one scratch array, the second
 with a smaller input (fewer rows, and for the two-kernel paths a smaller K),
 so that stale operands or accumulators from the first call would show.
 Shapes cover every path: the fused decode kernel with K split over
-workgroups (accumulators), the decode contraction (operands), and the
-prefill GEMMs at group sizes 128 and 64.
+workgroups (accumulators), the decode contraction (operands; one and several
+column tiles per workgroup), and the prefill GEMMs at group sizes 128 and 64.
 """
 import pytest
 
@@ -40,6 +40,7 @@ def inputs(torch, M, K, N, gs, seed):
 PAIRS = [  # (first call (M, K, N, gs), second, smaller call)
     ((4, 8192, 1024, 128), (1, 6272, 512, 64)),       # fused decode, K split: accumulators
     ((16, 4096, 1024, 128), (5, 1024, 512, 64)),      # decode contraction: operands
+    ((16, 4096, 8192, 128), (9, 2048, 4608, 64)),     # decode contraction, several tiles per workgroup
     ((2048, 4096, 1024, 128), (130, 1024, 288, 128)),  # prefill, group size 128
     ((256, 2048, 2048, 64), (17, 512, 160, 64)),      # prefill, group size 64
 ]
