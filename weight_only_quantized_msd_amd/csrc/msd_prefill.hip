@@ -302,16 +302,23 @@ __global__ __launch_bounds__(pf::THREADS, 1) void msd_gemm_kernel(
   static_assert(QW + SW <= WAVES, "one small copy per wave");
   static_assert(B_GROUP % 1024 == 0, "whole pieces");
 
-  // Two named buffers (not one array indexed by the parity of the group) so
-  // that the copies into one and the reads of the other are visibly disjoint.
+  // Named buffers (not one array indexed by the group) so that the copies
+  // into one and the reads of another are visibly disjoint.  128-column
+  // blocks have three (149 KB of LDS: the copies run two groups ahead),
+  // 256-column blocks two (a third would not fit).
+  constexpr int NBUF = BN == 128 ? 3 : 2;
   __shared__ __attribute__((aligned(16))) uint8_t sA0[A_GROUP];
   __shared__ __attribute__((aligned(16))) uint8_t sA1[A_GROUP];
+  __shared__ __attribute__((aligned(16))) uint8_t sA2[NBUF == 3 ? A_GROUP : 16];
   __shared__ __attribute__((aligned(16))) uint8_t sB0[B_GROUP];
   __shared__ __attribute__((aligned(16))) uint8_t sB1[B_GROUP];
+  __shared__ __attribute__((aligned(16))) uint8_t sB2[NBUF == 3 ? B_GROUP : 16];
   __shared__ __attribute__((aligned(16))) float sQ0[3 * BM];
   __shared__ __attribute__((aligned(16))) float sQ1[3 * BM];
+  __shared__ __attribute__((aligned(16))) float sQ2[NBUF == 3 ? 3 * BM : 4];
   __shared__ __attribute__((aligned(16))) uint16_t sS0[BN];
   __shared__ __attribute__((aligned(16))) uint16_t sS1[BN];
+  __shared__ __attribute__((aligned(16))) uint16_t sS2[NBUF == 3 ? BN : 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -456,23 +463,68 @@ __global__ __launch_bounds__(pf::THREADS, 1) void msd_gemm_kernel(
     epilogue(jl % MT, jl / MT, acc[jl & 1], q[jl % MT], sraw, g_);
   };
 
-  // Buffer 0 holds the even-indexed groups of the range, buffer 1 the odd
-  // ones.  While a group is computed from one buffer, the next group is
-  // copied into the other; each wave waits for its own copies, and the
-  // barrier then publishes all of them and frees the buffer just read.
-  dma(g_lo, sA0, sB0, sQ0, sS0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int g = g_lo; g < g_hi; g += 2) {
-    if (g + 1 < g_hi) dma(g + 1, sA1, sB1, sQ1, sS1);
-    compute(sA0, sB0, sQ0, sS0, g);
+  if constexpr (NBUF == 2) {
+    // Buffer 0 holds the even-indexed groups of the range, buffer 1 the odd
+    // ones.  While a group is computed from one buffer, the next group is
+    // copied into the other; each wave waits for its own copies, and the
+    // barrier then publishes all of them and frees the buffer just read.
+    dma(g_lo, sA0, sB0, sQ0, sS0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (g + 1 >= g_hi) break;
-    if (g + 2 < g_hi) dma(g + 2, sA0, sB0, sQ0, sS0);
-    compute(sA1, sB1, sQ1, sS1, g + 1);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    for (int g = g_lo; g < g_hi; g += 2) {
+      if (g + 1 < g_hi) dma(g + 1, sA1, sB1, sQ1, sS1);
+      compute(sA0, sB0, sQ0, sS0, g);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (g + 1 >= g_hi) break;
+      if (g + 2 < g_hi) dma(g + 2, sA0, sB0, sQ0, sS0);
+      compute(sA1, sB1, sQ1, sS1, g + 1);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+  } else {
+    // Group i of the range in buffer i % 3.  The step that computes group g
+    // first issues the copies of group g+2 (into the buffer group g-1 used,
+    // which every wave finished reading before the last barrier), then waits
+    // for its own copies of group g+1 only: a wave issues CPW pieces plus, in
+    // waves 0..QW+SW-1 (QW with Y_int), one small copy per group, and vector
+    // memory operations complete in order, so vmcnt(that count) leaves
+    // exactly group g+2's copies in flight.  The barrier is issued without a
+    // fence (a workgroup fence would wait for those copies too); the
+    // compiler-level memory barriers keep every LDS access on its side.
+    static_assert(PIECES == CPW * WAVES, "every wave issues CPW pieces");
+    const int ahead = CPW + (wave < QW + (YINT ? 0 : SW) ? 1 : 0);   // wave-uniform
+    auto end_step = [&](bool copies_ahead) {
+      // s_waitcnt immediates: vmcnt (bits 3:0) 7, 6 or 0, expcnt (6:4) 7 =
+      // no wait, lgkmcnt (11:8) 0
+      static_assert(CPW + 1 <= 15, "vmcnt immediate");
+      if (copies_ahead) {
+        if (ahead == CPW + 1) __builtin_amdgcn_s_waitcnt(0x0070 | (CPW + 1));
+        else __builtin_amdgcn_s_waitcnt(0x0070 | CPW);
+      } else {
+        __builtin_amdgcn_s_waitcnt(0x0070);
+      }
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+    dma(g_lo, sA0, sB0, sQ0, sS0);
+    asm volatile("" ::: "memory");
+    if (g_lo + 1 < g_hi) dma(g_lo + 1, sA1, sB1, sQ1, sS1);
+    end_step(g_lo + 1 < g_hi);
+    for (int g = g_lo; g < g_hi; g += 3) {
+      if (g + 2 < g_hi) dma(g + 2, sA2, sB2, sQ2, sS2);
+      compute(sA0, sB0, sQ0, sS0, g);
+      end_step(g + 2 < g_hi);
+      if (g + 1 >= g_hi) break;
+      if (g + 3 < g_hi) dma(g + 3, sA0, sB0, sQ0, sS0);
+      compute(sA1, sB1, sQ1, sS1, g + 1);
+      end_step(g + 3 < g_hi);
+      if (g + 2 >= g_hi) break;
+      if (g + 4 < g_hi) dma(g + 4, sA1, sB1, sQ1, sS1);
+      compute(sA2, sB2, sQ2, sS2, g + 2);
+      end_step(g + 4 < g_hi);
+    }
   }
 
   if constexpr (!YINT) {
