@@ -4,8 +4,10 @@
 One step = one call of the whole operator (steps 1-11: decomposition of x,
 integer contraction on MFMA, fp32 combine/accumulate, fp16 store) on one
 synthetic batch that is already resident in HBM, with the weights already in
-the library's tiled layout (converted once per weight, outside any timed
-region).  Steps cycle through enough distinct buffer sets (x, w, scale, y)
+the library's tiled layout and, where the group-size-128 prefill path runs,
+also in their operand form (FP6 MFMA operand tiles; both converted once per
+weight, outside any timed region).  Those workloads also report the step
+without the operand form ("without_operand_weights").  Steps cycle through enough distinct buffer sets (x, w, scale, y)
 that their footprint exceeds 512 MiB, twice the 256 MiB MALL, so every step
 streams its weights from HBM.  The K timed steps are captured once into a HIP
 graph; the headline replays it once between synchronizations.  The steps'
@@ -104,14 +106,15 @@ def prefill_splits(M, K, N):
     return -(-G // gps)
 
 
-def prefill_prep_bytes(M, K, N, gs):
+def prefill_prep_bytes(M, K, N, gs, operand_weights=False):
     """Algorithmic bytes of the prefill preparation kernel: it reads x and
     writes the level operand tiles (1536 bytes each: 16 rows x 128 k at group
     size 128, 32 rows x 64 k at group size 64) and the level weights (fp32,
     three per row and group); unless the GEMM converts the weights itself (group
-    size 64 with at most two 128-row blocks), it also reads the tiled int4
-    weights and writes their operand tiles (columns padded to the GEMM's
-    column block of 256, or 128 when 256 would give fewer than 256 tiles)."""
+    size 64 with at most two 128-row blocks) or reads the weights' operand form
+    (group size 128, operand_weights), it also reads the tiled int4 weights and
+    writes their operand tiles (columns padded to the GEMM's column block of
+    256, or 128 when 256 would give fewer than 256 tiles)."""
     G = K // gs
     per = 16 if gs == 128 else 32
     mpad = -(-M // 128) * 128
@@ -119,17 +122,23 @@ def prefill_prep_bytes(M, K, N, gs):
     bn = 256 if (not w_in_gemm and (mpad // 128) * -(-N // 256) >= 256) else 128
     npad = -(-N // bn) * bn
     b = 2 * M * K + 1536 * (3 * mpad // per) * G + 12 * mpad * G
-    if not w_in_gemm:
+    if not w_in_gemm and not (operand_weights and gs == 128):
         b += K * N // 2 + 1536 * (npad // per) * G
     return b
 
 
-def make_sets(torch, W, M, K, N, gs, nsets, seed, dist):
+def uses_operand_weights(path, gs):
+    """The weights' operand form is read by the group-128 prefill path only."""
+    return path == 2 and gs == 128
+
+
+def make_sets(torch, W, M, K, N, gs, nsets, seed, dist, operand_weights=False):
     """Seeded synthetic buffer sets with the workload's distributions, drawn on
     the GPU: x ~ N(0,1) (or U[-3,3]) fp16, int4 weights uniform over their
     range packed two per byte and then converted once into the library's
     tiled layout (outside any timed region, as a deployment converts its
-    static weights at load time), per-group scales uniform / lognormal fp16."""
+    static weights at load time), and with operand_weights also into their
+    operand form; per-group scales uniform / lognormal fp16."""
     gen = torch.Generator(device="cuda")
     sets = []
     G = K // gs
@@ -149,6 +158,7 @@ def make_sets(torch, W, M, K, N, gs, nsets, seed, dist):
         w_nd = (wu[:, 0::2] | (wu[:, 1::2] << 4)).to(torch.uint8).contiguous()
         w = W.wqbmm_a16w4_tile_weights(w_nd)
         del w_nd
+        w_op = W.wqbmm_a16w4_operand_weights(w, K) if operand_weights else None
         kind, p0, p1 = dist["scale"]
         if kind == "uniform":
             s = torch.rand((G, N), generator=gen, device="cuda") * (p1 - p0) + p0
@@ -156,7 +166,7 @@ def make_sets(torch, W, M, K, N, gs, nsets, seed, dist):
             s = torch.exp(torch.randn((G, N), generator=gen, device="cuda") * p1 + p0)
         s = s.to(torch.float16)
         y = torch.empty((M, N), dtype=torch.float16, device="cuda")
-        sets.append(dict(x=x, w=w, s=s, y=y))
+        sets.append(dict(x=x, w=w, o=w_op, s=s, y=y))
         del wv, wu
     return sets
 
@@ -307,25 +317,30 @@ def measure(torch, W, name, args, path_override=0):
     path = path_override or W.wqbmm_select_path(M, K, N, gs)
     dist = {"x": wl.x_dist, "w": (wl.w_low, wl.w_high), "scale": wl.scale_dist,
             "outlier_frac": wl.outlier_frac, "outlier_mult": wl.outlier_mult}
+    opw = uses_operand_weights(path, gs)
     nsets = max(2, min(256, math.ceil(MALL_COLD_BYTES / alg["bytes"])))
-    sets = make_sets(torch, W, M, K, N, gs, nsets, wl.seed, dist)
+    sets = make_sets(torch, W, M, K, N, gs, nsets, wl.seed, dist, operand_weights=opw)
     stream = torch.cuda.Stream()
     lib = W.lib()
     sptr = int(stream.cuda_stream)
-    print(f"[bench] {name}: M={M} K={K} N={N} gs={gs} path={path} sets={nsets}", file=sys.stderr, flush=True)
+    print(f"[bench] {name}: M={M} K={K} N={N} gs={gs} path={path} sets={nsets} operand_weights={opw}",
+          file=sys.stderr, flush=True)
 
-    def call(st):
+    def optr(st, use):
+        return st["o"].data_ptr() if use and st["o"] is not None else None
+
+    def call(st, use_op=True):
         def f():
-            rc = lib.wqbmm_a16w4_msd_path(st["x"].data_ptr(), st["w"].data_ptr(), st["s"].data_ptr(),
-                                          gs, M, K, N, st["y"].data_ptr(), path, sptr)
+            rc = lib.wqbmm_a16w4_msd_ex(st["x"].data_ptr(), st["w"].data_ptr(), optr(st, use_op),
+                                        st["s"].data_ptr(), gs, M, K, N, st["y"].data_ptr(), path, sptr)
             if rc:
-                raise W.WqbmmError(rc, "wqbmm_a16w4_msd_path")
+                raise W.WqbmmError(rc, "wqbmm_a16w4_msd_ex")
         return f
 
-    def stage(st, k):
+    def stage(st, k, use_op=True):
         def f():
             rc = lib.wqbmm_a16w4_msd_profile_stage(st["x"].data_ptr(), st["w"].data_ptr(),
-                                                   st["s"].data_ptr(), gs, M, K, N,
+                                                   optr(st, use_op), st["s"].data_ptr(), gs, M, K, N,
                                                    st["y"].data_ptr(), path, k, sptr)
             if rc:
                 raise W.WqbmmError(rc, "wqbmm_a16w4_msd_profile_stage")
@@ -349,6 +364,24 @@ def measure(torch, W, name, args, path_override=0):
     t = Timed(torch, stream, [stage(st, 2) for st in sets], steps, warmup)
     kern_ms, _ = t.replay_ms()
     del t
+    without = None
+    if opw:
+        # the same workload without the operand form: the preparation kernel
+        # converts the tiled weights on every call
+        t = Timed(torch, stream, [call(st, False) for st in sets], steps, warmup)
+        wo_ms, _ = t.replay_ms()
+        del t
+        t = Timed(torch, stream, [stage(st, 1, False) for st in sets], steps, warmup)
+        wo_prep_ms, _ = t.replay_ms()
+        del t
+        t = Timed(torch, stream, [stage(st, 2, False) for st in sets], steps, warmup)
+        wo_kern_ms, _ = t.replay_ms()
+        del t
+        without = {"ms_per_step": round(wo_ms, 6),
+                   "effective_TOPS": round(alg["eff_ops"] / (wo_ms * 1e-3) / 1e12, 3),
+                   "prep_avg_kernel_us": round(wo_prep_ms * 1e3, 3),
+                   "prep_algorithmic_bytes_per_launch": prefill_prep_bytes(M, K, N, gs),
+                   "main_avg_kernel_us": round(wo_kern_ms * 1e3, 3)}
 
     G = K // gs
     sha = kernel_sources_sha()
@@ -399,10 +432,14 @@ def measure(torch, W, name, args, path_override=0):
         extra["alu_view"] = {"bound": "alu", "ops_per_launch": combine_ops, "achieved": round(alu, 2),
                              "peak": round(VALU_F32_OPS_PEAK_T, 2), "unit": "T fp32 op/s",
                              "frac": round(alu / VALU_F32_OPS_PEAK_T, 4)}
-        prep_bytes = prefill_prep_bytes(M, K, N, gs)
+        prep_bytes = prefill_prep_bytes(M, K, N, gs, opw)
         extra["prep"] = {"kernel": prep_name, "avg_kernel_us": round(prep_ms * 1e3, 3),
                          "algorithmic_bytes_per_launch": prep_bytes,
                          "achieved_GBps": round(prep_bytes / (prep_ms * 1e-3) / 1e9, 1)}
+        if opw:
+            roof["operands"] = ("x level tiles MALL-resident, as the preparation kernel leaves them; "
+                                "weight tiles from the weights' operand form in HBM")
+            extra["without_operand_weights"] = without
     if isinstance(tinfo, dict):
         extra["traffic_detail"] = {k: tinfo[k] for k in tinfo if k not in ("kernel_sources_sha", "commands")}
     elif isinstance(tinfo, str):
@@ -411,6 +448,8 @@ def measure(torch, W, name, args, path_override=0):
     res = {
         "config": {"workload": f"{name}: M={M} K={K} N={N} group_size={gs}", "M": M, "K": K, "N": N,
                    "group_size": gs, "path": {1: "decode", 2: "prefill"}[path],
+                   "weights": ("tiled int4 + operand form (FP6), both converted once before timing"
+                               if opw else "tiled int4, converted once before timing"),
                    "buffer_sets": nsets, "footprint_MiB": round(nsets * alg["bytes"] / 2 ** 20, 1)},
         "ms_per_step": round(ev_ms, 6),
         "wall_ms_per_step": round(wall_ms, 6),
@@ -438,7 +477,8 @@ def sweep(torch, W, args):
     """Decode-vs-prefill split: the step time of each kernel path at
     M = 8..128 on the decode shape (K = N = 4096, group size 128) and the
     outlier shape (K = 8192, N = 28672, group size 64), MALL-cold as above,
-    with each path's kernels timed alone.  Returns a list of rows."""
+    with each path's kernels timed alone (the group-128 prefill path with the
+    weights' operand form).  Returns a list of rows."""
     from weight_only_quantized_msd_amd import datagen  # noqa: F401
     rows = []
     lib = W.lib()
@@ -447,7 +487,7 @@ def sweep(torch, W, args):
             alg = algorithmic(M, K, N, gs)
             nsets = max(2, min(64, math.ceil(MALL_COLD_BYTES / alg["bytes"])))
             dist = {"x": "normal", "w": (-8, 7), "scale": ("uniform", 0.005, 0.02)}
-            sets = make_sets(torch, W, M, K, N, gs, nsets, 7, dist)
+            sets = make_sets(torch, W, M, K, N, gs, nsets, 7, dist, operand_weights=gs == 128)
             stream = torch.cuda.Stream()
             sptr = int(stream.cuda_stream)
             for path in (1, 2):
@@ -460,12 +500,13 @@ def sweep(torch, W, args):
                     raise W.WqbmmError(rc, "sweep")
                 def call(st, k=0):
                     def f():
+                        op = st["o"].data_ptr() if st["o"] is not None else None
                         if k == 0:
-                            rc = lib.wqbmm_a16w4_msd_path(st["x"].data_ptr(), st["w"].data_ptr(),
-                                                          st["s"].data_ptr(), gs, M, K, N,
-                                                          st["y"].data_ptr(), path, sptr)
+                            rc = lib.wqbmm_a16w4_msd_ex(st["x"].data_ptr(), st["w"].data_ptr(), op,
+                                                        st["s"].data_ptr(), gs, M, K, N,
+                                                        st["y"].data_ptr(), path, sptr)
                         else:
-                            rc = lib.wqbmm_a16w4_msd_profile_stage(st["x"].data_ptr(), st["w"].data_ptr(),
+                            rc = lib.wqbmm_a16w4_msd_profile_stage(st["x"].data_ptr(), st["w"].data_ptr(), op,
                                                                    st["s"].data_ptr(), gs, M, K, N,
                                                                    st["y"].data_ptr(), path, k, sptr)
                         if rc:

@@ -134,6 +134,43 @@ wqbmm_status wqbmm_a16w4_msd_path(const void* x, const void* w_tiled,
                                   int path, void* stream);
 
 /*
+ * The weights' operand form: the FP6 (e2m3) MFMA operand tiles that the
+ * group-size-128 prefill GEMM contracts (each int4 weight halved, 6 bits;
+ * columns padded with zeros to a multiple of 256), converted ONCE from the
+ * tiled weights, like the tiled weights from the ND ones (the convert-once
+ * pattern of the aclnnCalculateMatmulWeightSizeV2 page's call example,
+ * section 调用示例).  Without it the prefill path's operand kernel converts
+ * the tiled weights again on every call (WQBMM-Exp page §6.1, UnfoldA); with
+ * it that kernel only decomposes x.  It costs 0.75 byte per weight (plus
+ * padding) beside the tiled weights' 0.5 and is optional: only the prefill
+ * path at group size 128 reads it.
+ * wqbmm_a16w4_operand_weight_bytes: its size in bytes,
+ *   (ceil(N/256)*256 / 32) * ceil(K/128) * 3072, or -1 if K or N breaks the
+ *   rules of wqbmm_a16w4_tiled_weight_bytes.  Pure host function.
+ * wqbmm_a16w4_operand_weights:
+ *   w_tiled    tiled weights for K x N (wqbmm_a16w4_tile_weights)
+ *   w_operand  wqbmm_a16w4_operand_weight_bytes(K, N) bytes, caller-allocated,
+ *              written completely
+ * Both pointers 16-byte aligned, not overlapping.
+ */
+int64_t wqbmm_a16w4_operand_weight_bytes(int64_t K, int64_t N);
+wqbmm_status wqbmm_a16w4_operand_weights(const void* w_tiled, int64_t K, int64_t N,
+                                         void* w_operand, void* stream);
+
+/*
+ * wqbmm_a16w4_msd_path with the weights' operand form as well.  w_operand is
+ * NULL (then this is wqbmm_a16w4_msd_path) or the output of
+ * wqbmm_a16w4_operand_weights for the same weights, K and N, 16-byte aligned
+ * (else WQBMM_ERR_INVALID); it is read only by the prefill path at group size
+ * 128, and the result is bit-identical to the call without it.  w_tiled is
+ * still required (the decode path and group size 64 read it).
+ */
+wqbmm_status wqbmm_a16w4_msd_ex(const void* x, const void* w_tiled, const void* w_operand,
+                                const void* antiquant_scale, int64_t group_size,
+                                int64_t M, int64_t K, int64_t N, void* y,
+                                int path, void* stream);
+
+/*
  * wqbmm_a16w4_msd without any device allocation, for callers that cannot
  * allocate device memory (code under graph capture, tight serving loops,
  * harnesses that forbid allocation).  Same operation, arguments, rules and
@@ -189,19 +226,22 @@ wqbmm_status wqbmm_a16w4_msd_yint(const void* x, const void* w_tiled,
  * wqbmm_a16w4_msd_path), so that its kernels can be timed separately.
  *   stage 1: the operand kernel only (WQBMM-Exp page §6.1 UnfoldA: x -> the
  *            three levels of §4.1 steps 1-8 and the rows' step-10 level
- *            weights; on the prefill path also w -> MFMA operand tiles), into
- *            this stream's workspace; y is not written.  The decode path at
+ *            weights; on the prefill path without w_operand also w -> MFMA
+ *            operand tiles), into this stream's workspace; y is not
+ *            written.  The decode path at
  *            M <= 4 is one fused kernel: nothing is launched.
  *   stage 2: the contraction kernel only (§4.1 steps 9-11) on the operands
  *            that the most recent call of the same path on the SAME stream
  *            prepared; y is written.  Returns WQBMM_ERR_INVALID if that call
- *            had another path, shape or group size (or none happened).  x is
- *            not re-read in this stage.  The decode path at M <= 4 runs its
- *            fused kernel (all of steps 1-11).
- * Arguments and rules as for wqbmm_a16w4_msd_path; other stage values give
+ *            had another path, shape or group size, or used w_operand where
+ *            this one does not or the other way round (or none happened).
+ *            x is not re-read in this stage.  The decode path at M <= 4 runs
+ *            its fused kernel (all of steps 1-11).
+ * Arguments and rules as for wqbmm_a16w4_msd_ex; other stage values give
  * WQBMM_ERR_INVALID.
  */
 wqbmm_status wqbmm_a16w4_msd_profile_stage(const void* x, const void* w_tiled,
+                                           const void* w_operand,
                                            const void* antiquant_scale, int64_t group_size,
                                            int64_t M, int64_t K, int64_t N, void* y,
                                            int path, int stage, void* stream);

@@ -149,10 +149,72 @@ def test_yint_validation(over, want):
     (dict(M=0, x=0, y=0), L.WQBMM_OK),
 ])
 def test_profile_stage_validation(over, want):
-    a = dict(x=FAKE, w=FAKE, s=FAKE, gs=64, M=2, K=256, N=64, y=FAKE, path=0, stage=1)
+    a = dict(x=FAKE, w=FAKE, o=None, s=FAKE, gs=64, M=2, K=256, N=64, y=FAKE, path=0, stage=1)
     a.update(over)
-    st = L.wqbmm_a16w4_msd_profile_stage_raw(a["x"], a["w"], a["s"], a["gs"], a["M"], a["K"],
+    st = L.wqbmm_a16w4_msd_profile_stage_raw(a["x"], a["w"], a["o"], a["s"], a["gs"], a["M"], a["K"],
                                              a["N"], a["y"], a["path"], a["stage"], None)
+    assert st == want
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(o=MIS), L.WQBMM_ERR_INVALID),              # a misaligned operand form
+    (dict(o=MIS, stage=2), L.WQBMM_ERR_INVALID),
+    (dict(o=FAKE, M=0), L.WQBMM_OK),
+    (dict(o=MIS, M=0), L.WQBMM_ERR_INVALID),         # checked even for an empty batch
+])
+def test_profile_stage_operand_validation(over, want):
+    a = dict(x=FAKE, w=FAKE, o=None, s=FAKE, gs=128, M=2, K=256, N=64, y=FAKE, path=2, stage=1)
+    a.update(over)
+    st = L.wqbmm_a16w4_msd_profile_stage_raw(a["x"], a["w"], a["o"], a["s"], a["gs"], a["M"], a["K"],
+                                             a["N"], a["y"], a["path"], a["stage"], None)
+    assert st == want
+
+
+EX_CASES = MSD_CASES + [
+    ("misaligned operand form", dict(o=MIS), L.WQBMM_ERR_INVALID),
+    ("operand form, empty batch", dict(o=FAKE, M=0), L.WQBMM_OK),
+    ("misaligned operand form, empty batch", dict(o=MIS, M=0), L.WQBMM_ERR_INVALID),
+    ("operand form does not replace w", dict(o=FAKE, w=0), L.WQBMM_ERR_NULLPTR),
+    ("null beats a misaligned operand form", dict(o=MIS, x=0), L.WQBMM_ERR_NULLPTR),
+    ("bad shape beats a misaligned operand form", dict(o=MIS, K=200), L.WQBMM_ERR_INVALID),
+]
+
+
+@pytest.mark.parametrize("name,over,want", EX_CASES, ids=[c[0] for c in EX_CASES])
+def test_msd_ex_validation(name, over, want):
+    a = dict(OK_ARGS, o=None, path=0)
+    a.update(over)
+    st = L.wqbmm_a16w4_msd_ex_raw(a["x"], a["w"], a["o"], a["s"], a["gs"], a["M"], a["K"], a["N"],
+                                  a["y"], a["path"], None)
+    assert st == want, (name, L.status_string(st))
+
+
+@pytest.mark.parametrize("K,N,want", [
+    (4096, 4096, (4096 // 32) * 32 * 3072),    # 1.5x the int4 bytes: 6 bits per weight
+    (4096, 4128, (4352 // 32) * 32 * 3072),    # columns padded to a multiple of 256
+    (8192, 28672, (28672 // 32) * 64 * 3072),
+    (192, 64, (256 // 32) * 2 * 3072),         # rows padded to 256
+    (1, 32, (256 // 32) * 1 * 3072),
+    (0, 64, -1), (64, 0, -1), (64, 48, -1),    # the tiled weights' shape rules
+    ((1 << 20) + 1, 64, -1), (64, (1 << 20) + 32, -1),
+])
+def test_operand_weight_bytes(K, N, want):
+    assert L.wqbmm_a16w4_operand_weight_bytes(K, N) == want
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(t=0), L.WQBMM_ERR_NULLPTR),
+    (dict(o=0), L.WQBMM_ERR_NULLPTR),
+    (dict(o=0, K=0), L.WQBMM_ERR_NULLPTR),
+    (dict(K=0), L.WQBMM_ERR_INVALID),
+    (dict(N=48), L.WQBMM_ERR_INVALID),
+    (dict(t=MIS), L.WQBMM_ERR_INVALID),
+    (dict(o=MIS), L.WQBMM_ERR_INVALID),
+])
+def test_operand_weights_validation(over, want):
+    a = dict(t=FAKE, K=256, N=64, o=FAKE)
+    a.update(over)
+    st = L.wqbmm_a16w4_operand_weights_raw(a["t"], a["K"], a["N"], a["o"], None)
     assert st == want
 
 

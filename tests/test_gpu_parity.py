@@ -464,6 +464,75 @@ def test_side_stream_and_alternating_shapes(torch_dev):
             assert torch.equal(y_side.view(torch.int16), ref.view(torch.int16)), name
 
 
+# The weights' operand form (wqbmm_a16w4_operand_weights): the group-128
+# prefill GEMM then reads its weight tiles from it instead of from the
+# preparation kernel.  Both GEMM column-block widths (256 at M = 2048; 128
+# with a K-split at M = 256 and at the ragged shapes), columns padded to the
+# 128-wide block inside the 256-padded form (N = 4128, N = 96), an odd count
+# of 128-row blocks (K = 384), and calls where the form is not read (decode
+# path, group size 64).  y must equal the call without the form bit for bit.
+OPW_CASES = [  # (name or None, M, K, N, gs, path)
+    ("prefill_m2048", None, None, None, None, PREFILL),
+    ("mid_m256", None, None, None, None, PREFILL),
+    (None, 200, 1024, 4128, 128, PREFILL),
+    (None, 130, 384, 96, 128, PREFILL),
+    (None, 65, 512, 160, 128, AUTO),
+    (None, 300, 2048, 2080, 128, PREFILL),
+    ("decode_m16", None, None, None, None, AUTO),
+    ("outlier_m128", None, None, None, None, PREFILL),
+]
+
+
+@pytest.mark.parametrize("case", OPW_CASES,
+                         ids=[c[0] or f"M{c[1]}K{c[2]}N{c[3]}g{c[4]}" for c in OPW_CASES])
+def test_operand_weights_bit_identical(torch_dev, case):
+    import weight_only_quantized_msd_amd as W
+    torch = torch_dev
+    name, M, K, N, gs, path = case
+    d = workload(name) if name else datagen.random_case(M, K, N, gs, seed=M + K + N)
+    M, K, N, gs = d["M"], d["K"], d["N"], d["group_size"]
+    x, w, s = to_dev(torch, d)
+    announce(f"operand weights M={M} K={K} N={N} gs={gs} path={path}")
+    w_op = W.wqbmm_a16w4_operand_weights(w, K)
+    assert w_op.numel() == -(-N // 256) * 8 * -(-K // 128) * 3072
+    ref = W.wqbmm_a16w4_msd_path(x, w, s, gs, path)
+    got = W.wqbmm_a16w4_msd_path(x, w, s, gs, path, w_operand=w_op)
+    again = W.wqbmm_a16w4_msd_path(x, w, s, gs, path, w_operand=w_op)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+    assert torch.equal(again.view(torch.int16), ref.view(torch.int16))
+    rows = sample_rows(M, 24, 5)
+    y32, _ = oracle.matmul(d["x"], d["w_packed"], d["scale"], gs, rows=rows)
+    check_y(got.cpu().numpy()[rows], y32, "with the operand form")
+    check_y_elementwise(got.cpu().numpy()[rows], y32, elementwise_bound(d, rows), "with the operand form")
+
+
+def test_operand_weights_stages(torch_dev):
+    """Stages with the operand form compose to the one-call result; stage 2
+    refuses operands that a stage 1 prepared with the form when it is called
+    without it (the weight tiles were not written), and the other way round."""
+    import weight_only_quantized_msd_amd as W
+    torch = torch_dev
+    d = workload("mid_m256")
+    gs = d["group_size"]
+    x, w, s = to_dev(torch, d)
+    announce("operand weights stages mid_m256")
+    w_op = W.wqbmm_a16w4_operand_weights(w, d["K"])
+    y1 = W.wqbmm_a16w4_msd_path(x, w, s, gs, PREFILL, w_operand=w_op)
+    W.wqbmm_a16w4_msd_profile_stage(x, w, s, gs, 1, path=PREFILL, w_operand=w_op)
+    y2 = W.wqbmm_a16w4_msd_profile_stage(x, w, s, gs, 2, path=PREFILL, w_operand=w_op)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    with pytest.raises(W.WqbmmError):
+        W.wqbmm_a16w4_msd_profile_stage(x, w, s, gs, 2, path=PREFILL)
+    W.wqbmm_a16w4_msd_profile_stage(x, w, s, gs, 1, path=PREFILL)
+    with pytest.raises(W.WqbmmError):
+        W.wqbmm_a16w4_msd_profile_stage(x, w, s, gs, 2, path=PREFILL, w_operand=w_op)
+    y3 = W.wqbmm_a16w4_msd_profile_stage(x, w, s, gs, 2, path=PREFILL)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y3.view(torch.int16))
+
+
 @pytest.mark.parametrize("name,path", [("decode_m16", PREFILL), ("prefill_m2048", PREFILL),
                                        ("outlier_m128", PREFILL), ("decode_m16", DECODE),
                                        ("ffn_up_m16", DECODE), ("decode_m1", DECODE)])
@@ -495,28 +564,31 @@ def test_profile_stages_compose_to_path(torch_dev, name, path):
             W.wqbmm_a16w4_msd_profile_stage(x, w, s, gs, 2, path=path)
 
 
-@pytest.mark.parametrize("name,path", [("decode_m16", DECODE), ("ffn_up_m16", DECODE),
-                                       ("tiny", PREFILL), ("outlier_m128", PREFILL)])
-def test_graph_replay_matches_eager(torch_dev, name, path):
+@pytest.mark.parametrize("name,path,opw", [("decode_m16", DECODE, False), ("ffn_up_m16", DECODE, False),
+                                           ("tiny", PREFILL, False), ("outlier_m128", PREFILL, False),
+                                           ("mid_m256", PREFILL, True)])
+def test_graph_replay_matches_eager(torch_dev, name, path, opw):
     """bench.py submits its timed steps as a captured graph: every replay, with
     eager work and synchronizations in between, must reproduce the eager bits
-    (the split-K counters re-arm inside the graph; no memset nodes)."""
+    (the split-K counters re-arm inside the graph; no memset nodes).  With
+    opw the captured call reads the weights' operand form."""
     import weight_only_quantized_msd_amd as W
     torch = torch_dev
     d = workload(name)
     gs = d["group_size"]
     x, w, s = to_dev(torch, d)
-    announce(f"graph {name} path={path}")
+    w_op = W.wqbmm_a16w4_operand_weights(w, d["K"]) if opw else None
+    announce(f"graph {name} path={path} operand form={opw}")
     ref = W.wqbmm_a16w4_msd_path(x, w, s, gs, path)
     torch.cuda.synchronize()
     side = torch.cuda.Stream()
     y = torch.empty_like(ref)
     with torch.cuda.stream(side):
-        W.wqbmm_a16w4_msd_path(x, w, s, gs, path, y=y, stream=side)   # warm this stream
+        W.wqbmm_a16w4_msd_path(x, w, s, gs, path, y=y, stream=side, w_operand=w_op)   # warm this stream
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=side, capture_error_mode="relaxed"):
-        W.wqbmm_a16w4_msd_path(x, w, s, gs, path, y=y, stream=side)
+        W.wqbmm_a16w4_msd_path(x, w, s, gs, path, y=y, stream=side, w_operand=w_op)
     for rep in range(4):
         y.fill_(7.0)
         other = W.wqbmm_a16w4_msd_path(x, w, s, gs, path)    # eager work in between

@@ -3,10 +3,15 @@
     w_tiled = wqbmm_a16w4_tile_weights(w_nd)          # once per weight
     y = wqbmm_a16w4_msd(x, w_tiled, antiquant_scale, group_size)
 
+    w_op = wqbmm_a16w4_operand_weights(w_tiled, K)    # optional, once per weight
+    y = wqbmm_a16w4_msd(x, w_tiled, antiquant_scale, group_size, w_operand=w_op)
+
 x: fp16 [M][K]; w_nd: uint8 [K][N/2] (two int4 per byte, column 2j in the low
 nibble), converted once on the device into the library's tiled layout
 (uint8 [N/16][ceil(K/128)*1024]); antiquant_scale: fp16 [K/group_size][N];
-y: fp16 [M][N].
+y: fp16 [M][N].  The optional operand form of the weights (FP6 MFMA operand
+tiles, 0.75 byte per weight) spares the group-size-128 prefill path its
+per-call weight conversion; results are bit-identical with or without it.
 
 The method is the multi-step decomposition (MSD) of the page
 "WeightQuantBatchMatmulExperiment 算子深度解析：A16W4 PerGroup 伪量化 MatMul 的
@@ -24,7 +29,8 @@ from ._lib import (WQBMM_ERR_ALLOC, WQBMM_ERR_CAPTURE, WQBMM_ERR_INVALID,  # noq
                    status_string, wqbmm_select_path, wqbmm_version)
 
 __all__ = [
-    "wqbmm_a16w4_tile_weights", "wqbmm_a16w4_msd", "wqbmm_a16w4_msd_path", "wqbmm_a16w4_msd_noalloc",
+    "wqbmm_a16w4_tile_weights", "wqbmm_a16w4_operand_weights", "wqbmm_a16w4_msd",
+    "wqbmm_a16w4_msd_path", "wqbmm_a16w4_msd_noalloc",
     "wqbmm_a16w4_msd_prepass",
     "wqbmm_a16w4_msd_yint", "wqbmm_a16w4_msd_profile_stage", "wqbmm_select_path", "wqbmm_status_string", "wqbmm_version",
     "WqbmmError",
@@ -74,6 +80,32 @@ def wqbmm_a16w4_tile_weights(w_nd, stream=None):
     return w_tiled
 
 
+def wqbmm_a16w4_operand_weights(w_tiled, K: int, stream=None):
+    """One-time conversion of tiled weights (for K rows) into their operand
+    form for the group-size-128 prefill GEMM; returns uint8
+    [wqbmm_a16w4_operand_weight_bytes(K, N)]."""
+    import torch
+    N = _weight_n(w_tiled, K)
+    nbytes = lib().wqbmm_a16w4_operand_weight_bytes(K, N)
+    if nbytes < 0:
+        check(WQBMM_ERR_INVALID, "wqbmm_a16w4_operand_weight_bytes")
+    w_op = torch.empty(nbytes, dtype=torch.uint8, device=w_tiled.device)
+    st = lib().wqbmm_a16w4_operand_weights(w_tiled.data_ptr(), K, N, w_op.data_ptr(),
+                                           _stream_ptr(stream))
+    check(st, "wqbmm_a16w4_operand_weights")
+    return w_op
+
+
+def _operand_ptr(w_operand, K, N):
+    import torch
+    if w_operand is None:
+        return None
+    _require(w_operand, torch.uint8, 1, "w_operand")
+    if w_operand.numel() != lib().wqbmm_a16w4_operand_weight_bytes(K, N):
+        raise ValueError("w_operand must be the wqbmm_a16w4_operand_weights output for this K and N")
+    return w_operand.data_ptr()
+
+
 def _weight_n(w_tiled, K):
     import torch
     _require(w_tiled, torch.uint8, 2, "w_tiled")
@@ -84,7 +116,7 @@ def _weight_n(w_tiled, K):
 
 
 def wqbmm_a16w4_msd_path(x, w_tiled, antiquant_scale, group_size: int, path: int,
-                         y=None, stream=None):
+                         y=None, stream=None, w_operand=None):
     import torch
     _require(x, torch.float16, 2, "x")
     _require(antiquant_scale, torch.float16, 2, "antiquant_scale")
@@ -99,17 +131,20 @@ def wqbmm_a16w4_msd_path(x, w_tiled, antiquant_scale, group_size: int, path: int
         _require(y, torch.float16, 2, "y")
         if tuple(y.shape) != (M, N):
             raise ValueError("y must be [M][N]")
-    st = lib().wqbmm_a16w4_msd_path(x.data_ptr(), w_tiled.data_ptr(),
-                                    antiquant_scale.data_ptr(), int(group_size), M, K, N,
-                                    y.data_ptr(), int(path), _stream_ptr(stream))
+    st = lib().wqbmm_a16w4_msd_ex(x.data_ptr(), w_tiled.data_ptr(), _operand_ptr(w_operand, K, N),
+                                  antiquant_scale.data_ptr(), int(group_size), M, K, N,
+                                  y.data_ptr(), int(path), _stream_ptr(stream))
     check(st, "wqbmm_a16w4_msd")
     return y
 
 
-def wqbmm_a16w4_msd(x, w_tiled, antiquant_scale, group_size: int, y=None, stream=None):
-    """The operator; returns y (fp16 [M][N]).  Asynchronous on the current stream."""
+def wqbmm_a16w4_msd(x, w_tiled, antiquant_scale, group_size: int, y=None, stream=None,
+                    w_operand=None):
+    """The operator; returns y (fp16 [M][N]).  Asynchronous on the current
+    stream.  w_operand: the weights' optional operand form
+    (wqbmm_a16w4_operand_weights)."""
     return wqbmm_a16w4_msd_path(x, w_tiled, antiquant_scale, group_size,
-                                WQBMM_PATH_AUTO, y=y, stream=stream)
+                                WQBMM_PATH_AUTO, y=y, stream=stream, w_operand=w_operand)
 
 
 def wqbmm_a16w4_msd_noalloc(x, w_tiled, antiquant_scale, group_size: int, y, stream=None):
@@ -160,7 +195,7 @@ def wqbmm_a16w4_msd_yint(x, w_tiled, group_size: int, g_begin: int, g_end: int,
 
 
 def wqbmm_a16w4_msd_profile_stage(x, w_tiled, antiquant_scale, group_size: int,
-                                  stage: int, path: int = 0, y=None, stream=None):
+                                  stage: int, path: int = 0, y=None, stream=None, w_operand=None):
     """Run one stage of a kernel path (1: operand kernel, 2: contraction on the
     operands the last call of that path on this stream prepared); returns y."""
     import torch
@@ -171,6 +206,7 @@ def wqbmm_a16w4_msd_profile_stage(x, w_tiled, antiquant_scale, group_size: int,
     if y is None:
         y = torch.empty((M, N), dtype=torch.float16, device=x.device)
     st = lib().wqbmm_a16w4_msd_profile_stage(x.data_ptr(), w_tiled.data_ptr(),
+                                             _operand_ptr(w_operand, K, N),
                                              antiquant_scale.data_ptr(), int(group_size), M, K, N,
                                              y.data_ptr(), int(path), int(stage), _stream_ptr(stream))
     check(st, "wqbmm_a16w4_msd_profile_stage")

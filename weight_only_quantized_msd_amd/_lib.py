@@ -40,10 +40,13 @@ SIGNATURES = {
     "wqbmm_a16w4_tile_weights": (_int, [_p, _i64, _i64, _p, _p]),
     "wqbmm_a16w4_msd": (_int, [_p, _p, _p, _i64, _i64, _i64, _i64, _p, _p]),
     "wqbmm_a16w4_msd_path": (_int, [_p, _p, _p, _i64, _i64, _i64, _i64, _p, _int, _p]),
+    "wqbmm_a16w4_operand_weight_bytes": (_i64, [_i64, _i64]),
+    "wqbmm_a16w4_operand_weights": (_int, [_p, _i64, _i64, _p, _p]),
+    "wqbmm_a16w4_msd_ex": (_int, [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _p, _int, _p]),
     "wqbmm_a16w4_msd_noalloc": (_int, [_p, _p, _p, _i64, _i64, _i64, _i64, _p, _p]),
     "wqbmm_a16w4_msd_prepass": (_int, [_p, _i64, _i64, _i64, _p, _p, _p]),
     "wqbmm_a16w4_msd_yint": (_int, [_p, _p, _i64, _i64, _i64, _i64, _i64, _i64, _p, _int, _p]),
-    "wqbmm_a16w4_msd_profile_stage": (_int, [_p, _p, _p, _i64, _i64, _i64, _i64, _p, _int, _int, _p]),
+    "wqbmm_a16w4_msd_profile_stage": (_int, [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _p, _int, _int, _p]),
     "wqbmm_select_path": (_int, [_i64, _i64, _i64, _i64]),
     "wqbmm_status_string": (ctypes.c_char_p, [_int]),
     "wqbmm_version": (_int, []),
@@ -114,6 +117,18 @@ def wqbmm_a16w4_msd_path_raw(x, w, scale, group_size, M, K, N, y, path, stream) 
     return lib().wqbmm_a16w4_msd_path(x, w, scale, group_size, M, K, N, y, path, stream)
 
 
+def wqbmm_a16w4_operand_weight_bytes(K, N) -> int:
+    return lib().wqbmm_a16w4_operand_weight_bytes(K, N)
+
+
+def wqbmm_a16w4_operand_weights_raw(w_tiled, K, N, w_operand, stream) -> int:
+    return lib().wqbmm_a16w4_operand_weights(w_tiled, K, N, w_operand, stream)
+
+
+def wqbmm_a16w4_msd_ex_raw(x, w, w_operand, scale, group_size, M, K, N, y, path, stream) -> int:
+    return lib().wqbmm_a16w4_msd_ex(x, w, w_operand, scale, group_size, M, K, N, y, path, stream)
+
+
 def wqbmm_a16w4_msd_noalloc_raw(x, w, scale, group_size, M, K, N, y, stream) -> int:
     return lib().wqbmm_a16w4_msd_noalloc(x, w, scale, group_size, M, K, N, y, stream)
 
@@ -126,8 +141,10 @@ def wqbmm_a16w4_msd_yint_raw(x, w, group_size, M, K, N, g_begin, g_end, y_int, p
     return lib().wqbmm_a16w4_msd_yint(x, w, group_size, M, K, N, g_begin, g_end, y_int, path, stream)
 
 
-def wqbmm_a16w4_msd_profile_stage_raw(x, w, scale, group_size, M, K, N, y, path, stage, stream) -> int:
-    return lib().wqbmm_a16w4_msd_profile_stage(x, w, scale, group_size, M, K, N, y, path, stage, stream)
+def wqbmm_a16w4_msd_profile_stage_raw(x, w, w_operand, scale, group_size, M, K, N, y, path, stage,
+                                      stream) -> int:
+    return lib().wqbmm_a16w4_msd_profile_stage(x, w, w_operand, scale, group_size, M, K, N, y, path,
+                                               stage, stream)
 
 
 def wqbmm_probe_stream_read_raw(src, nbytes, sink, stream) -> int:

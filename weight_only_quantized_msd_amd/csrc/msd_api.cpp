@@ -90,13 +90,19 @@ struct Needs {
   size_t ops = 0;
 };
 
-size_t prefill_ops_bytes(const wqbmm::PrefillLayout& L) {
-  return round_up(L.a_bytes, 256) + round_up(L.q_bytes, 256) + round_up(L.b_bytes, 256) +
-         round_up(L.part_bytes, 256);
+// The group-128 prefill path reads the weights' operand form instead of
+// converting the tiled weights when the caller passes it.
+bool uses_operand_weights(int path, int64_t gs, const void* w_op) {
+  return w_op != nullptr && path == WQBMM_PATH_PREFILL && gs == 128;
+}
+
+size_t prefill_ops_bytes(const wqbmm::PrefillLayout& L, bool own_weight_tiles) {
+  return round_up(L.a_bytes, 256) + round_up(L.q_bytes, 256) +
+         (own_weight_tiles ? round_up(L.b_bytes, 256) : 0) + round_up(L.part_bytes, 256);
 }
 
 Needs needs_of(int path, int64_t gs, int64_t M, int64_t K, int64_t N, int64_t g_begin, int64_t g_end,
-               bool yint) {
+               bool yint, bool operand_weights) {
   Needs n;
   if (path == WQBMM_PATH_DECODE) {
     if (M > 4) {
@@ -105,7 +111,7 @@ Needs needs_of(int path, int64_t gs, int64_t M, int64_t K, int64_t N, int64_t g_
       n.acc = wqbmm::decode_accum_bytes(wqbmm::decode_plan((int)gs, M, K, N, g_begin, g_end), M, N);
     }
   } else {
-    n.ops = prefill_ops_bytes(wqbmm::prefill_layout((int)gs, M, K, N));
+    n.ops = prefill_ops_bytes(wqbmm::prefill_layout((int)gs, M, K, N), !operand_weights);
   }
   n.acc = round_up(n.acc, 256);
   n.ops = round_up(n.ops, 256);
@@ -142,6 +148,7 @@ struct Workspace {
   // (prep_path 0: none, WQBMM_PATH_DECODE or WQBMM_PATH_PREFILL)
   int prep_path = 0;
   int64_t prep_gs = 0, prep_m = -1, prep_k = 0, prep_n = 0;
+  bool prep_opw = false;
 };
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 std::vector<void*> g_retired;
@@ -235,16 +242,19 @@ int resolve_path(int path, int64_t M, int64_t K, int64_t N, int64_t gs) {
 wqbmm_status launch_status(hipError_t e) { return e == hipSuccess ? WQBMM_OK : WQBMM_ERR_LAUNCH; }
 
 // Records (stage 0 or 1) or checks (stage 2) which path and shape the
-// operands in the ops region of (dev, stream) belong to.
+// operands in the ops region of (dev, stream) belong to, and whether the
+// weights' operand form stood in for the weight tiles.
 wqbmm_status track_operands(int dev, hipStream_t stream, int path, int stage, int64_t gs, int64_t M,
-                            int64_t K, int64_t N) {
+                            int64_t K, int64_t N, bool opw) {
   std::lock_guard<std::mutex> lk(g_mu);
   Workspace& ws = g_ws[std::make_pair(dev, stream)];
   if (stage == 2)
-    return (ws.prep_path == path && ws.prep_gs == gs && ws.prep_m == M && ws.prep_k == K && ws.prep_n == N)
+    return (ws.prep_path == path && ws.prep_gs == gs && ws.prep_m == M && ws.prep_k == K &&
+            ws.prep_n == N && ws.prep_opw == opw)
                ? WQBMM_OK : WQBMM_ERR_INVALID;
   ws.prep_path = path;
   ws.prep_gs = gs; ws.prep_m = M; ws.prep_k = K; ws.prep_n = N;
+  ws.prep_opw = opw;
   return WQBMM_OK;
 }
 
@@ -264,48 +274,55 @@ wqbmm_status run_decode(const Buffers& b, const void* x, const void* w, const vo
 }
 
 // The prefill path.  stage 0: both kernels; 1: preparation only; 2: GEMM only.
-wqbmm_status run_prefill(const Buffers& b, const void* x, const void* w, const void* scale, int64_t gs,
-                         int64_t M, int64_t K, int64_t N, int64_t g_begin, int64_t g_end, void* y,
-                         int32_t* y_int, int stage, hipStream_t stream) {
+// With the weights' operand form (w_op, group size 128) the GEMM reads its
+// weight tiles there and the preparation kernel converts only x.
+wqbmm_status run_prefill(const Buffers& b, const void* x, const void* w, const void* w_op,
+                         const void* scale, int64_t gs, int64_t M, int64_t K, int64_t N,
+                         int64_t g_begin, int64_t g_end, void* y, int32_t* y_int, int stage,
+                         hipStream_t stream) {
   const wqbmm::PrefillLayout L = wqbmm::prefill_layout((int)gs, M, K, N);
+  const bool opw = uses_operand_weights(WQBMM_PATH_PREFILL, gs, w_op);
   uint8_t* a_t = b.ops;
   float* q_t = reinterpret_cast<float*>(b.ops + round_up(L.a_bytes, 256));
-  uint8_t* b_t = b.ops + round_up(L.a_bytes, 256) + round_up(L.q_bytes, 256);
-  float* part = reinterpret_cast<float*>(b_t + round_up(L.b_bytes, 256));
+  uint8_t* own_b = b.ops + round_up(L.a_bytes, 256) + round_up(L.q_bytes, 256);
+  float* part = reinterpret_cast<float*>(own_b + (opw ? 0 : round_up(L.b_bytes, 256)));
+  uint8_t* b_t = opw ? static_cast<uint8_t*>(const_cast<void*>(w_op)) : own_b;
   if (stage != 2) {
-    const wqbmm_status st =
-        launch_status(wqbmm::launch_prefill_prep(x, w, (int)gs, M, K, N, L, a_t, q_t, b_t, stream));
+    const wqbmm_status st = launch_status(
+        wqbmm::launch_prefill_prep(x, w, (int)gs, M, K, N, L, a_t, q_t, b_t, !opw, stream));
     if (st != WQBMM_OK || stage == 1) return st;
   }
   return launch_status(wqbmm::launch_prefill_gemm(a_t, q_t, b_t, w, scale, (int)gs, M, K, N, L,
                                                   g_begin, g_end, y, y_int, part, stream));
 }
 
-wqbmm_status run_path(const Buffers& b, int path, const void* x, const void* w, const void* scale,
-                      int64_t gs, int64_t M, int64_t K, int64_t N, int64_t g_begin, int64_t g_end,
-                      void* y, int32_t* y_int, int stage, hipStream_t stream) {
+wqbmm_status run_path(const Buffers& b, int path, const void* x, const void* w, const void* w_op,
+                      const void* scale, int64_t gs, int64_t M, int64_t K, int64_t N,
+                      int64_t g_begin, int64_t g_end, void* y, int32_t* y_int, int stage,
+                      hipStream_t stream) {
   if (path == WQBMM_PATH_DECODE)
     return run_decode(b, x, w, scale, gs, M, K, N, g_begin, g_end, y, y_int, stage, stream);
-  return run_prefill(b, x, w, scale, gs, M, K, N, g_begin, g_end, y, y_int, stage, stream);
+  return run_prefill(b, x, w, w_op, scale, gs, M, K, N, g_begin, g_end, y, y_int, stage, stream);
 }
 
 // Steps 1-11 (or 1-9 with y_int) on one of the two kernel paths, with this
 // stream's workspace.  Stages as in wqbmm_a16w4_msd_profile_stage (0: all).
-wqbmm_status run(const void* x, const void* w, const void* scale, int64_t gs, int64_t M,
-                 int64_t K, int64_t N, int64_t g_begin, int64_t g_end, void* y, int32_t* y_int,
-                 int path, int stage, hipStream_t stream) {
+wqbmm_status run(const void* x, const void* w, const void* w_op, const void* scale, int64_t gs,
+                 int64_t M, int64_t K, int64_t N, int64_t g_begin, int64_t g_end, void* y,
+                 int32_t* y_int, int path, int stage, hipStream_t stream) {
   int dev = -1;
   wqbmm_status st = check_device(&dev);
   if (st != WQBMM_OK) return st;
+  const bool opw = uses_operand_weights(path, gs, w_op);
   Buffers b;
-  st = get_workspace(dev, stream, needs_of(path, gs, M, K, N, g_begin, g_end, y_int != nullptr), &b);
+  st = get_workspace(dev, stream, needs_of(path, gs, M, K, N, g_begin, g_end, y_int != nullptr, opw), &b);
   if (st != WQBMM_OK) return st;
   const bool two_kernels = path == WQBMM_PATH_PREFILL || M > 4;
   if (two_kernels) {
-    st = track_operands(dev, stream, path, stage, gs, M, K, N);
+    st = track_operands(dev, stream, path, stage, gs, M, K, N, opw);
     if (st != WQBMM_OK) return st;
   }
-  return run_path(b, path, x, w, scale, gs, M, K, N, g_begin, g_end, y, y_int, stage, stream);
+  return run_path(b, path, x, w, w_op, scale, gs, M, K, N, g_begin, g_end, y, y_int, stage, stream);
 }
 
 }  // namespace
@@ -395,14 +412,40 @@ wqbmm_status validate_call(const void* x, const void* w_tiled, const void* scale
 
 extern "C" {
 
+wqbmm_status wqbmm_a16w4_msd_ex(const void* x, const void* w_tiled, const void* w_operand,
+                                const void* antiquant_scale, int64_t group_size, int64_t M,
+                                int64_t K, int64_t N, void* y, int path, void* stream) {
+  int p = 0;
+  const wqbmm_status st = validate_call(x, w_tiled, antiquant_scale, true, y, group_size, M, K, N, path, &p);
+  if (st != WQBMM_OK) return st;
+  if (!aligned16(w_operand)) return WQBMM_ERR_INVALID;
+  if (M == 0) return WQBMM_OK;
+  return run(x, w_tiled, w_operand, antiquant_scale, group_size, M, K, N, 0, K / group_size, y,
+             nullptr, p, 0, static_cast<hipStream_t>(stream));
+}
+
 wqbmm_status wqbmm_a16w4_msd_path(const void* x, const void* w_tiled,
                                   const void* antiquant_scale, int64_t group_size, int64_t M,
                                   int64_t K, int64_t N, void* y, int path, void* stream) {
-  int p = 0;
-  const wqbmm_status st = validate_call(x, w_tiled, antiquant_scale, true, y, group_size, M, K, N, path, &p);
-  if (st != WQBMM_OK || M == 0) return st;
-  return run(x, w_tiled, antiquant_scale, group_size, M, K, N, 0, K / group_size, y, nullptr, p, 0,
-             static_cast<hipStream_t>(stream));
+  return wqbmm_a16w4_msd_ex(x, w_tiled, nullptr, antiquant_scale, group_size, M, K, N, y, path,
+                            stream);
+}
+
+int64_t wqbmm_a16w4_operand_weight_bytes(int64_t K, int64_t N) {
+  if (K <= 0 || N <= 0 || K > kMaxK || N > kMaxN || N % 32 != 0) return -1;
+  return (int64_t)wqbmm::operand_weight_bytes(K, N);
+}
+
+wqbmm_status wqbmm_a16w4_operand_weights(const void* w_tiled, int64_t K, int64_t N, void* w_operand,
+                                         void* stream) {
+  if (!w_tiled || !w_operand) return WQBMM_ERR_NULLPTR;
+  if (K <= 0 || N <= 0 || K > kMaxK || N > kMaxN || N % 32 != 0) return WQBMM_ERR_INVALID;
+  if (!aligned16(w_tiled) || !aligned16(w_operand)) return WQBMM_ERR_INVALID;
+  int dev = -1;
+  wqbmm_status st = check_device(&dev);
+  if (st != WQBMM_OK) return st;
+  return launch_status(wqbmm::launch_operand_weights(w_tiled, K, N, static_cast<uint8_t*>(w_operand),
+                                                     static_cast<hipStream_t>(stream)));
 }
 
 wqbmm_status wqbmm_a16w4_msd(const void* x, const void* w_tiled,
@@ -424,10 +467,10 @@ wqbmm_status wqbmm_a16w4_msd_noalloc(const void* x, const void* w_tiled,
   if (st != WQBMM_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   Buffers b;
-  st = scratch_buffers(dev, s, needs_of(p, group_size, M, K, N, 0, K / group_size, false), &b);
+  st = scratch_buffers(dev, s, needs_of(p, group_size, M, K, N, 0, K / group_size, false, false), &b);
   if (st != WQBMM_OK) return st;
-  return run_path(b, p, x, w_tiled, antiquant_scale, group_size, M, K, N, 0, K / group_size, y,
-                  nullptr, 0, s);
+  return run_path(b, p, x, w_tiled, nullptr, antiquant_scale, group_size, M, K, N, 0, K / group_size,
+                  y, nullptr, 0, s);
 }
 
 wqbmm_status wqbmm_a16w4_msd_prepass(const void* x, int64_t group_size, int64_t M, int64_t K,
@@ -454,21 +497,21 @@ wqbmm_status wqbmm_a16w4_msd_yint(const void* x, const void* w_tiled, int64_t gr
   if (st != WQBMM_OK) return st;
   if (g_begin < 0 || g_end > K / group_size || g_begin >= g_end) return WQBMM_ERR_INVALID;
   if (M == 0) return WQBMM_OK;
-  return run(x, w_tiled, nullptr, group_size, M, K, N, g_begin, g_end, nullptr, y_int, p, 0,
+  return run(x, w_tiled, nullptr, nullptr, group_size, M, K, N, g_begin, g_end, nullptr, y_int, p, 0,
              static_cast<hipStream_t>(stream));
 }
 
 wqbmm_status wqbmm_a16w4_msd_profile_stage(const void* x, const void* w_tiled,
-                                           const void* antiquant_scale, int64_t group_size,
-                                           int64_t M, int64_t K, int64_t N, void* y, int path,
-                                           int stage, void* stream) {
+                                           const void* w_operand, const void* antiquant_scale,
+                                           int64_t group_size, int64_t M, int64_t K, int64_t N,
+                                           void* y, int path, int stage, void* stream) {
   int p = 0;
   const wqbmm_status st = validate_call(x, w_tiled, antiquant_scale, true, y, group_size, M, K, N, path, &p);
   if (st != WQBMM_OK) return st;
-  if (stage < 1 || stage > 2) return WQBMM_ERR_INVALID;
+  if (!aligned16(w_operand) || stage < 1 || stage > 2) return WQBMM_ERR_INVALID;
   if (M == 0) return WQBMM_OK;
-  return run(x, w_tiled, antiquant_scale, group_size, M, K, N, 0, K / group_size, y, nullptr, p,
-             stage, static_cast<hipStream_t>(stream));
+  return run(x, w_tiled, w_operand, antiquant_scale, group_size, M, K, N, 0, K / group_size, y,
+             nullptr, p, stage, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

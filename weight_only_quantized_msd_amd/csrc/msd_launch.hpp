@@ -38,16 +38,28 @@ struct PrefillLayout {
   int64_t npad;        // columns padded to a multiple of bn
   size_t a_bytes;      // level tiles of x: 3 * (mpad/16) * G tiles of 1536 bytes
   size_t q_bytes;      // level weights, [group][row block][level][128] fp32
-  size_t b_bytes;      // weight tiles: (npad/16) * G tiles of 1536 bytes (0 if w_in_gemm)
+  size_t b_bytes;      // weight tiles (0 if w_in_gemm); at group size 128 their columns are
+                       // padded to a multiple of 256 whatever bn is
   bool w_in_gemm;      // the GEMM converts the tiled int4 weights itself (few row blocks)
   int64_t splits = 1;  // K-splits of the GEMM (few tiles); > 1: fp32 partial sums + a reduction
   size_t part_bytes = 0;   // splits * M * N fp32 partial sums (0 without a split)
 };
 PrefillLayout prefill_layout(int gs, int64_t M, int64_t K, int64_t N);
 
+// weights == false (group size 128 only): the weight tiles b_t are the
+// weights' operand form from launch_operand_weights and are not written.
 hipError_t launch_prefill_prep(const void* x, const void* w, int gs, int64_t M, int64_t K,
                                int64_t N, const PrefillLayout& L, uint8_t* a_t, float* q_t,
-                               uint8_t* b_t, hipStream_t stream);
+                               uint8_t* b_t, bool weights, hipStream_t stream);
+
+// The weights' operand form for the group-128 GEMM: the weight tiles the
+// preparation kernel writes (FP6 e2m3, [256-column block][128-row block][16
+// column tiles of 1536 bytes], columns padded to a multiple of 256 with
+// zeros), converted once from the tiled weights.
+inline int64_t operand_weight_npad(int64_t N) { return (N + 255) / 256 * 256; }
+size_t operand_weight_bytes(int64_t K, int64_t N);
+hipError_t launch_operand_weights(const void* w_tiled, int64_t K, int64_t N, uint8_t* w_op,
+                                  hipStream_t stream);
 
 // y_int == nullptr: groups [g_begin, g_end) are combined into y (fp16 [M][N]);
 // otherwise they are stored as int32 Y_int.  With L.splits > 1 the GEMM

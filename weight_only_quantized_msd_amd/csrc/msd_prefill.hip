@@ -45,7 +45,12 @@
 //   row tiles of a level that one GEMM wave holds, and two adjacent column
 //   tiles.
 //   A_t: [row block of 128][group][level][row tile 0..7][tile]
-//   B_t: [column block of BN][group][column tile 0..BN/16-1][tile]
+//   B_t: [block of 256 columns][group][column tile 0..15][tile]: a group's
+//        B operands of a 256-column GEMM block are one run of 24 KB, those of
+//        a 128-column block one half of it.  B_t depends on the weights
+//        alone, so it is either written by the preparation kernel on each
+//        call or converted once and kept (the weights' operand form); its
+//        columns are padded to a multiple of 256 either way.
 //   Q_t: [group][row block][level][128 rows] fp32: A_max * w_l, the row's
 //        step-10 weight of level l (w_l = 1/7.49, 1/(7.49*14.98),
 //        1/(7.49*14.98^2)), formed once per (row, group)
@@ -142,16 +147,18 @@ __device__ __forceinline__ v6i pack_e2m3(const v16f& u, const v16f& v, float div
 // bytes per lane) into their parts of the tile pair.  TPW = 2 (many rows): a
 // wave per tile pair; TPW = 1 (up to four row blocks, where a wave's latency
 // rather than the bytes sets the time): a wave per row tile.
-// Waves [xwaves, ...): one (pair of column tiles, pair of 128-row blocks)
-// each: four 16-byte tiled-weight chunks per lane (column tiles up to the
-// padded width; those beyond N become zeros), all loaded before any is
-// converted in place into operand lane l of its column tile (column blocks
-// of BN), and each block's tile pair stored whole.
+// Waves [xwaves, xwaves + wwaves): one (pair of column tiles, pair of
+// 128-row blocks) each: four 16-byte tiled-weight chunks per lane (column
+// tiles up to the padded width; those beyond N become zeros), all loaded
+// before any is converted in place into operand lane l of its column tile,
+// and each block's tile pair stored whole.  wwaves is 0 when the weights'
+// operand form is kept from an earlier conversion (x unused: xwaves 0).
 template <int GS, int TPW>
 __global__ __launch_bounds__(256) void msd_prep_kernel(const uint16_t* __restrict__ x,
                                                        const uint8_t* __restrict__ wt, int M,
-                                                       int Mpad, int K, int N, int Npad, int BN,
-                                                       int64_t xwaves, uint8_t* __restrict__ a_t,
+                                                       int Mpad, int K, int N,
+                                                       int64_t xwaves, int64_t wwaves,
+                                                       uint8_t* __restrict__ a_t,
                                                        float* __restrict__ q_t,
                                                        uint8_t* __restrict__ b_t) {
   static_assert(GS == 128, "the group-128 path (group size 64 has a kernel of its own)");
@@ -218,8 +225,8 @@ __global__ __launch_bounds__(256) void msd_prep_kernel(const uint16_t* __restric
   const int KB = (K + kTileRows - 1) / kTileRows;
   const int KBP = (KB + 1) / 2;
   const int64_t u = wid - xwaves;
+  if (u >= wwaves) return;     // wwaves: (column tile pairs up to the 256-padded width) x KBP
   const int ctp = (int)(u / KBP), kbp = (int)(u % KBP);
-  if (ctp >= Npad / (2 * kTileCols)) return;
   const int NTR = N / kTileCols;                     // real column tiles
   uint4 v[2][2];                                      // [block of the pair][column tile of the pair]
 #pragma unroll
@@ -231,8 +238,6 @@ __global__ __launch_bounds__(256) void msd_prep_kernel(const uint16_t* __restric
       v[i][h] = *reinterpret_cast<const uint4*>(wt + (ok ? ((int64_t)nt * KB + kb) * 64 + lane : 0) * 16);
     }
   __builtin_amdgcn_sched_barrier(0);                 // every load ahead of the first conversion
-  const int CT = BN / 16;
-  const int cb = (2 * ctp) / CT, ct0 = (2 * ctp) % CT;   // ct0 even: the pair's first column tile
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int kb = 2 * kbp + i;
@@ -255,7 +260,7 @@ __global__ __launch_bounds__(256) void msd_prep_kernel(const uint16_t* __restric
         }
       pk[h] = pack_e2m3(w[0], w[1], 2.0f);
     }
-    uint8_t* pair = b_t + (((int64_t)cb * G + kb) * CT + ct0) * TILE;
+    uint8_t* pair = b_t + (((int64_t)(ctp / 8) * KB + kb) * 8 + ctp % 8) * (2 * TILE);
     *reinterpret_cast<v4i*>(pair + lane * 16) = v4i{pk[0][0], pk[0][1], pk[0][2], pk[0][3]};
     *reinterpret_cast<v4i*>(pair + TILE_LO + lane * 16) = v4i{pk[1][0], pk[1][1], pk[1][2], pk[1][3]};
     *reinterpret_cast<v2i*>(pair + 2 * TILE_LO + lane * 8) = v2i{pk[0][4], pk[0][5]};
@@ -357,7 +362,9 @@ __global__ __launch_bounds__(pf::THREADS, 1) void msd_gemm_kernel(
   // 256-byte copy per wave.  (The 4-byte copies take byte pointers: typed
   // float pointers made the compiler crash in its SGPR-copy pass.)
   const uint8_t* a_run = a_t + (int64_t)rb * G * A_GROUP;
-  const uint8_t* b_run = b_t + (int64_t)cb * G * B_GROUP;
+  // the block's B run of group 0 (groups 24 KB apart: 16 column tiles)
+  constexpr int B_STRIDE = 16 * TILE;
+  const uint8_t* b_run = b_t + (int64_t)(cb * BN / 256) * G * B_STRIDE + (cb * BN % 256) / 16 * TILE;
   const int sc_col = min(n0 + 2 * (wave - QW) * 64 + 2 * lane, N - 2);
   auto dma = [&](int g_, uint8_t* sa, uint8_t* sb, float* sq, uint16_t* ss) {
 #pragma unroll
@@ -365,7 +372,7 @@ __global__ __launch_bounds__(pf::THREADS, 1) void msd_gemm_kernel(
       const int p = wave * CPW + c;                   // wave-uniform
       if (p < PIECES) {
         const uint8_t* src = p < A_KB ? a_run + (int64_t)g_ * A_GROUP + p * 1024
-                                      : b_run + (int64_t)g_ * B_GROUP + (p - A_KB) * 1024;
+                                      : b_run + (int64_t)g_ * B_STRIDE + (p - A_KB) * 1024;
         uint8_t* dst = p < A_KB ? sa + p * 1024 : sb + (p - A_KB) * 1024;
         __builtin_amdgcn_global_load_lds(src + lane * 16, dst, 16, 0, 0);
       }
@@ -631,7 +638,7 @@ PrefillLayout prefill_layout(int gs, int64_t M, int64_t K, int64_t N) {
   const int64_t G = K / gs;
   L.a_bytes = (size_t)(3 * (L.mpad / 16) * G) * pf::TILE;
   L.q_bytes = (size_t)(G * (L.mpad / pf::BM)) * pf::Q_GROUP;
-  L.b_bytes = (size_t)((L.npad / 16) * G) * pf::TILE;
+  L.b_bytes = (size_t)(operand_weight_npad(N) / 16 * G) * pf::TILE;   // 256-column blocks
   L.w_in_gemm = false;
   set_splits(L, (L.mpad / pf::BM) * (L.npad / L.bn), G, M, N);
   return L;
@@ -639,23 +646,41 @@ PrefillLayout prefill_layout(int gs, int64_t M, int64_t K, int64_t N) {
 
 hipError_t launch_prefill_prep(const void* x, const void* w, int gs, int64_t M, int64_t K,
                                int64_t N, const PrefillLayout& L, uint8_t* a_t, float* q_t,
-                               uint8_t* b_t, hipStream_t stream) {
+                               uint8_t* b_t, bool weights, hipStream_t stream) {
   if (gs == 64) return launch_prefill64_prep(x, w, M, K, N, L, a_t, q_t, b_t, stream);
   // up to 4 row blocks: one row tile per x wave (twice the waves, each half
   // as long); beyond, a tile pair per wave
   const int tpw = L.mpad <= 4 * pf::BM ? 1 : 2;
   const int64_t xwaves = (L.mpad / (16 * tpw)) * (K / gs);          // (row tile(s), group) tasks
-  const int64_t wwaves = (L.npad / 32) * ((tiled_kblocks(K) + 1) / 2);   // (column tile pair, block pair)
+  const int64_t npw = operand_weight_npad(N);                      // B_t's 256-column blocks
+  const int64_t wwaves =                                            // (column tile pair, block pair)
+      weights ? (npw / 32) * ((tiled_kblocks(K) + 1) / 2) : 0;
   const unsigned blocks = (unsigned)((xwaves + wwaves + 3) / 4);
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   const uint8_t* wp = static_cast<const uint8_t*>(w);
-  const int m = (int)M, mp = (int)L.mpad, k = (int)K, n = (int)N, np = (int)L.npad, bn = (int)L.bn;
+  const int m = (int)M, mp = (int)L.mpad, k = (int)K, n = (int)N;
   if (tpw == 1)
     hipLaunchKernelGGL((msd_prep_kernel<128, 1>), dim3(blocks), dim3(256), 0, stream, xp, wp, m, mp,
-                       k, n, np, bn, xwaves, a_t, q_t, b_t);
+                       k, n, xwaves, wwaves, a_t, q_t, b_t);
   else
     hipLaunchKernelGGL((msd_prep_kernel<128, 2>), dim3(blocks), dim3(256), 0, stream, xp, wp, m, mp,
-                       k, n, np, bn, xwaves, a_t, q_t, b_t);
+                       k, n, xwaves, wwaves, a_t, q_t, b_t);
+  return hipGetLastError();
+}
+
+size_t operand_weight_bytes(int64_t K, int64_t N) {
+  return (size_t)(operand_weight_npad(N) / 16) * (size_t)tiled_kblocks(K) * pf::TILE;
+}
+
+// The weights' part of the preparation kernel alone.
+hipError_t launch_operand_weights(const void* w_tiled, int64_t K, int64_t N, uint8_t* w_op,
+                                  hipStream_t stream) {
+  const int64_t npad = operand_weight_npad(N);
+  const int64_t wwaves = (npad / 32) * ((tiled_kblocks(K) + 1) / 2);
+  const unsigned blocks = (unsigned)((wwaves + 3) / 4);
+  hipLaunchKernelGGL((msd_prep_kernel<128, 2>), dim3(blocks), dim3(256), 0, stream, nullptr,
+                     static_cast<const uint8_t*>(w_tiled), 0, 0, (int)K, (int)N,
+                     (int64_t)0, wwaves, nullptr, nullptr, w_op);
   return hipGetLastError();
 }
 
