@@ -365,7 +365,7 @@ def measure(torch, W, name, args, path_override=0):
     kern_ms, _ = t.replay_ms()
     del t
     without = None
-    if opw:
+    if opw and not args.no_operand_compare:
         # the same workload without the operand form: the preparation kernel
         # converts the tiled weights on every call
         t = Timed(torch, stream, [call(st, False) for st in sets], steps, warmup)
@@ -439,7 +439,8 @@ def measure(torch, W, name, args, path_override=0):
         if opw:
             roof["operands"] = ("x level tiles MALL-resident, as the preparation kernel leaves them; "
                                 "weight tiles from the weights' operand form in HBM")
-            extra["without_operand_weights"] = without
+            if without:
+                extra["without_operand_weights"] = without
     if isinstance(tinfo, dict):
         extra["traffic_detail"] = {k: tinfo[k] for k in tinfo if k not in ("kernel_sources_sha", "commands")}
     elif isinstance(tinfo, str):
@@ -552,6 +553,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-plain-read", action="store_true")
+    ap.add_argument("--no-operand-compare", action="store_true",
+                    help="skip the group-128 prefill step without the weights' operand form")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the bench line: the decode-vs-prefill M sweep (one JSON line)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
