@@ -54,11 +54,10 @@ __device__ __forceinline__ float msd_div(float t, float d, float y) {
   return __builtin_fmaf(__builtin_fmaf(-q0, d, t), y, q0);
 }
 
-// Round half to even of |t| < 2^22 with the 1.5*2^23 trick: u = t + kMagic
-// lands where the float spacing is 1, so the (round-to-nearest-even) sum
-// holds rint(t) in its low mantissa bits -- its low byte is rint(t) as a
-// two's-complement int8 -- and u - kMagic is rint(t) exactly (kMagic is even,
-// so ties go to the even integer as with rintf).
+// Round half to even is v_rndne_f32 (rintf).  For an integer-valued r with
+// |r| < 2^22, u = r + kMagic (1.5*2^23) lands where the float spacing is 1,
+// so the sum is exact and holds r in its low mantissa bits: its low byte is r
+// as a two's-complement int8.
 constexpr float kMagic = 12582912.0f;
 
 // ---- WQBMM-Exp page §4.1 steps 1-8: the one decomposition every kernel uses
@@ -98,23 +97,25 @@ __device__ __forceinline__ void msd_group_scale(uint32_t max_bits, float& amax, 
 // round(tmp3).  Every operation is one IEEE fp32 rounding in this order (no
 // contraction; tmp = 7.49*a is one fused multiply-add with a zero addend
 // straight from the fp16 value: exact widening, one rounding of the product;
-// the division is correctly rounded, see msd_div); round is half to even,
-// done by the kMagic sum.  Out: the sums u_l = A_l + kMagic (their low byte
-// is A_l as int8) and the levels r_l = A_l as floats (a kernel uses either).
-// |A_l| <= 7 follows from 7.49 < 7.5 and |residual| <= 0.5.
+// the division is correctly rounded, see msd_div); round is half to even
+// (rintf).  Out: the levels r_l = A_l as floats and the sums u_l = A_l +
+// kMagic, whose low byte is A_l as int8 (a kernel uses either; the other is
+// not computed).  |A_l| <= 7 follows from 7.49 < 7.5 and |residual| <= 0.5.
+// (A level that rounds to zero from below is -0.0 in r_l; it has the same
+// value, byte and contribution as +0.0.)
 __device__ __forceinline__ void msd_levels(uint32_t h, float amax, float rcp, float (&u)[3],
                                            float (&r)[3]) {
 #pragma clang fp contract(off)
   const _Float16 a = __builtin_bit_cast(_Float16, (uint16_t)h);
   const float t1 = msd_div(__builtin_fmaf((float)a, kF1, 0.0f), amax, rcp);
-  u[0] = t1 + kMagic;
-  r[0] = u[0] - kMagic;
+  r[0] = __builtin_rintf(t1);
+  u[0] = r[0] + kMagic;
   const float t2 = (t1 - r[0]) * kF2;
-  u[1] = t2 + kMagic;
-  r[1] = u[1] - kMagic;
+  r[1] = __builtin_rintf(t2);
+  u[1] = r[1] + kMagic;
   const float t3 = (t2 - r[1]) * kF2;
-  u[2] = t3 + kMagic;
-  r[2] = u[2] - kMagic;
+  r[2] = __builtin_rintf(t3);
+  u[2] = r[2] + kMagic;
 }
 
 // Maximum over WIDTH (4, 8 or 16) consecutive, aligned lanes of non-negative

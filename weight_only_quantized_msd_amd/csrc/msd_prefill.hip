@@ -162,7 +162,7 @@ __global__ __launch_bounds__(256) void msd_prep_kernel(const uint16_t* __restric
                                                        float* __restrict__ q_t,
                                                        uint8_t* __restrict__ b_t) {
   static_assert(GS == 128, "the group-128 path (group size 64 has a kernel of its own)");
-  static_assert(TPW == 1 || TPW == 2, "one row tile or a pair per wave");
+  static_assert(TPW == 1 || TPW == 2 || TPW == 4, "one row tile, a pair or two pairs per wave");
   using namespace pf;
   const int G = K / GS;
   const int lane = threadIdx.x & 63;
@@ -171,20 +171,31 @@ __global__ __launch_bounds__(256) void msd_prep_kernel(const uint16_t* __restric
     const int tt = (int)(wid / G), g = (int)(wid % G);
     const int r = lane >> 2, kq = lane & 3;
     const int t0 = TPW * tt;                                // the wave's first row tile
-    const int rb = t0 / RT, rt0 = (t0 & ~1) % RT;          // rt0 even: the pair's first row tile
+    const int rb = t0 / RT;                                 // (its TPW tiles lie in one row block)
+    // every tile's loads first (TPW x 64 bytes per lane in flight), then the
+    // tiles one after the other
+    uint4 xa[TPW][4];
+    bool real[TPW];
+#pragma unroll
+    for (int pp = 0; pp < TPW; ++pp) {
+      const int m = (t0 + pp) * 16 + r;
+      real[pp] = m < M;                                     // padding rows decompose zeros
+      const uint16_t* src = x + (real[pp] ? (int64_t)m * K + (int64_t)g * GS + 16 * kq : 0);
+#pragma unroll
+      for (int c = 0; c < 4; ++c)   // c = 0, 1: u (k = 16kq + 8c ..); c = 2, 3: v (k = 64 + 16kq + 8(c-2) ..)
+        xa[pp][c] = *reinterpret_cast<const uint4*>(src + (c < 2 ? 8 * c : 64 + 8 * (c - 2)));
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int pp = 0; pp < TPW; ++pp) {
       const int p = (t0 + pp) & 1;                         // position within the pair
+      const int rt0 = ((t0 + pp) & ~1) % RT;               // the pair's first row tile
       const int m = (t0 + pp) * 16 + r;
-      const bool real = m < M;                       // padding rows decompose zeros
-      const uint16_t* src = x + (real ? (int64_t)m * K + (int64_t)g * GS + 16 * kq : 0);
       uint4 xv[4];
       uint32_t mb = 0;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        // c = 0, 1: u (k = 16kq + 8c ..); c = 2, 3: v (k = 64 + 16kq + 8(c-2) ..)
-        const uint4 v = *reinterpret_cast<const uint4*>(src + (c < 2 ? 8 * c : 64 + 8 * (c - 2)));
-        xv[c] = real ? v : make_uint4(0u, 0u, 0u, 0u);
+        xv[c] = real[pp] ? xa[pp][c] : make_uint4(0u, 0u, 0u, 0u);
         mb = max(mb, chunk_max_bits(xv[c]));
       }
       // steps 1-8 (msd_device.hpp): the group is the 4 lanes of this row
@@ -662,8 +673,11 @@ hipError_t launch_prefill_prep(const void* x, const void* w, int gs, int64_t M, 
   if (tpw == 1)
     hipLaunchKernelGGL((msd_prep_kernel<128, 1>), dim3(blocks), dim3(256), 0, stream, xp, wp, m, mp,
                        k, n, xwaves, wwaves, a_t, q_t, b_t);
-  else
+  else if (tpw == 2)
     hipLaunchKernelGGL((msd_prep_kernel<128, 2>), dim3(blocks), dim3(256), 0, stream, xp, wp, m, mp,
+                       k, n, xwaves, wwaves, a_t, q_t, b_t);
+  else
+    hipLaunchKernelGGL((msd_prep_kernel<128, 4>), dim3(blocks), dim3(256), 0, stream, xp, wp, m, mp,
                        k, n, xwaves, wwaves, a_t, q_t, b_t);
   return hipGetLastError();
 }
