@@ -507,6 +507,64 @@ def test_operand_weights_bit_identical(torch_dev, case):
     check_y_elementwise(got.cpu().numpy()[rows], y32, elementwise_bound(d, rows), "with the operand form")
 
 
+def e2m3_decode(code):
+    """Values of 6-bit e2m3 codes (sign, 2 exponent bits with bias 1, 3
+    mantissa bits; exponent 0 is subnormal: m/8)."""
+    code = np.asarray(code, np.int64)
+    sign = np.where(code & 0x20, -1.0, 1.0)
+    e, m = (code >> 3) & 3, code & 7
+    mag = np.where(e == 0, m / 8.0, (1.0 + m / 8.0) * 2.0 ** (e - 1))
+    return sign * mag
+
+
+def operand_reference_values(buf, K, N):
+    """The weights' operand form read back as values, restated from its
+    documented layout: [256-column block][128-row block][16 column tiles,
+    stored as 8 pairs of 3072 bytes: dwords 0-3 of both tiles' lanes (1 KB
+    each), then dwords 4-5 (512 bytes each)]; lane l of column tile t holds
+    column 16t + l%16 and 32 six-bit slots, slot 2j = k 16(l/16) + j and slot
+    2j+1 = k 64 + 16(l/16) + j of the block.  Returns w/2 as [K][N]."""
+    NB, KB = -(-N // 256), -(-K // 128)
+    b = buf.reshape(NB, KB, 8, 3072)
+    lo = np.stack([b[..., 0:1024], b[..., 1024:2048]], axis=3).reshape(NB, KB, 8, 2, 64, 16)
+    hi = np.stack([b[..., 2048:2560], b[..., 2560:3072]], axis=3).reshape(NB, KB, 8, 2, 64, 8)
+    lane_bytes = np.concatenate([lo, hi], axis=-1)                     # 24 bytes = 192 bits
+    bits = np.unpackbits(lane_bytes, axis=-1, bitorder="little").reshape(NB, KB, 8, 2, 64, 32, 6)
+    codes = (bits.astype(np.int64) << np.arange(6)).sum(-1)              # [.., lane, slot]
+    vals = e2m3_decode(codes)
+    out = np.zeros((KB * 128, NB * 256))
+    lane = np.arange(64)
+    for j in range(16):
+        for half in range(2):
+            k = 64 * half + 16 * (lane // 16) + j                         # [lane]
+            v = vals[..., 2 * j + half]                                     # [NB, KB, pair, p, lane]
+            for pr in range(8):
+                for p in range(2):
+                    col = (2 * pr + p) * 16 + lane % 16
+                    for nb in range(NB):
+                        for kb in range(KB):
+                            out[128 * kb + k, 256 * nb + col] = v[nb, kb, pr, p]
+    return out[:K, :N], out
+
+
+@pytest.mark.parametrize("K,N", [(256, 96), (384, 288), (1024, 544)])
+def test_operand_weights_match_documented_layout(torch_dev, K, N):
+    """The operand form holds w/2 in e2m3 at the documented positions, and
+    zeros in the padding (rows past K, columns past N)."""
+    import weight_only_quantized_msd_amd as W
+    torch = torch_dev
+    d = datagen.random_case(1, K, N, 128, seed=K * 7 + N)
+    announce(f"operand form layout K={K} N={N}")
+    w_tiled = W.wqbmm_a16w4_tile_weights(torch.from_numpy(d["w_packed"]).cuda())
+    w_op = W.wqbmm_a16w4_operand_weights(w_tiled, K)
+    torch.cuda.synchronize()
+    got, full = operand_reference_values(w_op.cpu().numpy(), K, N)
+    assert np.array_equal(got, d["w"].astype(np.float64) / 2.0)
+    pad = full.copy()
+    pad[:K, :N] = 0.0
+    assert not pad.any(), "padding is not zero"
+
+
 def test_operand_weights_stages(torch_dev):
     """Stages with the operand form compose to the one-call result; stage 2
     refuses operands that a stage 1 prepared with the form when it is called
