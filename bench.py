@@ -92,13 +92,22 @@ def kernels_of(path, M, K, N, gs):
     return "msd_prep64_kernel", ("msd_gemm64w_kernel" if mblocks <= 2 else "msd_gemm64_kernel")
 
 
+def prefill_bn(M, N):
+    """Column block of the group-128 GEMM (msd_prefill.hip prefill_layout):
+    256 when its rounds of 256 workgroups cost less, a 256-column tile
+    counting 7/4 of a 128-column one."""
+    mb = -(-M // 128)
+    t256, t128 = mb * -(-N // 256), mb * -(-N // 128)
+    return 256 if (t128 >= 256 and -(-t256 // 256) * 7 < -(-t128 // 256) * 4) else 128
+
+
 def prefill_splits(M, K, N):
     """K-splits of the group-128 GEMM (msd_prefill.hip set_splits): enough to
     bring the workgroups to about 256 when the tiles alone are fewer, each
     split at least two groups long."""
     G = K // 128
     mb = -(-M // 128)
-    bn = 256 if mb * -(-N // 256) >= 256 else 128
+    bn = prefill_bn(M, N)
     tiles = mb * -(-N // bn)
     s = 1 if tiles >= 256 else 256 // tiles
     s = min(s, max(1, G // 2))
@@ -113,14 +122,17 @@ def prefill_prep_bytes(M, K, N, gs, operand_weights=False):
     three per row and group); unless the GEMM converts the weights itself (group
     size 64 with at most two 128-row blocks) or reads the weights' operand form
     (group size 128, operand_weights), it also reads the tiled int4 weights and
-    writes their operand tiles (columns padded to the GEMM's column block of
-    256, or 128 when 256 would give fewer than 256 tiles)."""
+    writes their operand tiles (columns padded to 256 at group size 128, to
+    the GEMM's column block at group size 64)."""
     G = K // gs
     per = 16 if gs == 128 else 32
     mpad = -(-M // 128) * 128
     w_in_gemm = gs == 64 and mpad // 128 <= 2
-    bn = 256 if (not w_in_gemm and (mpad // 128) * -(-N // 256) >= 256) else 128
-    npad = -(-N // bn) * bn
+    if gs == 128:
+        npad = -(-N // 256) * 256                  # the weight tiles' 256-column blocks
+    else:
+        bn = 256 if (not w_in_gemm and (mpad // 128) * -(-N // 256) >= 256) else 128
+        npad = -(-N // bn) * bn
     b = 2 * M * K + 1536 * (3 * mpad // per) * G + 12 * mpad * G
     if not w_in_gemm and not (operand_weights and gs == 128):
         b += K * N // 2 + 1536 * (npad // per) * G

@@ -478,6 +478,9 @@ OPW_CASES = [  # (name or None, M, K, N, gs, path)
     (None, 130, 384, 96, 128, PREFILL),
     (None, 65, 512, 160, 128, AUTO),
     (None, 300, 2048, 2080, 128, PREFILL),
+    # 11 row blocks: 187 tiles of 256 columns (one round, no K-split) beat
+    # 363 of 128 (two rounds); the last 256-column block is half padding
+    (None, 1300, 512, 4128, 128, PREFILL),
     ("decode_m16", None, None, None, None, AUTO),
     ("outlier_m128", None, None, None, None, PREFILL),
 ]

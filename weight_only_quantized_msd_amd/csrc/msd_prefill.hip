@@ -637,14 +637,19 @@ void set_splits(PrefillLayout& L, int64_t tiles, int64_t G, int64_t M, int64_t N
   L.part_bytes = L.splits > 1 ? (size_t)L.splits * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
-// Column blocks of 256 when that still gives at least one workgroup per CU
-// (256 workgroups), else of 128.
+// Column blocks of 256 or 128.  The GEMM holds one workgroup per CU, so its
+// time is about (rounds of 256 workgroups) x (one workgroup's time), and a
+// 128 x 256 tile takes about 7/4 of a 128 x 128 one (72 against 41 us per
+// tile at K = 4096, measured).  256-column blocks when their rounds cost less
+// (M = 1280 or 1536 at N = 4096: one round of 256-column tiles against two of
+// 128-column ones); with fewer than 256 tiles of 128 columns, 128 and a K-split.
 PrefillLayout prefill_layout(int gs, int64_t M, int64_t K, int64_t N) {
   if (gs == 64) return prefill64_layout(M, K, N);
   PrefillLayout L;
   L.mpad = (M + pf::BM - 1) / pf::BM * pf::BM;
-  const int64_t tiles256 = (L.mpad / pf::BM) * ((N + 255) / 256);
-  L.bn = tiles256 >= 256 ? 256 : 128;
+  const int64_t mb = L.mpad / pf::BM;
+  const int64_t t256 = mb * ((N + 255) / 256), t128 = mb * ((N + 127) / 128);
+  L.bn = (t128 >= 256 && ((t256 + 255) / 256) * 7 < ((t128 + 255) / 256) * 4) ? 256 : 128;
   L.npad = (N + L.bn - 1) / L.bn * L.bn;
   const int64_t G = K / gs;
   L.a_bytes = (size_t)(3 * (L.mpad / 16) * G) * pf::TILE;
