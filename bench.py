@@ -101,6 +101,16 @@ def prefill_bn(M, N):
     return 256 if (t128 >= 256 and -(-t256 // 256) * 7 < -(-t128 // 256) * 4) else 128
 
 
+def prefill64_bn(M, N):
+    """Column block of the group-64 GEMM (msd_prefill64.hip prefill64_layout):
+    128 with the in-GEMM weight conversion (up to two row blocks), else 256
+    when its rounds of 256 workgroups cost less, a 256-column tile counting
+    15/8 of a 128-column one."""
+    mb = -(-M // 128)
+    t256, t128 = mb * -(-N // 256), mb * -(-N // 128)
+    return 256 if (mb > 2 and -(-t256 // 256) * 15 < -(-t128 // 256) * 8) else 128
+
+
 def prefill_splits(M, K, N):
     """K-splits of the group-128 GEMM (msd_prefill.hip set_splits): enough to
     bring the workgroups to about 256 when the tiles alone are fewer, each
@@ -131,8 +141,7 @@ def prefill_prep_bytes(M, K, N, gs, operand_weights=False):
     if gs == 128:
         npad = -(-N // 256) * 256                  # the weight tiles' 256-column blocks
     else:
-        bn = 256 if (not w_in_gemm and (mpad // 128) * -(-N // 256) >= 256) else 128
-        npad = -(-N // bn) * bn
+        npad = -(-N // prefill64_bn(M, N)) * prefill64_bn(M, N)
     b = 2 * M * K + 1536 * (3 * mpad // per) * G + 12 * mpad * G
     if not w_in_gemm and not (operand_weights and gs == 128):
         b += K * N // 2 + 1536 * (npad // per) * G

@@ -481,6 +481,11 @@ OPW_CASES = [  # (name or None, M, K, N, gs, path)
     # 11 row blocks: 187 tiles of 256 columns (one round, no K-split) beat
     # 363 of 128 (two rounds); the last 256-column block is half padding
     (None, 1300, 512, 4128, 128, PREFILL),
+    # group size 64 past two row blocks: 128-column blocks (three rounds of
+    # 128-column tiles against two of 256) and 256-column blocks with fewer
+    # than 256 tiles (one round against two)
+    (None, 384, 256, 28672, 64, PREFILL),
+    (None, 640, 512, 8192, 64, PREFILL),
     ("decode_m16", None, None, None, None, AUTO),
     ("outlier_m128", None, None, None, None, PREFILL),
 ]

@@ -728,14 +728,18 @@ __global__ __launch_bounds__(1024, 1) void msd_gemm64w_kernel(
 // ---------------------------------------------------------------- launchers
 
 // Up to two row blocks: weights converted in the GEMM (128-column blocks);
-// more: converted once by the preparation kernel, column blocks of 256 when
-// that still gives at least one workgroup per CU, else of 128.
+// more: converted once by the preparation kernel, column blocks of 256 or 128.
+// The GEMM holds one workgroup per CU and a 128 x 256 tile takes about 15/8
+// of a 128 x 128 one (213 against 114 us per tile at K = 8192, measured), so
+// 256-column blocks when their rounds of 256 workgroups cost less by that
+// count.
 PrefillLayout prefill64_layout(int64_t M, int64_t K, int64_t N) {
   PrefillLayout L;
   L.mpad = (M + p64::BM - 1) / p64::BM * p64::BM;
-  L.w_in_gemm = L.mpad / p64::BM <= 2;
-  const int64_t tiles256 = (L.mpad / p64::BM) * ((N + 255) / 256);
-  L.bn = (!L.w_in_gemm && tiles256 >= 256) ? 256 : 128;
+  const int64_t mb = L.mpad / p64::BM;
+  L.w_in_gemm = mb <= 2;
+  const int64_t t256 = mb * ((N + 255) / 256), t128 = mb * ((N + 127) / 128);
+  L.bn = (!L.w_in_gemm && ((t256 + 255) / 256) * 15 < ((t128 + 255) / 256) * 8) ? 256 : 128;
   L.npad = (N + L.bn - 1) / L.bn * L.bn;
   const int64_t G = K / 64;
   L.a_bytes = (size_t)(3 * (L.mpad / 32) * G) * p64::TILE;
