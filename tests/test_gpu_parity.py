@@ -481,6 +481,8 @@ OPW_CASES = [  # (name or None, M, K, N, gs, path)
     # 11 row blocks: 187 tiles of 256 columns (one round, no K-split) beat
     # 363 of 128 (two rounds); the last 256-column block is half padding
     (None, 1300, 512, 4128, 128, PREFILL),
+    # 256 tiles of 128 columns (one round, no K-split) beat 128 of 256
+    (None, 1024, 512, 4096, 128, PREFILL),
     # group size 64 past two row blocks: 128-column blocks (three rounds of
     # 128-column tiles against two of 256) and 256-column blocks with fewer
     # than 256 tiles (one round against two)

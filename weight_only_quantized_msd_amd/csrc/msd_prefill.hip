@@ -664,9 +664,10 @@ hipError_t launch_prefill_prep(const void* x, const void* w, int gs, int64_t M, 
                                int64_t N, const PrefillLayout& L, uint8_t* a_t, float* q_t,
                                uint8_t* b_t, bool weights, hipStream_t stream) {
   if (gs == 64) return launch_prefill64_prep(x, w, M, K, N, L, a_t, q_t, b_t, stream);
-  // up to 4 row blocks: one row tile per x wave (twice the waves, each half
-  // as long); beyond, a tile pair per wave
-  const int tpw = L.mpad <= 4 * pf::BM ? 1 : 2;
+  // up to 16 row blocks: one row tile per x wave (twice the waves, each half
+  // as long); beyond, a tile pair per wave (measured: one tile per wave is
+  // faster up to M = 2048, 9.3 -> 8.9 us there, slower at 4096)
+  const int tpw = L.mpad <= 16 * pf::BM ? 1 : 2;
   const int64_t xwaves = (L.mpad / (16 * tpw)) * (K / gs);          // (row tile(s), group) tasks
   const int64_t npw = operand_weight_npad(N);                      // B_t's 256-column blocks
   const int64_t wwaves =                                            // (column tile pair, block pair)
