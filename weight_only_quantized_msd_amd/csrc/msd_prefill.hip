@@ -144,15 +144,17 @@ __device__ __forceinline__ v6i pack_e2m3(const v16f& u, const v16f& v, float div
 // 16*kq + j, v: k = 64 + 16*kq + j), so a group's maximum is a 4-lane
 // reduction; the rows' level weights A_max * w_l go to Q_t.  Per row tile
 // and level a wave stores dwords 0-3 (16 bytes per lane) and dwords 4-5 (8
-// bytes per lane) into their parts of the tile pair.  TPW = 2 (many rows): a
-// wave per tile pair; TPW = 1 (up to four row blocks, where a wave's latency
-// rather than the bytes sets the time): a wave per row tile.
+// bytes per lane) into their parts of the tile pair.  A wave issues the loads
+// of all its TPW row tiles before it decomposes the first.  (The launcher
+// takes one row tile per wave up to 16 row blocks and a pair beyond; TPW = 4
+// is built as well.)
 // Waves [xwaves, xwaves + wwaves): one (pair of column tiles, pair of
 // 128-row blocks) each: four 16-byte tiled-weight chunks per lane (column
-// tiles up to the padded width; those beyond N become zeros), all loaded
+// tiles up to the 256-padded width; those beyond N become zeros), all loaded
 // before any is converted in place into operand lane l of its column tile,
-// and each block's tile pair stored whole.  wwaves is 0 when the weights'
-// operand form is kept from an earlier conversion (x unused: xwaves 0).
+// and each block's tile pair stored whole.  wwaves is 0 when the GEMM reads
+// the weights' operand form; the one-time conversion into that form runs
+// the weight waves alone (xwaves 0, x unused).
 template <int GS, int TPW>
 __global__ __launch_bounds__(256) void msd_prep_kernel(const uint16_t* __restrict__ x,
                                                        const uint8_t* __restrict__ wt, int M,
