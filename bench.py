@@ -491,6 +491,90 @@ def measure(torch, W, name, args, path_override=0):
     return res
 
 
+def probe_overlap(torch, steps, warmup, iters=2000):
+    """The MFMA / VALU co-issue probe (wqbmm_probe_mfma_valu): the time of
+    each mode per launch (HIP events over a graph of `steps` launches, median
+    of 5 replays), and the ratios that say whether the two kinds of work
+    overlap on a SIMD: 1.0 for `both_in_each_wave` / (mfma + fma) means no
+    overlap."""
+    from weight_only_quantized_msd_amd import _lib as L
+    out = torch.empty(131072, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.Stream()
+    sp = int(stream.cuda_stream)
+    res = {}
+    for mode, name in [(0, "mfma_only"), (1, "fma_only"), (2, "both_in_each_wave"), (3, "one_kind_per_wave")]:
+        def f(mode=mode):
+            rc = L.wqbmm_probe_mfma_valu_raw(mode, iters, out.data_ptr(), sp)
+            if rc:
+                raise RuntimeError(f"wqbmm_probe_mfma_valu: {rc}")
+        t = Timed(torch, stream, [f], steps, warmup)
+        res[name] = round(t.spread(5)["median_ms"] * 1e3, 2)
+        del t
+    alone = res["mfma_only"] + res["fma_only"]
+    return {"unit": "us per launch", "rounds": iters,
+            "round": "12 FP6 16x16x128 MFMAs and/or 64 fp32 FMAs per wave, 2 waves per SIMD",
+            "us": res,
+            "both_in_each_wave_over_sum": round(res["both_in_each_wave"] / alone, 3),
+            "one_kind_per_wave_over_sum": round(res["one_kind_per_wave"] / alone, 3)}
+
+
+SHAPES_DEFAULT = [(128, 4096, 4096, 128), (256, 4096, 4096, 128), (512, 4096, 4096, 128),
+                  (1024, 4096, 4096, 128), (1536, 4096, 4096, 128), (2048, 4096, 4096, 128),
+                  (3072, 4096, 4096, 128), (512, 4096, 11008, 128), (256, 4096, 8192, 128),
+                  (384, 8192, 28672, 64), (1024, 4096, 11008, 64)]
+
+
+def shapes(torch, W, shape_list, steps, warmup):
+    """Prefill-path step time (median of 5 replays, MALL-cold) at arbitrary
+    shapes, each kernel alone beside it, with the weights' operand form and,
+    at group size 128, without it.  Returns a list of rows."""
+    rows = []
+    lib = W.lib()
+    for M, K, N, gs in shape_list:
+        alg = algorithmic(M, K, N, gs)
+        nsets = max(2, min(64, math.ceil(MALL_COLD_BYTES / alg["bytes"])))
+        dist = {"x": "normal", "w": (-8, 7), "scale": ("uniform", 0.005, 0.02)}
+        sets = make_sets(torch, W, M, K, N, gs, nsets, 7, dist, operand_weights=gs == 128)
+        stream = torch.cuda.Stream()
+        sptr = int(stream.cuda_stream)
+        row = {"M": M, "K": K, "N": N, "group_size": gs,
+               "column_block": prefill_bn(M, N) if gs == 128 else prefill64_bn(M, N),
+               "k_splits": prefill_splits(M, K, N) if gs == 128 else 1}
+        for use in ((True, False) if gs == 128 else (False,)):
+            def call(st, k=0, use=use):
+                def f():
+                    op = st["o"].data_ptr() if use else None
+                    if k == 0:
+                        rc = lib.wqbmm_a16w4_msd_ex(st["x"].data_ptr(), st["w"].data_ptr(), op,
+                                                    st["s"].data_ptr(), gs, M, K, N, st["y"].data_ptr(),
+                                                    2, sptr)
+                    else:
+                        rc = lib.wqbmm_a16w4_msd_profile_stage(st["x"].data_ptr(), st["w"].data_ptr(), op,
+                                                               st["s"].data_ptr(), gs, M, K, N,
+                                                               st["y"].data_ptr(), 2, k, sptr)
+                    if rc:
+                        raise W.WqbmmError(rc, "shapes")
+                return f
+            print(f"[shapes] M={M} K={K} N={N} gs={gs} operand_form={use}", file=sys.stderr, flush=True)
+            t = Timed(torch, stream, [call(st) for st in sets], steps, warmup)
+            step = t.spread(5)["median_ms"]
+            del t
+            t = Timed(torch, stream, [call(st, 1) for st in sets], steps, warmup)
+            prep = t.replay_ms()[0]
+            del t
+            t = Timed(torch, stream, [call(st, 2) for st in sets], steps, warmup)
+            main = t.replay_ms()[0]
+            del t
+            key = "with_operand_form" if use else ("without_operand_form" if gs == 128 else "step")
+            row[key] = {"step_us": round(step * 1e3, 2), "prep_us": round(prep * 1e3, 2),
+                        "gemm_us": round(main * 1e3, 2),
+                        "effective_TOPS": round(alg["eff_ops"] / (step * 1e-3) / 1e12, 1)}
+        rows.append(row)
+        del sets
+        torch.cuda.synchronize()
+    return rows
+
+
 SWEEP_M = [8, 12, 16, 24, 32, 48, 64, 96, 128]
 SWEEP_SHAPES = [("K4096_N4096_g128", 4096, 4096, 128), ("K8192_N28672_g64", 8192, 28672, 64)]
 
@@ -578,6 +662,11 @@ def main():
                     help="skip the group-128 prefill step without the weights' operand form")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the bench line: the decode-vs-prefill M sweep (one JSON line)")
+    ap.add_argument("--shapes", nargs="?", const="default", default=None,
+                    help="instead of the bench line: the prefill path at shapes 'M,K,N,gs;...' "
+                         "(default: a built-in list), with and without the weights' operand form")
+    ap.add_argument("--probe-overlap", action="store_true",
+                    help="instead of the bench line: the MFMA / VALU co-issue probe (one JSON line)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -600,6 +689,18 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    if args.shapes:
+        lst = SHAPES_DEFAULT if args.shapes == "default" else [
+            tuple(int(v) for v in item.split(",")) for item in args.shapes.split(";") if item]
+        print(json.dumps({"shapes": shapes(torch, W, lst, args.steps, args.warmup), "steps": args.steps,
+                          "kernel_sources_sha": kernel_sources_sha()}), flush=True)
+        return
+
+    if args.probe_overlap:
+        print(json.dumps({"probe_overlap": probe_overlap(torch, args.steps, args.warmup),
+                          "kernel_sources_sha": kernel_sources_sha()}), flush=True)
+        return
 
     if args.sweep:
         print(json.dumps({"sweep": sweep(torch, W, args), "steps": args.steps,

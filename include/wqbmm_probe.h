@@ -1,5 +1,5 @@
 /*
- * wqbmm_probe.h -- measurement helper exported by libwqbmm.so beside the
+ * wqbmm_probe.h -- measurement helpers exported by libwqbmm.so beside the
  * operator (include/wqbmm.h).  Not part of the operator.
  *
  * The weight-streaming (decode) kernels of the operator are bound by HBM
@@ -31,6 +31,27 @@ extern "C" {
  * breaks the rules (nothing launched), 4 if the launch failed.
  */
 int wqbmm_probe_stream_read(const void* src, int64_t bytes, void* sink, void* stream);
+
+/* Floats `wqbmm_probe_mfma_valu` writes to `out`: one per thread of its
+ * 256 workgroups of 512 threads. */
+#define WQBMM_PROBE_MFMA_VALU_OUT 131072
+
+/*
+ * Whether MFMA and VALU work overlap on a SIMD (the prefill GEMMs issue
+ * both: FP6 MFMAs for step 9, fp32 FMAs for the combine of step 10).  Runs
+ * 256 workgroups of 8 waves (two per SIMD), `iters` rounds each, a round
+ * being per wave, by `mode`:
+ *   0  a block of 12 independent v_mfma_scale_f32_16x16x128_f8f6f4 (FP6)
+ *   1  a block of 64 fp32 FMAs (16 independent chains)
+ *   2  both blocks, one after the other
+ *   3  waves 0-3 the MFMA block only, waves 4-7 the FMA block only (one wave
+ *      of each kind per SIMD)
+ * No memory traffic inside the loop.  out: WQBMM_PROBE_MFMA_VALU_OUT floats
+ * of device memory, written (values of no meaning).  Asynchronous on
+ * `stream`.  Returns 0 on success, 1 if out is NULL, 2 if mode is not 0-3 or
+ * iters not in [1, 2^20] (nothing launched), 4 if the launch failed.
+ */
+int wqbmm_probe_mfma_valu(int mode, int iters, void* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -246,3 +246,12 @@ def test_tile_weights_validation(over, want):
     a.update(over)
     st = L.wqbmm_a16w4_tile_weights_raw(a["w"], a["K"], a["N"], a["t"], None)
     assert st == want
+
+
+@pytest.mark.parametrize("mode,iters,out,want", [
+    (0, 10, 0, 1),            # null output
+    (4, 10, FAKE, 2), (-1, 10, FAKE, 2),
+    (0, 0, FAKE, 2), (0, (1 << 20) + 1, FAKE, 2),
+])
+def test_probe_mfma_valu_validation(mode, iters, out, want):
+    assert L.wqbmm_probe_mfma_valu_raw(mode, iters, out, None) == want

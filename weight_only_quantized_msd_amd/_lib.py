@@ -52,6 +52,7 @@ SIGNATURES = {
     "wqbmm_version": (_int, []),
     # include/wqbmm_probe.h (measurement helper)
     "wqbmm_probe_stream_read": (_int, [_p, _i64, _p, _p]),
+    "wqbmm_probe_mfma_valu": (_int, [_int, _int, _p, _p]),
 }
 
 _lib = None
@@ -149,6 +150,10 @@ def wqbmm_a16w4_msd_profile_stage_raw(x, w, w_operand, scale, group_size, M, K, 
 
 def wqbmm_probe_stream_read_raw(src, nbytes, sink, stream) -> int:
     return lib().wqbmm_probe_stream_read(src, nbytes, sink, stream)
+
+
+def wqbmm_probe_mfma_valu_raw(mode, iters, out, stream) -> int:
+    return lib().wqbmm_probe_mfma_valu(mode, iters, out, stream)
 
 
 def wqbmm_select_path(M, K, N, group_size) -> int:

@@ -1,11 +1,19 @@
-// msd_probe.hip -- measurement helper, not part of the operator: a plain
-// streaming read of a byte range, the achievable-bandwidth reference that the
-// weight-streaming (decode) kernels are compared with.  It reads every byte
+// msd_probe.hip -- measurement helpers, not part of the operator.
+//
+// (1) A plain streaming read of a byte range, the achievable-bandwidth
+// reference that the weight-streaming (decode) kernels are compared with.  It reads every byte
 // once with 16-byte nontemporal loads (the loads the decode kernels use for
 // their weights): a wave's load covers 1 KB, four loads in flight per lane.
 // Each lane folds what it read into one word and stores it only if it equals
 // a value the caller's data never produces, so the loads cannot be dropped
 // and the kernel writes nothing in practice.
+//
+// (2) An MFMA / VALU co-issue probe: whether the FP6 MFMAs and the fp32
+// FMAs of the prefill GEMMs' combine overlap on a SIMD.  256 workgroups of 8
+// waves (two per SIMD, as in the group-128 GEMM), each round a block of 12
+// independent v_mfma_scale_f32_16x16x128_f8f6f4 (eight accumulators) and/or
+// a block of 64 fp32 FMAs in 16 independent chains, no memory traffic inside
+// the loop; the results are summed into one float per thread at the end.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -38,7 +46,65 @@ __global__ __launch_bounds__(kThreads) void msd_probe_read_kernel(const u32x4* _
   if (h == 0x9E3779B9u) sink[0] = h;
 }
 
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kOvlThreads = 512;
+constexpr int kOvlBlocks = 256;
+constexpr int kOvlMfma = 12;    // MFMAs per round
+constexpr int kOvlFma = 64;     // fp32 FMAs per round
+
+// mode 0: MFMA blocks only; 1: FMA blocks only; 2: every wave an MFMA block
+// then an FMA block per round; 3: waves 0-3 MFMA blocks only, waves 4-7 FMA
+// blocks only (one of each kind per SIMD).
+__global__ __launch_bounds__(kOvlThreads) void msd_probe_mfma_valu_kernel(int mode, int iters,
+                                                                         float* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  // e2m3 codes of small values in every byte (any bit pattern is a valid
+  // operand; these keep the sums finite)
+  const int pat = 0x08080808 | (lane & 3);
+  const i32x8 a = {pat, pat, pat, pat, pat, pat, 0, 0};
+  const i32x8 b = {pat ^ 1, pat, pat ^ 2, pat, pat, pat ^ 3, 0, 0};
+  f32x4 acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float x[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x[i] = (float)(lane + i) * 0.001f;
+  const float m = 0.999f, c = 0.001f;
+  const bool do_mfma = mode == 0 || mode == 2 || (mode == 3 && wave < 4);   // wave-uniform
+  const bool do_fma = mode == 1 || mode == 2 || (mode == 3 && wave >= 4);
+  for (int it = 0; it < iters; ++it) {
+    if (do_mfma) {
+#pragma unroll
+      for (int j = 0; j < kOvlMfma; ++j)
+        acc[j & 7] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[j & 7], 2, 2, 0, 127, 0, 127);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (do_fma) {
+#pragma unroll
+      for (int j = 0; j < kOvlFma; ++j) x[j & 15] = __builtin_fmaf(x[j & 15], m, c);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sum += x[i];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sum += acc[i][0] + acc[i][1] + acc[i][2] + acc[i][3];
+  out[(int64_t)blockIdx.x * kOvlThreads + threadIdx.x] = sum;
+}
+
 }  // namespace
+
+extern "C" int wqbmm_probe_mfma_valu(int mode, int iters, void* out, void* stream) {
+  if (!out) return 1;
+  if (mode < 0 || mode > 3 || iters < 1 || iters > (1 << 20)) return 2;
+  hipLaunchKernelGGL(msd_probe_mfma_valu_kernel, dim3(kOvlBlocks), dim3(kOvlThreads), 0,
+                     static_cast<hipStream_t>(stream), mode, iters, static_cast<float*>(out));
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
 
 extern "C" int wqbmm_probe_stream_read(const void* src, int64_t bytes, void* sink, void* stream) {
   if (!src || !sink) return 1;
