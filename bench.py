@@ -502,7 +502,8 @@ def probe_overlap(torch, steps, warmup, iters=2000):
     stream = torch.cuda.Stream()
     sp = int(stream.cuda_stream)
     res = {}
-    for mode, name in [(0, "mfma_only"), (1, "fma_only"), (2, "both_in_each_wave"), (3, "one_kind_per_wave")]:
+    for mode, name in [(0, "mfma_only"), (1, "fma_only"), (2, "both_in_each_wave"), (3, "one_kind_per_wave"),
+                       (4, "both_in_each_wave_barrier_per_round")]:
         def f(mode=mode):
             rc = L.wqbmm_probe_mfma_valu_raw(mode, iters, out.data_ptr(), sp)
             if rc:
@@ -515,7 +516,9 @@ def probe_overlap(torch, steps, warmup, iters=2000):
             "round": "12 FP6 16x16x128 MFMAs and/or 64 fp32 FMAs per wave, 2 waves per SIMD",
             "us": res,
             "both_in_each_wave_over_sum": round(res["both_in_each_wave"] / alone, 3),
-            "one_kind_per_wave_over_sum": round(res["one_kind_per_wave"] / alone, 3)}
+            "one_kind_per_wave_over_sum": round(res["one_kind_per_wave"] / alone, 3),
+            "both_in_each_wave_barrier_per_round_over_sum":
+                round(res["both_in_each_wave_barrier_per_round"] / alone, 3)}
 
 
 SHAPES_DEFAULT = [(128, 4096, 4096, 128), (256, 4096, 4096, 128), (512, 4096, 4096, 128),

@@ -46,9 +46,10 @@ int wqbmm_probe_stream_read(const void* src, int64_t bytes, void* sink, void* st
  *   2  both blocks, one after the other
  *   3  waves 0-3 the MFMA block only, waves 4-7 the FMA block only (one wave
  *      of each kind per SIMD)
+ *   4  as 2, with a workgroup barrier after every round
  * No memory traffic inside the loop.  out: WQBMM_PROBE_MFMA_VALU_OUT floats
  * of device memory, written (values of no meaning).  Asynchronous on
- * `stream`.  Returns 0 on success, 1 if out is NULL, 2 if mode is not 0-3 or
+ * `stream`.  Returns 0 on success, 1 if out is NULL, 2 if mode is not 0-4 or
  * iters not in [1, 2^20] (nothing launched), 4 if the launch failed.
  */
 int wqbmm_probe_mfma_valu(int mode, int iters, void* out, void* stream);

@@ -67,7 +67,8 @@
 // interleaved (4 VALU per output and group: three for the levels, one for
 // the scale and the running sum).  The operand reads from LDS are the
 // GEMM's largest cost after the MFMA and the combine (FP6 MFMA and VALU
-// issue do not overlap here): a wave reads 6 A + NT B tiles per group, the
+// issue overlap only partly on a SIMD, the less the more often the waves are
+// realigned by a barrier): a wave reads 6 A + NT B tiles per group, the
 // fewest for 16 x 16 output tiles per wave (64 x 64 waves read 12 + 4).
 // Per group a workgroup reads 36 KB + BN/16 * 1.5 KB of operands; LDS holds
 // one group's operands, weights and scales, double-buffered: the next group

@@ -56,7 +56,9 @@ constexpr int kOvlFma = 64;     // fp32 FMAs per round
 
 // mode 0: MFMA blocks only; 1: FMA blocks only; 2: every wave an MFMA block
 // then an FMA block per round; 3: waves 0-3 MFMA blocks only, waves 4-7 FMA
-// blocks only (one of each kind per SIMD).
+// blocks only (one of each kind per SIMD); 4: as 2 with a workgroup barrier
+// after every round (the waves of a SIMD kept in the same phase, as a GEMM's
+// group barrier keeps them).
 __global__ __launch_bounds__(kOvlThreads) void msd_probe_mfma_valu_kernel(int mode, int iters,
                                                                          float* __restrict__ out) {
   const int lane = threadIdx.x & 63;
@@ -73,8 +75,8 @@ __global__ __launch_bounds__(kOvlThreads) void msd_probe_mfma_valu_kernel(int mo
 #pragma unroll
   for (int i = 0; i < 16; ++i) x[i] = (float)(lane + i) * 0.001f;
   const float m = 0.999f, c = 0.001f;
-  const bool do_mfma = mode == 0 || mode == 2 || (mode == 3 && wave < 4);   // wave-uniform
-  const bool do_fma = mode == 1 || mode == 2 || (mode == 3 && wave >= 4);
+  const bool do_mfma = mode == 0 || mode == 2 || mode == 4 || (mode == 3 && wave < 4);   // wave-uniform
+  const bool do_fma = mode == 1 || mode == 2 || mode == 4 || (mode == 3 && wave >= 4);
   for (int it = 0; it < iters; ++it) {
     if (do_mfma) {
 #pragma unroll
@@ -87,6 +89,7 @@ __global__ __launch_bounds__(kOvlThreads) void msd_probe_mfma_valu_kernel(int mo
       for (int j = 0; j < kOvlFma; ++j) x[j & 15] = __builtin_fmaf(x[j & 15], m, c);
     }
     __builtin_amdgcn_sched_barrier(0);
+    if (mode == 4) __builtin_amdgcn_s_barrier();   // every wave of the workgroup takes it
   }
   float sum = 0.f;
 #pragma unroll
@@ -100,7 +103,7 @@ __global__ __launch_bounds__(kOvlThreads) void msd_probe_mfma_valu_kernel(int mo
 
 extern "C" int wqbmm_probe_mfma_valu(int mode, int iters, void* out, void* stream) {
   if (!out) return 1;
-  if (mode < 0 || mode > 3 || iters < 1 || iters > (1 << 20)) return 2;
+  if (mode < 0 || mode > 4 || iters < 1 || iters > (1 << 20)) return 2;
   hipLaunchKernelGGL(msd_probe_mfma_valu_kernel, dim3(kOvlBlocks), dim3(kOvlThreads), 0,
                      static_cast<hipStream_t>(stream), mode, iters, static_cast<float*>(out));
   return hipGetLastError() == hipSuccess ? 0 : 4;
