@@ -498,12 +498,15 @@ def probe_overlap(torch, steps, warmup, iters=2000):
     overlap on a SIMD: 1.0 for `both_in_each_wave` / (mfma + fma) means no
     overlap."""
     from weight_only_quantized_msd_amd import _lib as L
-    out = torch.empty(131072, dtype=torch.float32, device="cuda")
+    out = torch.empty(262144, dtype=torch.float32, device="cuda")
     stream = torch.cuda.Stream()
     sp = int(stream.cuda_stream)
     res = {}
     for mode, name in [(0, "mfma_only"), (1, "fma_only"), (2, "both_in_each_wave"), (3, "one_kind_per_wave"),
-                       (4, "both_in_each_wave_barrier_per_round")]:
+                       (4, "both_in_each_wave_barrier_per_round"), (6, "one_wave_per_simd_mfma_only"),
+                       (7, "one_wave_per_simd_fma_only"), (5, "one_wave_per_simd_both"),
+                       (9, "four_waves_per_simd_mfma_only"), (10, "four_waves_per_simd_fma_only"),
+                       (8, "four_waves_per_simd_both")]:
         def f(mode=mode):
             rc = L.wqbmm_probe_mfma_valu_raw(mode, iters, out.data_ptr(), sp)
             if rc:
@@ -518,7 +521,13 @@ def probe_overlap(torch, steps, warmup, iters=2000):
             "both_in_each_wave_over_sum": round(res["both_in_each_wave"] / alone, 3),
             "one_kind_per_wave_over_sum": round(res["one_kind_per_wave"] / alone, 3),
             "both_in_each_wave_barrier_per_round_over_sum":
-                round(res["both_in_each_wave_barrier_per_round"] / alone, 3)}
+                round(res["both_in_each_wave_barrier_per_round"] / alone, 3),
+            "one_wave_per_simd_both_over_sum":
+                round(res["one_wave_per_simd_both"] / (res["one_wave_per_simd_mfma_only"]
+                                                      + res["one_wave_per_simd_fma_only"]), 3),
+            "four_waves_per_simd_both_over_sum":
+                round(res["four_waves_per_simd_both"] / (res["four_waves_per_simd_mfma_only"]
+                                                        + res["four_waves_per_simd_fma_only"]), 3)}
 
 
 SHAPES_DEFAULT = [(128, 4096, 4096, 128), (256, 4096, 4096, 128), (512, 4096, 4096, 128),

@@ -32,9 +32,9 @@ extern "C" {
  */
 int wqbmm_probe_stream_read(const void* src, int64_t bytes, void* sink, void* stream);
 
-/* Floats `wqbmm_probe_mfma_valu` writes to `out`: one per thread of its
- * 256 workgroups of 512 threads. */
-#define WQBMM_PROBE_MFMA_VALU_OUT 131072
+/* Floats `wqbmm_probe_mfma_valu` may write to `out`: one per thread of its
+ * (up to) 512 workgroups of 512 threads. */
+#define WQBMM_PROBE_MFMA_VALU_OUT 262144
 
 /*
  * Whether MFMA and VALU work overlap on a SIMD (the prefill GEMMs issue
@@ -47,9 +47,12 @@ int wqbmm_probe_stream_read(const void* src, int64_t bytes, void* sink, void* st
  *   3  waves 0-3 the MFMA block only, waves 4-7 the FMA block only (one wave
  *      of each kind per SIMD)
  *   4  as 2, with a workgroup barrier after every round
+ *   5, 6, 7  as 2, 0 and 1 with waves 4-7 idle (one wave per SIMD)
+ *   8, 9, 10 as 2, 0 and 1 with 512 workgroups (two per CU: four waves per
+ *            SIMD)
  * No memory traffic inside the loop.  out: WQBMM_PROBE_MFMA_VALU_OUT floats
  * of device memory, written (values of no meaning).  Asynchronous on
- * `stream`.  Returns 0 on success, 1 if out is NULL, 2 if mode is not 0-4 or
+ * `stream`.  Returns 0 on success, 1 if out is NULL, 2 if mode is not 0-10 or
  * iters not in [1, 2^20] (nothing launched), 4 if the launch failed.
  */
 int wqbmm_probe_mfma_valu(int mode, int iters, void* out, void* stream);

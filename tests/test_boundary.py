@@ -250,7 +250,7 @@ def test_tile_weights_validation(over, want):
 
 @pytest.mark.parametrize("mode,iters,out,want", [
     (0, 10, 0, 1),            # null output
-    (5, 10, FAKE, 2), (-1, 10, FAKE, 2),
+    (11, 10, FAKE, 2), (-1, 10, FAKE, 2),
     (0, 0, FAKE, 2), (0, (1 << 20) + 1, FAKE, 2),
 ])
 def test_probe_mfma_valu_validation(mode, iters, out, want):

@@ -58,7 +58,9 @@ constexpr int kOvlFma = 64;     // fp32 FMAs per round
 // then an FMA block per round; 3: waves 0-3 MFMA blocks only, waves 4-7 FMA
 // blocks only (one of each kind per SIMD); 4: as 2 with a workgroup barrier
 // after every round (the waves of a SIMD kept in the same phase, as a GEMM's
-// group barrier keeps them).
+// group barrier keeps them); 5, 6, 7: as 2, 0, 1 with waves 4-7 idle (one
+// wave per SIMD); 8, 9, 10: as 2, 0, 1 with twice the workgroups (two per
+// CU: four waves per SIMD).
 __global__ __launch_bounds__(kOvlThreads) void msd_probe_mfma_valu_kernel(int mode, int iters,
                                                                          float* __restrict__ out) {
   const int lane = threadIdx.x & 63;
@@ -75,8 +77,15 @@ __global__ __launch_bounds__(kOvlThreads) void msd_probe_mfma_valu_kernel(int mo
 #pragma unroll
   for (int i = 0; i < 16; ++i) x[i] = (float)(lane + i) * 0.001f;
   const float m = 0.999f, c = 0.001f;
-  const bool do_mfma = mode == 0 || mode == 2 || mode == 4 || (mode == 3 && wave < 4);   // wave-uniform
-  const bool do_fma = mode == 1 || mode == 2 || mode == 4 || (mode == 3 && wave >= 4);
+  const bool one_per_simd = mode >= 5 && mode <= 7;
+  const bool do_mfma = mode == 0 || mode == 2 || mode == 4 || mode == 5 || mode == 6 ||
+                       mode == 8 || mode == 9 || (mode == 3 && wave < 4);   // wave-uniform
+  const bool do_fma = mode == 1 || mode == 2 || mode == 4 || mode == 5 || mode == 7 ||
+                      mode == 8 || mode == 10 || (mode == 3 && wave >= 4);
+  if (one_per_simd && wave >= 4) {   // idle waves write their slot and leave
+    out[(int64_t)blockIdx.x * kOvlThreads + threadIdx.x] = 0.f;
+    return;
+  }
   for (int it = 0; it < iters; ++it) {
     if (do_mfma) {
 #pragma unroll
@@ -103,8 +112,9 @@ __global__ __launch_bounds__(kOvlThreads) void msd_probe_mfma_valu_kernel(int mo
 
 extern "C" int wqbmm_probe_mfma_valu(int mode, int iters, void* out, void* stream) {
   if (!out) return 1;
-  if (mode < 0 || mode > 4 || iters < 1 || iters > (1 << 20)) return 2;
-  hipLaunchKernelGGL(msd_probe_mfma_valu_kernel, dim3(kOvlBlocks), dim3(kOvlThreads), 0,
+  if (mode < 0 || mode > 10 || iters < 1 || iters > (1 << 20)) return 2;
+  const unsigned blocks = mode >= 8 ? 2 * kOvlBlocks : kOvlBlocks;
+  hipLaunchKernelGGL(msd_probe_mfma_valu_kernel, dim3(blocks), dim3(kOvlThreads), 0,
                      static_cast<hipStream_t>(stream), mode, iters, static_cast<float*>(out));
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
