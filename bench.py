@@ -94,10 +94,12 @@ def kernels_of(path, M, K, N, gs):
 
 def prefill_bn(M, N):
     """Column block of the group-128 GEMM (msd_prefill.hip prefill_layout):
-    256 when its rounds of 256 workgroups cost less, a 256-column tile
-    counting 7/4 of a 128-column one."""
+    64 for at most 32 tiles of 128 columns; else 256 when its rounds of 256
+    workgroups cost less, a 256-column tile counting 7/4 of a 128-column one."""
     mb = -(-M // 128)
     t256, t128 = mb * -(-N // 256), mb * -(-N // 128)
+    if t128 <= 32:
+        return 64
     return 256 if (t128 >= 256 and -(-t256 // 256) * 7 < -(-t128 // 256) * 4) else 128
 
 

@@ -310,21 +310,22 @@ __global__ __launch_bounds__(pf::THREADS, 1) void msd_gemm_kernel(
     uint16_t* __restrict__ y, int32_t* __restrict__ y_int, float* __restrict__ part) {
   using namespace pf;
   constexpr int CT = BN / 16;                          // column tiles per block
-  constexpr int NT = CT / WAVES_N;                     // column tiles per wave: 8 or 4
+  constexpr int NT = CT / WAVES_N;                     // column tiles per wave: 8, 4 or 2
   constexpr int WN = NT * 16;                          // columns per wave
   constexpr int B_GROUP = CT * TILE;                   // one group of a column block
   constexpr int A_KB = A_GROUP / 1024;                 // 36 pieces of 1 KB
-  constexpr int PIECES = A_KB + B_GROUP / 1024;        // 60 or 48
+  constexpr int PIECES = A_KB + B_GROUP / 1024;        // 60, 48 or 42
   constexpr int CPW = (PIECES + WAVES - 1) / WAVES;    // pieces per wave: 8 or 6
   constexpr int QW = Q_GROUP / 256;                    // 256-byte copies of the weights: 6
-  constexpr int SW = BN * 2 / 256;                     // 256-byte copies of the scales: 2 or 1
+  constexpr int SW = (BN * 2 + 255) / 256;             // 256-byte copies of the scales: 2 or 1
+  constexpr int SN = SW * 128;                         // scales copied per group (>= BN)
   static_assert(QW + SW <= WAVES, "one small copy per wave");
   static_assert(B_GROUP % 1024 == 0, "whole pieces");
 
   // Named buffers (not one array indexed by the group) so that the copies
   // into one and the reads of another are visibly disjoint.  128-column
   // blocks have three (149 KB of LDS: the copies run two groups ahead),
-  // 256-column blocks two (a third would not fit).
+  // 256- and 64-column blocks two (a third would not fit at 256).
   constexpr int NBUF = BN == 128 ? 3 : 2;
   __shared__ __attribute__((aligned(16))) uint8_t sA0[A_GROUP];
   __shared__ __attribute__((aligned(16))) uint8_t sA1[A_GROUP];
@@ -335,9 +336,9 @@ __global__ __launch_bounds__(pf::THREADS, 1) void msd_gemm_kernel(
   __shared__ __attribute__((aligned(16))) float sQ0[3 * BM];
   __shared__ __attribute__((aligned(16))) float sQ1[3 * BM];
   __shared__ __attribute__((aligned(16))) float sQ2[NBUF == 3 ? 3 * BM : 4];
-  __shared__ __attribute__((aligned(16))) uint16_t sS0[BN];
-  __shared__ __attribute__((aligned(16))) uint16_t sS1[BN];
-  __shared__ __attribute__((aligned(16))) uint16_t sS2[NBUF == 3 ? BN : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t sS0[SN];
+  __shared__ __attribute__((aligned(16))) uint16_t sS1[SN];
+  __shared__ __attribute__((aligned(16))) uint16_t sS2[NBUF == 3 ? SN : 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -559,7 +560,7 @@ __global__ __launch_bounds__(pf::THREADS, 1) void msd_gemm_kernel(
     static_assert(4 * WM * YS <= A_GROUP && WN * 2 <= YS - 16, "staging fits the A buffers");
     uint8_t* st = (wave < 4 ? sA0 : sA1) + (wave % 4) * (WM * YS);
     if (splits > 1) {
-      if constexpr (BN == 128) {                         // a split GEMM has 128-column blocks
+      if constexpr (BN <= 128) {                         // a split GEMM has 128- or 64-column blocks
         static_assert(WN * 4 <= YS - 16, "fp32 rows fit the stride");
 #pragma unroll
         for (int r = 0; r < MT; ++r)
@@ -640,7 +641,7 @@ void set_splits(PrefillLayout& L, int64_t tiles, int64_t G, int64_t M, int64_t N
   L.part_bytes = L.splits > 1 ? (size_t)L.splits * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
-// Column blocks of 256 or 128.  The GEMM holds one workgroup per CU, so its
+// Column blocks of 256, 128 or 64.  The GEMM holds one workgroup per CU, so its
 // time is about (rounds of 256 workgroups) x (one workgroup's time), and a
 // 128 x 256 tile takes about 7/4 of a 128 x 128 one (72 against 41 us per
 // tile at K = 4096, measured).  256-column blocks when their rounds cost less
@@ -653,6 +654,11 @@ PrefillLayout prefill_layout(int gs, int64_t M, int64_t K, int64_t N) {
   const int64_t mb = L.mpad / pf::BM;
   const int64_t t256 = mb * ((N + 255) / 256), t128 = mb * ((N + 127) / 128);
   L.bn = (t128 >= 256 && ((t256 + 255) / 256) * 7 < ((t128 + 255) / 256) * 4) ? 256 : 128;
+  // At most 32 tiles of 128 columns (eight or more K-splits at K = 4096):
+  // 64-column blocks halve the splits for the same workgroups, and with them
+  // the fp32 partial sums (M = 128, K = N = 4096: 24.4 -> 22.4 us; with 64 or
+  // more tiles of 128 they were slower: M = 256, 29.2 against 28.5 us).
+  if (t128 <= 32) L.bn = 64;
   L.npad = (N + L.bn - 1) / L.bn * L.bn;
   const int64_t G = K / gs;
   L.a_bytes = (size_t)(3 * (L.mpad / 16) * G) * pf::TILE;
@@ -714,7 +720,7 @@ hipError_t launch_prefill_gemm(const uint8_t* a_t, const float* q_t, const uint8
   if (gs == 64)
     return launch_prefill64_gemm(a_t, q_t, b_t, w_tiled, scale, M, K, N, L, g_begin, g_end, y, y_int,
                                  stream);
-  if (L.bn != 128 && L.bn != 256) return hipErrorInvalidValue;
+  if (L.bn != 64 && L.bn != 128 && L.bn != 256) return hipErrorInvalidValue;
   const int mblocks = (int)(L.mpad / pf::BM);
   const int nblocks = (int)(L.npad / L.bn);
   // the layout's split count over this group range (a Y_int export needs no
@@ -723,9 +729,9 @@ hipError_t launch_prefill_gemm(const uint8_t* a_t, const float* q_t, const uint8
   int64_t splits = std::min<int64_t>(L.splits, range);
   const int64_t gps = (range + splits - 1) / splits;
   splits = (range + gps - 1) / gps;
-  // (a split GEMM stages its fp32 partial sums for 128-column blocks only;
-  // the layout splits only below 256 tiles, where the blocks are 128 wide)
-  if (splits > 1 && !y_int && (!part || splits > L.splits || L.bn != 128)) return hipErrorInvalidValue;
+  // (a split GEMM stages its fp32 partial sums for 128- and 64-column blocks;
+  // the layout splits only below 256 tiles, where the blocks are that wide)
+  if (splits > 1 && !y_int && (!part || splits > L.splits || L.bn > 128)) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(mblocks * nblocks * splits));
   const uint16_t* sp = static_cast<const uint16_t*>(scale);
   uint16_t* yp = static_cast<uint16_t*>(y);
@@ -736,7 +742,9 @@ hipError_t launch_prefill_gemm(const uint8_t* a_t, const float* q_t, const uint8
                      q_t, b_t, sp, m, mp, k, n, gb, ge, mblocks, nblocks, S, GPS, yp, y_int, part)
 #define WQBMM_GEMM_BN(GS_, Y_)                                                                   \
   do {                                                                                           \
-    if (L.bn == 256) WQBMM_GEMM_LAUNCH(GS_, 256, Y_); else WQBMM_GEMM_LAUNCH(GS_, 128, Y_);       \
+    if (L.bn == 256) WQBMM_GEMM_LAUNCH(GS_, 256, Y_);                                           \
+    else if (L.bn == 128) WQBMM_GEMM_LAUNCH(GS_, 128, Y_);                                      \
+    else WQBMM_GEMM_LAUNCH(GS_, 64, Y_);                                                        \
   } while (0)
   if (y_int) WQBMM_GEMM_BN(128, true); else WQBMM_GEMM_BN(128, false);
 #undef WQBMM_GEMM_BN
