@@ -589,14 +589,16 @@ def shapes(torch, W, shape_list, steps, warmup):
     return rows
 
 
-SWEEP_M = [8, 12, 16, 24, 32, 48, 64, 96, 128]
-SWEEP_SHAPES = [("K4096_N4096_g128", 4096, 4096, 128), ("K8192_N28672_g64", 8192, 28672, 64)]
+SWEEP_M = [8, 12, 16, 24, 32, 48, 64, 80, 96, 128]
+SWEEP_SHAPES = [("K4096_N4096_g128", 4096, 4096, 128), ("K4096_N11008_g128", 4096, 11008, 128),
+                ("K8192_N28672_g64", 8192, 28672, 64)]
 
 
 def sweep(torch, W, args):
     """Decode-vs-prefill split: the step time of each kernel path at
-    M = 8..128 on the decode shape (K = N = 4096, group size 128) and the
-    outlier shape (K = 8192, N = 28672, group size 64), MALL-cold as above,
+    M = 8..128 on the decode shape (K = N = 4096, group size 128), a wider
+    group-128 shape (K = 4096, N = 11008) and the outlier shape (K = 8192,
+    N = 28672, group size 64), MALL-cold as above,
     with each path's kernels timed alone (the group-128 prefill path with the
     weights' operand form).  Returns a list of rows."""
     from weight_only_quantized_msd_amd import datagen  # noqa: F401

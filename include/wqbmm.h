@@ -49,7 +49,7 @@
  *     N >= 1, K % group_size == 0, N % 32 == 0, M <= 2^24, K <= 2^20,
  *     N <= 2^20, every pointer 16-byte aligned.
  *   - group_size must be 64 or 128 (other positive values: WQBMM_ERR_UNSUPPORTED).
- *   - Workspace.  The two-kernel paths (decode at 4 < M <= 64, prefill) pass
+ *   - Workspace.  The two-kernel paths (decode at 4 < M <= 96, prefill) pass
  *     operands between their kernels through device memory, and the fused
  *     decode kernel (M <= 4) with K > 4096 sums its K-splits in accumulators.
  *     The library keeps that memory per (device, stream): allocated on first
@@ -91,7 +91,7 @@ typedef enum wqbmm_status {
 /* Kernel path selector for the *_path / *_yint entry points. */
 typedef enum wqbmm_path {
   WQBMM_PATH_AUTO = 0,     /* what wqbmm_a16w4_msd picks (wqbmm_select_path)      */
-  WQBMM_PATH_DECODE = 1,   /* weight-streaming kernels; valid for M <= 64        */
+  WQBMM_PATH_DECODE = 1,   /* weight-streaming kernels; valid for M <= 96        */
   WQBMM_PATH_PREFILL = 2   /* operand preparation + MFMA GEMM; any M            */
 } wqbmm_path;
 
@@ -127,7 +127,7 @@ wqbmm_status wqbmm_a16w4_msd(const void* x, const void* w_tiled,
                              void* stream);
 
 /* Same operation with an explicit kernel path (WQBMM_PATH_*).  The decode
- * path with M > 64 returns WQBMM_ERR_INVALID. */
+ * path with M > 96 returns WQBMM_ERR_INVALID. */
 wqbmm_status wqbmm_a16w4_msd_path(const void* x, const void* w_tiled,
                                   const void* antiquant_scale, int64_t group_size,
                                   int64_t M, int64_t K, int64_t N, void* y,
@@ -247,8 +247,9 @@ wqbmm_status wqbmm_a16w4_msd_profile_stage(const void* x, const void* w_tiled,
                                            int path, int stage, void* stream);
 
 /* The path wqbmm_a16w4_msd takes for this shape (WQBMM_PATH_DECODE or
- * WQBMM_PATH_PREFILL): decode for M <= 48, and for M <= 64 at group size
- * 128; prefill otherwise (set from a measured sweep of both paths over M).
+ * WQBMM_PATH_PREFILL): decode for M <= 48; at group size 128 also for
+ * M <= 96 when K*N <= 2^24 and for M <= 64 when K*N <= 3*2^24; prefill
+ * otherwise (set from measured sweeps of both paths over M and shape).
  * Pure host function. */
 int wqbmm_select_path(int64_t M, int64_t K, int64_t N, int64_t group_size);
 

@@ -52,7 +52,13 @@ def test_select_path():
     assert L.wqbmm_select_path(48, 8192, 28672, 64) == L.WQBMM_PATH_DECODE
     assert L.wqbmm_select_path(49, 8192, 28672, 64) == L.WQBMM_PATH_PREFILL
     assert L.wqbmm_select_path(64, 4096, 4096, 128) == L.WQBMM_PATH_DECODE
-    assert L.wqbmm_select_path(65, 4096, 4096, 128) == L.WQBMM_PATH_PREFILL
+    assert L.wqbmm_select_path(96, 4096, 4096, 128) == L.WQBMM_PATH_DECODE
+    assert L.wqbmm_select_path(97, 4096, 4096, 128) == L.WQBMM_PATH_PREFILL
+    assert L.wqbmm_select_path(65, 4096, 4096, 64) == L.WQBMM_PATH_PREFILL
+    assert L.wqbmm_select_path(64, 4096, 11008, 128) == L.WQBMM_PATH_DECODE
+    assert L.wqbmm_select_path(65, 4096, 11008, 128) == L.WQBMM_PATH_PREFILL
+    assert L.wqbmm_select_path(49, 8192, 8192, 128) == L.WQBMM_PATH_PREFILL
+    assert L.wqbmm_select_path(48, 8192, 8192, 128) == L.WQBMM_PATH_DECODE
     assert L.wqbmm_select_path(2048, 4096, 4096, 128) == L.WQBMM_PATH_PREFILL
 
 
@@ -93,7 +99,7 @@ def test_msd_validation(name, over, want):
 @pytest.mark.parametrize("path,M,want", [
     (3, 4, L.WQBMM_ERR_INVALID),            # unknown path
     (-1, 4, L.WQBMM_ERR_INVALID),
-    (L.WQBMM_PATH_DECODE, 65, L.WQBMM_ERR_INVALID),   # decode kernels cover M <= 64
+    (L.WQBMM_PATH_DECODE, 97, L.WQBMM_ERR_INVALID),   # decode kernels cover M <= 96
     (L.WQBMM_PATH_DECODE, 0, L.WQBMM_OK),
     (L.WQBMM_PATH_PREFILL, 0, L.WQBMM_OK),
 ])
@@ -124,7 +130,7 @@ def test_prepass_validation(over, want):
     (dict(ge=5), L.WQBMM_ERR_INVALID),          # K/gs = 4 groups
     (dict(gb=2, ge=2), L.WQBMM_ERR_INVALID),    # empty range
     (dict(gb=3, ge=1), L.WQBMM_ERR_INVALID),
-    (dict(path=L.WQBMM_PATH_DECODE, M=65), L.WQBMM_ERR_INVALID),
+    (dict(path=L.WQBMM_PATH_DECODE, M=97), L.WQBMM_ERR_INVALID),
     (dict(M=0), L.WQBMM_OK),
 ])
 def test_yint_validation(over, want):
@@ -145,7 +151,7 @@ def test_yint_validation(over, want):
     (dict(gs=96, K=192), L.WQBMM_ERR_UNSUPPORTED),
     (dict(path=3), L.WQBMM_ERR_INVALID),
     (dict(path=-1), L.WQBMM_ERR_INVALID),
-    (dict(path=L.WQBMM_PATH_DECODE, M=65), L.WQBMM_ERR_INVALID),
+    (dict(path=L.WQBMM_PATH_DECODE, M=97), L.WQBMM_ERR_INVALID),
     (dict(M=0, x=0, y=0), L.WQBMM_OK),
 ])
 def test_profile_stage_validation(over, want):

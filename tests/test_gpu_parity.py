@@ -246,7 +246,8 @@ def test_y_within_tolerance(torch_dev, name, path, nrows):
 RAGGED = [  # (M, K, N, gs)
     (1, 64, 32, 64), (2, 128, 96, 128), (3, 192, 160, 64), (4, 640, 288, 128),
     (5, 576, 4128, 64), (13, 1024, 416, 128), (16, 2560, 544, 128), (17, 512, 160, 64),
-    (40, 1152, 224, 128), (64, 704, 96, 64), (65, 512, 160, 128),
+    (40, 1152, 224, 128), (64, 704, 96, 64), (65, 512, 160, 128), (81, 768, 96, 64),
+    (96, 1152, 224, 128),
     (130, 384, 288, 128), (257, 256, 128, 64),
     # M <= 4 with K split over workgroups and a last chunk that ends inside it
     (1, 4736, 96, 64), (3, 6272, 160, 128),
@@ -267,7 +268,7 @@ def test_ragged_shapes(torch_dev, M, K, N, gs):
     ra, _ = oracle.decompose(d["x"], gs)
     G = K // gs
     ref_yi = oracle.yint(ra, d["w"], gs, 0, G)
-    paths = (DECODE, PREFILL) if M <= 64 else (PREFILL,)
+    paths = (DECODE, PREFILL) if M <= 96 else (PREFILL,)
     bound = elementwise_bound(d)
     for p in paths:
         announce(f"ragged M={M} K={K} N={N} gs={gs} path={p}")
@@ -279,17 +280,20 @@ def test_ragged_shapes(torch_dev, M, K, N, gs):
         assert np.array_equal(yi.cpu().numpy(), ref_yi), f"path {p} Y_int"
 
 
-# The decode contraction for 4 < M <= 64 (operand kernel + full-K contraction,
+# The decode contraction for 4 < M <= 96 (operand kernel + full-K contraction,
 # rows in slices of 16): K beyond 4096 (several load rounds per wave), a
 # single 128-row block, K not a multiple of 128 at group size 64, Y_int over
 # group ranges that start and end inside a 128-row block, and every slice
-# count with full and ragged last slices (M = 17, 31, 32, 33, 48, 63, 64).
+# count with full and ragged last slices (M = 17, 31, 32, 33, 48, 63, 64, 65,
+# 80, 93, 96).
 GEMV_CASES = [  # (M, K, N, gs, g_begin, g_end)
     (16, 8192, 512, 128, 0, 64), (8, 12288, 256, 128, 37, 91), (16, 8192, 384, 64, 5, 118),
     (5, 64, 96, 64, 0, 1), (9, 128, 64, 128, 0, 1), (12, 320, 160, 64, 1, 4),
     (17, 4096, 512, 128, 0, 32), (31, 2048, 256, 64, 3, 29), (32, 8192, 384, 128, 11, 60),
     (33, 1024, 288, 128, 0, 8), (48, 4096, 256, 64, 0, 64), (63, 640, 160, 64, 1, 9),
     (64, 4096, 512, 128, 0, 32), (64, 12288, 128, 64, 90, 150),
+    (65, 2048, 256, 128, 0, 16), (80, 4096, 160, 64, 7, 53), (93, 640, 96, 64, 1, 9),
+    (96, 4096, 512, 128, 0, 32), (96, 8192, 384, 64, 20, 110),
 ]
 
 
@@ -626,7 +630,7 @@ def test_profile_stages_compose_to_path(torch_dev, name, path):
     with pytest.raises(W.WqbmmError):
         W.wqbmm_a16w4_msd_profile_stage(x[: max(1, d["M"] // 2)].contiguous(), w, s, gs, 2, path=path)
     other = PREFILL if path == DECODE else DECODE
-    if d["M"] <= 64:   # operands of the other path are not these
+    if d["M"] <= 96:   # operands of the other path are not these
         W.wqbmm_a16w4_msd_profile_stage(x, w, s, gs, 1, path=other)
         with pytest.raises(W.WqbmmError):
             W.wqbmm_a16w4_msd_profile_stage(x, w, s, gs, 2, path=path)

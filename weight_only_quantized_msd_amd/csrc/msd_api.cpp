@@ -30,7 +30,7 @@ using wqbmm::DecodePlan;
 constexpr int64_t kMaxM = int64_t(1) << 24;
 constexpr int64_t kMaxK = int64_t(1) << 20;
 constexpr int64_t kMaxN = int64_t(1) << 20;
-constexpr int kDecodeMaxM = 64;
+constexpr int kDecodeMaxM = 96;
 
 // NULL counts as aligned: it is only accepted where the array is empty (M == 0).
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -329,19 +329,29 @@ wqbmm_status run(const void* x, const void* w, const void* w_op, const void* sca
 
 extern "C" {
 
-// The split between the two kernel paths, from the M sweep of both paths
-// (MALL-cold step time, one MI355X):
-//   K = N = 4096, group size 128: decode 7.9 / 9.8 / 11.8 / 13.4 us at
-//     M = 16 / 32 / 48 / 64 against the prefill path's 53-54 us at every M
-//     up to 128 (one 128-row block);
-//   K = 8192, N = 28672, group size 64: decode 42.3 / 62.2 / 84.2 / 129.6 us
-//     at M = 16 / 32 / 48 / 64 against prefill 111-113 us.
-// Decode up to 48 rows everywhere; from 49 to 64 rows only at group size
-// 128 (at group size 64 the four-slice contraction, 3 waves per SIMD, loses).
+// The split between the two kernel paths, from sweeps of both paths over M
+// (MALL-cold step time, one MI355X; the group-128 prefill path with the
+// weights' operand form).  The decode contraction's cost grows with the row
+// slices (every column tile reads every slice's level chunks) times the
+// rounds of column tiles; the prefill path's stays about flat up to one
+// 128-row block:
+//   K = N = 4096, group size 128: decode 7.6 / 9.8 / 11.9 / 13.3 / 15.9 /
+//     17.5 us at M = 16 / 32 / 48 / 64 / 80 / 96 against prefill 16-21 us;
+//   K = 4096, N = 11008: decode 16.7 / 21.7 / 29.2 / 35.2 us at M = 32 / 48 /
+//     64 / 80 against prefill 31-32 us;
+//   K = 4096, N = 14336 and K = N = 8192: decode 26-27 us at M = 48, 35-37 us
+//     at 64, against prefill 31-32 us;
+//   K = 8192, N = 28672, group size 64: decode 41 / 63 / 85 / 128 us at M =
+//     16 / 32 / 48 / 64 against prefill 110-111 us.
+// Decode up to 48 rows everywhere; at group size 128 up to 96 rows for at
+// most 2^24 weights and up to 64 for at most 3 * 2^24.
 int wqbmm_select_path(int64_t M, int64_t K, int64_t N, int64_t group_size) {
-  (void)K; (void)N;
   if (M <= 48) return WQBMM_PATH_DECODE;
-  if (M <= kDecodeMaxM && group_size == 128) return WQBMM_PATH_DECODE;
+  if (group_size == 128) {
+    const int64_t weights = K * N;
+    if (M <= 96 && weights <= (int64_t(1) << 24)) return WQBMM_PATH_DECODE;
+    if (M <= 64 && weights <= 3 * (int64_t(1) << 24)) return WQBMM_PATH_DECODE;
+  }
   return WQBMM_PATH_PREFILL;
 }
 

@@ -1,4 +1,4 @@
-// msd_decode_gemv.hip -- the MSD matmul for 4 < M <= 64 as two kernels: x is
+// msd_decode_gemv.hip -- the MSD matmul for 4 < M <= 96 as two kernels: x is
 // decomposed ONCE into int4-packed MFMA operands, then a GEMV-shaped
 // contraction streams the weights with every workgroup covering whole K.
 //
@@ -19,7 +19,7 @@
 //   wave      = a contiguous run of 128-row blocks (WK waves split K),
 //   reduction = the WK waves' fp32 sums added in LDS in a fixed order.
 //
-// Rows of x come in slices of 16 (R = ceil(M/16) <= 4 slices): each weight
+// Rows of x come in slices of 16 (R = ceil(M/16) <= 6 slices): each weight
 // chunk a wave loads is the MFMA operand of all R slices, so the weights are
 // streamed once whatever M is, while the level operands (every row of x, for
 // every column tile) grow with R.
@@ -486,7 +486,7 @@ __global__ __launch_bounds__(64 * WK) void msd_decode_gemv_multi_kernel(
 namespace dg {
 constexpr int WK = 8;    // waves per workgroup (K split within the workgroup)
 constexpr int KBW = 4;   // 128-row blocks per wave and load round
-constexpr int kMaxSlices = 4;
+constexpr int kMaxSlices = 6;
 constexpr int kCUs = 256;   // column tiles beyond this: the multi-tile contraction
 }  // namespace dg
 
@@ -559,7 +559,9 @@ hipError_t launch_decode_gemv(const void* x, const void* w, const void* scale, i
       case 1: WQBMM_GEMV_LAUNCH(GS_, 1, Y_); break;                                                 \
       case 2: WQBMM_GEMV_LAUNCH(GS_, 2, Y_); break;                                                 \
       case 3: WQBMM_GEMV_LAUNCH(GS_, 3, Y_); break;                                                 \
-      default: WQBMM_GEMV_LAUNCH(GS_, 4, Y_); break;                                                \
+      case 4: WQBMM_GEMV_LAUNCH(GS_, 4, Y_); break;                                                 \
+      case 5: WQBMM_GEMV_LAUNCH(GS_, 5, Y_); break;                                                 \
+      default: WQBMM_GEMV_LAUNCH(GS_, 6, Y_); break;                                                \
     }                                                                                               \
   } while (0)
   if (gs == 64) {

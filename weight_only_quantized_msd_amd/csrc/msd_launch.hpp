@@ -101,7 +101,7 @@ hipError_t launch_decode(const void* x, const void* w, const void* scale, int gs
                          int64_t K, int64_t N, int64_t g_begin, int64_t g_end, void* y,
                          int32_t* y_int, uint64_t* accum, const DecodePlan& plan, hipStream_t stream);
 
-// Decode for 4 < M <= 64 (msd_decode_gemv.hip): an operand kernel decomposes
+// Decode for 4 < M <= 96 (msd_decode_gemv.hip): an operand kernel decomposes
 // x once into int4-packed level operands (slices of 16 rows) and level
 // weights in `ws` (decode_gemv_workspace_bytes), then a contraction kernel
 // covers all of K per 16-column tile (no K-split hand-off).  stage 0: both
