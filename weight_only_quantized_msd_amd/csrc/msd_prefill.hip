@@ -490,17 +490,27 @@ __global__ __launch_bounds__(pf::THREADS, 1) void msd_gemm_kernel(
     // ones.  While a group is computed from one buffer, the next group is
     // copied into the other; each wave waits for its own copies, and the
     // barrier then publishes all of them and frees the buffer just read.
+    // At 64-column blocks a scheduling barrier keeps the wait after the whole
+    // group's compute: the compiler otherwise hoists it above the last third
+    // of the group's MFMAs (they touch no memory), and the wave waits on its
+    // copies early (M = 96 and 128 at K = N = 4096: GEMM 17.6 -> 16.6 and
+    // 18.5 -> 17.6 us).  At 256-column blocks the hoisted form is faster
+    // (prefill_m2048 GEMM 73.2 against 73.4 us, M = 1536 67.6 against 68.9):
+    // there the MFMAs left after the barrier overlap the next group's
+    // operand reads.
     dma(g_lo, sA0, sB0, sQ0, sS0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int g = g_lo; g < g_hi; g += 2) {
       if (g + 1 < g_hi) dma(g + 1, sA1, sB1, sQ1, sS1);
       compute(sA0, sB0, sQ0, sS0, g);
+      if constexpr (BN == 64) __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (g + 1 >= g_hi) break;
       if (g + 2 < g_hi) dma(g + 2, sA0, sB0, sQ0, sS0);
       compute(sA1, sB1, sQ1, sS1, g + 1);
+      if constexpr (BN == 64) __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
