@@ -51,9 +51,9 @@
 //        alone, so it is either written by the preparation kernel on each
 //        call or converted once and kept (the weights' operand form); its
 //        columns are padded to a multiple of 256 either way.
-//   Q_t: [group][row block][level][128 rows] fp32: A_max * w_l, the row's
-//        step-10 weight of level l (w_l = 1/7.49, 1/(7.49*14.98),
-//        1/(7.49*14.98^2)), formed once per (row, group)
+//   Q_t: [group][row block][128 rows] fp32: A_max * w_1 (w_1 = 1/7.49), the
+//        row's step-10 weight of level 1, formed once per (row, group); the
+//        GEMM weighs levels 2 and 3 by the constant ratio k = 1/14.98
 //   Rows beyond M and columns beyond N hold zeros (written by the prep
 //   kernel), so the operands of one group of a workgroup tile are two
 //   contiguous runs: 36 KB of A and BN/16 * 1.5 KB of B.
@@ -64,8 +64,9 @@
 // operands and the rows' weights for the group and walks its column tiles,
 // reading the next column tile's B operand while the current one is used:
 // per output tile 3 MFMAs, with the fp32 combine of the previous output tile
-// interleaved (4 VALU per output and group: three for the levels, one for
-// the scale and the running sum).  The operand reads from LDS are the
+// interleaved (4 VALU per output and group: Y1 + k*(Y2 + k*Y3) with k =
+// 1/14.98 in two, the row's A_max*w_1 in one, the scale and the running sum
+// in one).  The operand reads from LDS are the
 // GEMM's largest cost after the MFMA and the combine (FP6 MFMA and VALU
 // issue overlap only partly on a SIMD, the less the more often the waves are
 // realigned by a barrier): a wave reads 6 A + NT B tiles per group, the
@@ -100,7 +101,7 @@ constexpr int TILE = 1536;     // bytes of one operand tile (16 x 128 k, e2m3)
 constexpr int TILE_LO = 1024;  // its [lane][dwords 0-3] part
 constexpr int TILE_HI = 512;   // its [lane][dwords 4-5] part
 constexpr int A_GROUP = 3 * RT * TILE;   // one group of a row block: 36 KB
-constexpr int Q_GROUP = 3 * BM * 4;      // level weights of a row block: 1.5 KB
+constexpr int Q_GROUP = BM * 4;          // level-1 weights of a row block: 512 bytes
 constexpr int NXCD = 8;
 constexpr int BAND = 4;        // row blocks per band of the tile order
 }  // namespace pf
@@ -111,10 +112,10 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-// Step-10 level weights for exact integer Y_l (no unpack scaling here).
+// Step-10 level weights for exact integer Y_l (no unpack scaling here): w_1
+// per row (times A_max), and the ratio of consecutive level weights.
 constexpr float kE1 = (float)(1.0 / (double)kF1);
-constexpr float kE2 = (float)(1.0 / (double)(kF1 * kF2));
-constexpr float kE3 = (float)(1.0 / (double)(kF1 * kF2 * kF2));
+constexpr float kK = (float)(1.0 / (double)kF2);   // 1/14.98: w_2/w_1 and w_3/w_2
 
 // E8M0 block scales of the MFMA: 2^0 for A (levels as they are), 2^1 for B
 // (weights stored halved).
@@ -143,7 +144,7 @@ __device__ __forceinline__ v6i pack_e2m3(const v16f& u, const v16f& v, float div
 // TPW x 16 x GS elements, one row tile after the other.  Lane l takes row
 // l/4 and, with kq = l%4, the elements of operand lane 16*kq + row (u: k =
 // 16*kq + j, v: k = 64 + 16*kq + j), so a group's maximum is a 4-lane
-// reduction; the rows' level weights A_max * w_l go to Q_t.  Per row tile
+// reduction; the rows' level-1 weights A_max * w_1 go to Q_t.  Per row tile
 // and level a wave stores dwords 0-3 (16 bytes per lane) and dwords 4-5 (8
 // bytes per lane) into their parts of the tile pair.  A wave issues the loads
 // of all its TPW row tiles before it decomposes the first.  (The launcher
@@ -226,10 +227,8 @@ __global__ __launch_bounds__(256) void msd_prep_kernel(const uint16_t* __restric
         *reinterpret_cast<v4i*>(pair + p * TILE_LO + slot * 16) = v4i{pk[0], pk[1], pk[2], pk[3]};
         *reinterpret_cast<v2i*>(pair + 2 * TILE_LO + p * TILE_HI + slot * 8) = v2i{pk[4], pk[5]};
       }
-      if (kq < 3) {                                  // lanes kq = 0, 1, 2: level weight kq of row m
-        const float w = kq == 0 ? kE1 : (kq == 1 ? kE2 : kE3);
-        q_t[(((int64_t)g * (Mpad / BM) + rb) * 3 + kq) * BM + (m % BM)] = amax * w;
-      }
+      if (kq == 0)                                   // the row's level-1 weight
+        q_t[((int64_t)g * (Mpad / BM) + rb) * BM + (m % BM)] = amax * kE1;
     }
     return;
   }
@@ -316,7 +315,7 @@ __global__ __launch_bounds__(pf::THREADS, 1) void msd_gemm_kernel(
   constexpr int A_KB = A_GROUP / 1024;                 // 36 pieces of 1 KB
   constexpr int PIECES = A_KB + B_GROUP / 1024;        // 60, 48 or 42
   constexpr int CPW = (PIECES + WAVES - 1) / WAVES;    // pieces per wave: 8 or 6
-  constexpr int QW = Q_GROUP / 256;                    // 256-byte copies of the weights: 6
+  constexpr int QW = Q_GROUP / 256;                    // 256-byte copies of the level-1 weights: 2
   constexpr int SW = (BN * 2 + 255) / 256;             // 256-byte copies of the scales: 2 or 1
   constexpr int SN = SW * 128;                         // scales copied per group (>= BN)
   static_assert(QW + SW <= WAVES, "one small copy per wave");
@@ -333,9 +332,9 @@ __global__ __launch_bounds__(pf::THREADS, 1) void msd_gemm_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t sB0[B_GROUP];
   __shared__ __attribute__((aligned(16))) uint8_t sB1[B_GROUP];
   __shared__ __attribute__((aligned(16))) uint8_t sB2[NBUF == 3 ? B_GROUP : 16];
-  __shared__ __attribute__((aligned(16))) float sQ0[3 * BM];
-  __shared__ __attribute__((aligned(16))) float sQ1[3 * BM];
-  __shared__ __attribute__((aligned(16))) float sQ2[NBUF == 3 ? 3 * BM : 4];
+  __shared__ __attribute__((aligned(16))) float sQ0[BM];
+  __shared__ __attribute__((aligned(16))) float sQ1[BM];
+  __shared__ __attribute__((aligned(16))) float sQ2[NBUF == 3 ? BM : 4];
   __shared__ __attribute__((aligned(16))) uint16_t sS0[SN];
   __shared__ __attribute__((aligned(16))) uint16_t sS1[SN];
   __shared__ __attribute__((aligned(16))) uint16_t sS2[NBUF == 3 ? SN : 8];
@@ -373,7 +372,7 @@ __global__ __launch_bounds__(pf::THREADS, 1) void msd_gemm_kernel(
   // Group g_'s operands -> LDS by DMA (global_load_lds, 16 bytes per lane:
   // lane i's bytes land at the destination + 16*i, so a 1 KB piece keeps its
   // layout).  Pieces [0, 36) are the block's A run, the rest its B run.  The
-  // level weights (fp32) and the scales (fp16 pairs) go 4 bytes per lane, one
+  // level-1 weights (fp32) and the scales (fp16 pairs) go 4 bytes per lane, one
   // 256-byte copy per wave.  (The 4-byte copies take byte pointers: typed
   // float pointers made the compiler crash in its SGPR-copy pass.)
   const uint8_t* a_run = a_t + (int64_t)rb * G * A_GROUP;
@@ -411,8 +410,11 @@ __global__ __launch_bounds__(pf::THREADS, 1) void msd_gemm_kernel(
       for (int i = 0; i < 4; ++i) yacc[r][c][i] = 0.0f;
 
   // Steps 10-11 for output tile (row tile PR, column tile PC) from its three
-  // level results; or the Y_int export.
-  auto epilogue = [&](int pr, int pc, const v4f (&a3)[3], const v4f (&qq)[3], const uint32_t (&sraw)[NT], int g_) {
+  // level results; or the Y_int export.  The level sums are folded as
+  // Y1 + k*(Y2 + k*Y3) with k = 1/14.98 (= w_2/w_1 = w_3/w_2), then multiplied
+  // by the row's A_max*w_1 and the column's scale and added to the running
+  // sum: 4 VALU per output and group, with one level weight per row held.
+  auto epilogue = [&](int pr, int pc, const v4f (&a3)[3], const v4f& q1, const uint32_t (&sraw)[NT], int g_) {
     if constexpr (YINT) {
       const int64_t gi = g_ - g_begin;
       const int n = n0 + wn * WN + pc * 16 + (lane & 15);
@@ -429,9 +431,9 @@ __global__ __launch_bounds__(pf::THREADS, 1) void msd_gemm_kernel(
       const float sc = half_bits_to_float(sraw[pc]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float tt = a3[0][i] * qq[0][i];
-        tt = __builtin_fmaf(a3[1][i], qq[1][i], tt);
-        tt = __builtin_fmaf(a3[2][i], qq[2][i], tt);
+        float tt = __builtin_fmaf(a3[2][i], kK, a3[1][i]);
+        tt = __builtin_fmaf(tt, kK, a3[0][i]);
+        tt = tt * q1[i];
         yacc[pr][pc][i] = __builtin_fmaf(tt, sc, yacc[pr][pc][i]);
       }
     }
@@ -452,15 +454,13 @@ __global__ __launch_bounds__(pf::THREADS, 1) void msd_gemm_kernel(
 #pragma unroll
     for (int l = 0; l < 3; ++l) lds_operand_pair(sa + (l * RT + wm * MT) * TILE, lane, af[0][l], af[1][l]);
     uint32_t sraw[NT];
-    v4f q[MT][3];                // the row tiles' level weights
+    v4f q[MT];                   // the row tiles' level-1 weights A_max * w_1
     if constexpr (!YINT) {
 #pragma unroll
       for (int c = 0; c < NT; ++c) sraw[c] = ss[wn * WN + c * 16 + (lane & 15)];
 #pragma unroll
       for (int r = 0; r < MT; ++r)
-#pragma unroll
-        for (int l = 0; l < 3; ++l)
-          q[r][l] = *reinterpret_cast<const v4f*>(sq + l * BM + (wm * MT + r) * 16 + 4 * (lane >> 4));
+        q[r] = *reinterpret_cast<const v4f*>(sq + (wm * MT + r) * 16 + 4 * (lane >> 4));
     }
     v4f acc[2][3];               // MFMA results of the current and the previous output tile
 #pragma unroll
