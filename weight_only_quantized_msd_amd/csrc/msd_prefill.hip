@@ -443,9 +443,11 @@ __global__ __launch_bounds__(pf::THREADS, 1) void msd_gemm_kernel(
   // of B operands and its 2 x 3 level operands (one pair per level), then
   // walks its column tiles with the next pair of B operands read ahead (two
   // pairs of B registers in turn): per output tile 3 MFMAs, then the combine
-  // of the previous output tile (so the combine never waits for the MFMA it
-  // follows).  A register that a load overwrites was last read by MFMAs
-  // issued before that load.
+  // of the output tile D before it (so the combine never waits for the MFMAs
+  // it follows).  A register that a load overwrites was last read by MFMAs
+  // issued before that load.  (Issuing one MFMA, then a few VALU, in turn,
+  // through scheduling-group barriers, was slower: 80 -> 84-90 us at
+  // prefill_m2048, the combines then waiting on MFMA results.)
   static_assert(MT == 2 && NT % 2 == 0, "operand tiles are read in pairs");
   auto compute = [&](const uint8_t* sa, const uint8_t* sb, const float* sq, const uint16_t* ss, int g_) {
     v8i bf[2][2];
@@ -462,7 +464,11 @@ __global__ __launch_bounds__(pf::THREADS, 1) void msd_gemm_kernel(
       for (int r = 0; r < MT; ++r)
         q[r] = *reinterpret_cast<const v4f*>(sq + (wm * MT + r) * 16 + 4 * (lane >> 4));
     }
-    v4f acc[2][3];               // MFMA results of the current and the previous output tile
+    // output tiles between an MFMA and its combine: two at 256-column blocks
+    // (the combine then reads results six MFMAs old; prefill_m2048 step
+    // 79.7-80.9 -> 78.2-78.4 us on one box), one otherwise (mixed at 128)
+    constexpr int D = BN == 256 ? 2 : 1;
+    v4f acc[D + 1][3];           // MFMA results of the current and the D previous output tiles
 #pragma unroll
     for (int c = 0; c < NT; ++c) {
       const int cp = c / 2;
@@ -470,19 +476,20 @@ __global__ __launch_bounds__(pf::THREADS, 1) void msd_gemm_kernel(
         lds_operand_pair(sb + (wn * NT + c + 2) * TILE, lane, bf[(cp + 1) & 1][0], bf[(cp + 1) & 1][1]);
 #pragma unroll
       for (int r = 0; r < MT; ++r) {
-        const int j = c * MT + r, cur = j & 1;
+        const int j = c * MT + r, cur = j % (D + 1);
 #pragma unroll
         for (int l = 0; l < 3; ++l)
           acc[cur][l] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
               af[r][l], bf[cp & 1][c & 1], v4f{0.f, 0.f, 0.f, 0.f}, 2, 2, 0, kScaleA, 0, kScaleB);
-        if (j > 0) {
-          const int pc = (j - 1) / MT, pr = (j - 1) % MT;
-          epilogue(pr, pc, acc[cur ^ 1], q[pr], sraw, g_);
+        if (j >= D) {
+          const int pj = j - D, pc = pj / MT, pr = pj % MT;
+          epilogue(pr, pc, acc[pj % (D + 1)], q[pr], sraw, g_);
         }
       }
     }
-    constexpr int jl = MT * NT - 1;
-    epilogue(jl % MT, jl / MT, acc[jl & 1], q[jl % MT], sraw, g_);
+#pragma unroll
+    for (int pj = MT * NT - D; pj < MT * NT; ++pj)
+      epilogue(pj % MT, pj / MT, acc[pj % (D + 1)], q[pj % MT], sraw, g_);
   };
 
   if constexpr (NBUF == 2) {
