@@ -130,8 +130,8 @@ def prefill_splits(M, K, N):
 def prefill_prep_bytes(M, K, N, gs, operand_weights=False):
     """Algorithmic bytes of the prefill preparation kernel: it reads x and
     writes the level operand tiles (1536 bytes each: 16 rows x 128 k at group
-    size 128, 32 rows x 64 k at group size 64) and the level weights (fp32,
-    three per row and group); unless the GEMM converts the weights itself (group
+    size 128, 32 rows x 64 k at group size 64) and the level weights (fp32 per
+    row and group: A_max * w_1 alone at group size 128, all three at 64); unless the GEMM converts the weights itself (group
     size 64 with at most two 128-row blocks) or reads the weights' operand form
     (group size 128, operand_weights), it also reads the tiled int4 weights and
     writes their operand tiles (columns padded to 256 at group size 128, to
@@ -144,7 +144,7 @@ def prefill_prep_bytes(M, K, N, gs, operand_weights=False):
         npad = -(-N // 256) * 256                  # the weight tiles' 256-column blocks
     else:
         npad = -(-N // prefill64_bn(M, N)) * prefill64_bn(M, N)
-    b = 2 * M * K + 1536 * (3 * mpad // per) * G + 12 * mpad * G
+    b = 2 * M * K + 1536 * (3 * mpad // per) * G + (4 if gs == 128 else 12) * mpad * G
     if not w_in_gemm and not (operand_weights and gs == 128):
         b += K * N // 2 + 1536 * (npad // per) * G
     return b
