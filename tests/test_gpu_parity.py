@@ -638,7 +638,7 @@ def test_profile_stages_compose_to_path(torch_dev, name, path):
 
 @pytest.mark.parametrize("name,path,opw", [("decode_m16", DECODE, False), ("ffn_up_m16", DECODE, False),
                                            ("tiny", PREFILL, False), ("outlier_m128", PREFILL, False),
-                                           ("mid_m256", PREFILL, True)])
+                                           ("mid_m256", PREFILL, True), ("prefill_m2048", PREFILL, True)])
 def test_graph_replay_matches_eager(torch_dev, name, path, opw):
     """bench.py submits its timed steps as a captured graph: every replay, with
     eager work and synchronizations in between, must reproduce the eager bits
