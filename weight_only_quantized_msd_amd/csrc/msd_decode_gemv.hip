@@ -343,16 +343,22 @@ __global__ __launch_bounds__(64 * WK) void msd_decode_gemv_multi_kernel(
     for (int i = 0; i < QF; ++i) sQ[wk][QF * lane + i] = qt[qo + i];
   }
 
-  // weights and scales of column tile nt (loads only; unconditional)
+  // weights and scales of column tile nt (loads only).  The loads are issued
+  // whether or not the run has tile nt: past its end every lane reads the
+  // first 16 bytes of the weights and the first scales (one line, results
+  // unused), so that every path issues the same loads and each tile waits
+  // only for its own (a load under a branch leaves the compiler no count to
+  // wait for but zero, which also waits for the next tile's loads).
   auto load_tile = [&](int nt, v4i (&wv)[KBR], uint32_t (&sst)[SV == 4 ? 2 : 1]) __attribute__((always_inline)) {
-    const uint8_t* wcol = wt + (int64_t)nt * KB * 1024 + lane * 16;
+    const bool real = nt < t_hi;                 // uniform
+    const uint8_t* wcol = real ? wt + (int64_t)nt * KB * 1024 + lane * 16 : wt;
 #pragma unroll
     for (int j = 0; j < KBR; ++j) {
       const int kb = wb_lo + j < wb_hi ? wb_lo + j : kb_any;
-      wv[j] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wcol + (int64_t)kb * 1024));
+      wv[j] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wcol + (real ? (int64_t)kb * 1024 : 0)));
     }
     const int gc = min(kb_any * GPB + sgi, G - 1);
-    const uint16_t* sp = scale + (int64_t)gc * N + nt * kTileCols + sc0;
+    const uint16_t* sp = real ? scale + (int64_t)gc * N + nt * kTileCols + sc0 : scale;
     if constexpr (SV == 1) sst[0] = *sp;
     else if constexpr (SV == 2) sst[0] = *reinterpret_cast<const uint32_t*>(sp);
     else {
@@ -464,21 +470,23 @@ __global__ __launch_bounds__(64 * WK) void msd_decode_gemv_multi_kernel(
   };
 
   // a ring of D register sets: the loads of tile t + D are issued as soon as
-  // tile t is computed (a third set, where the registers allow it, measured
-  // slower: 12.9 against 12.2 us at M = 16, K = 4096, N = 11008)
+  // tile t is computed (a third set measured slower: M = 16, K = 4096,
+  // N = 11008 contraction 9.1 against 8.3 us; K = 8192, N = 28672, group
+  // size 64 42.3 against 35.3 us, where it also spills)
   constexpr int D = 2;
   v4i wr[D][KBR];
   uint32_t sr[D][SV == 4 ? 2 : 1];
 #pragma unroll
-  for (int i = 0; i < D; ++i)
-    if (t_lo + i < t_hi) load_tile(t_lo + i, wr[i], sr[i]);
+  for (int i = 0; i < D; ++i) load_tile(t_lo + i, wr[i], sr[i]);
   for (int nt = t_lo; nt < t_hi; nt += D) {
 #pragma unroll
     for (int i = 0; i < D; ++i) {
       const int t = nt + i;
-      if (t >= t_hi) break;                          // uniform
+      // uniform; the run's last tile is done (a return, not a break, so that
+      // no path reaches the loop head without the loads of the pass before)
+      if (t >= t_hi) return;
       do_tile(t, i & 1, wr[i], sr[i]);
-      if (t + D < t_hi) load_tile(t + D, wr[i], sr[i]);
+      load_tile(t + D, wr[i], sr[i]);
     }
   }
 }
