@@ -120,7 +120,10 @@ __global__ __launch_bounds__(64 * WK) void msd_decode_gemv_kernel(
   constexpr int QG = 48 * R;                     // level weights per group: [slice][level][16 rows]
   constexpr int QF = RG * QG / 64;               // staged level weights per lane
   constexpr int SV = RG * 16 / 64;               // staged scales per lane
-  constexpr int D = R <= 2 ? 2 : 1;              // blocks in flight
+  // blocks in flight: at one slice all of a round's (an 8-wave workgroup at
+  // K = 4096: its whole share; M = 8-16, K = N = 4096 step about 1% faster than
+  // two), at two slices two, beyond that one (registers)
+  constexpr int D = R == 1 ? KBW : (R == 2 ? 2 : 1);
   static_assert(QF * 64 == RG * QG && SV * 64 == RG * 16 && (SV == 1 || SV == 2), "round shape");
   static_assert(QG % QF == 0, "a lane's staged level weights lie in one group");
   __shared__ float4 sRed[WK > 1 ? WK - 1 : 1][R][64];

@@ -463,12 +463,17 @@ __global__ __launch_bounds__(64 * WAVES_M * p64::WAVES_N, 1) void msd_gemm64_ker
 // of the GEMM (read K*N/2, write 3*K*N/4 bytes, read again) costs more than
 // the GEMM's own use of it.  This variant reads the tiled int4 weights itself
 // and converts them to e2m3 operands one stage ahead of their use:
-//   iteration s:  waves 0-3 convert the int4 block of stage s+1 (loaded into
-//                 their registers during iteration s-1; column tile w, both
-//                 groups) into the e2m3 buffer of the other parity; copies
-//                 (global_load_lds) of stage s+1's x operands, level weights
-//                 and scales; waves 0-3 load the int4 block of stage s+2; all
-//                 16 waves compute stage s; one barrier.
+//   iteration s:  waves 0-7 convert the int4 block of stage s+1 (loaded into
+//                 their registers during iteration s-1; wave w: column tile
+//                 w % 4, group w / 4 of the stage) into the e2m3 buffer of the
+//                 other parity; copies (global_load_lds) of stage s+1's x
+//                 operands, level weights and scales; waves 0-7 load their
+//                 part of the int4 block of stage s+2; all 16 waves compute
+//                 stage s; one barrier.
+// Two converter waves per SIMD, each converting one group: with one per SIMD
+// converting both groups, the other three waited for that wave's extra VALU
+// work at the barrier (outlier_m128 step 113.5-114.5 -> 111.9-112.4 us,
+// medians of replays, four rounds alternating on one box).
 // The int4 loads are the last memory operations of an iteration and stay in
 // flight across its barrier (the wait before it leaves them outstanding).
 // Buffers: x operands, level weights, scales and e2m3 weights double, 103 KB
@@ -509,7 +514,8 @@ __global__ __launch_bounds__(1024, 1) void msd_gemm64w_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / CT;                    // row tile of 32
   const int wn = wave % CT;                    // column tile of 32
-  const bool converter = wave < CT;            // wave-uniform
+  const bool converter = wave < 2 * CT;        // wave-uniform
+  const int cst = wave / CT;                   // a converter wave's group of the stage
 
   // tile order: as the other GEMMs (contiguous ranges per XCD, bands of BAND
   // row blocks, column-major within a band); speed only
@@ -533,10 +539,11 @@ __global__ __launch_bounds__(1024, 1) void msd_gemm64w_kernel(
   const uint8_t* x_run = x_t + (int64_t)rb * G * X_GROUP;
   const uint32_t s_off = 2u * (uint32_t)min(n0 + 2 * lane, N - 2);   // this lane's scale pair
 
-  // Converter wave c, lane l: column 32c + l%32 of the block, k-half l/32 of
-  // each group; its int4 tile (16 columns; tiles past N read a valid tile,
-  // their outputs are not stored) and the chunk lanes of k-quarters 2(l/32)
-  // and 2(l/32)+1, whose 16 bytes hold the lane's 32 k of both groups.
+  // Converter wave c, lane l: column 32(c % 4) + l%32 of the block, k-half
+  // l/32 of group c / 4 of the stage; its int4 tile (16 columns; tiles past N
+  // read a valid tile, their outputs are not stored) and the chunk lanes of
+  // k-quarters 2(l/32) and 2(l/32)+1, whose 16 bytes hold the lane's 32 k of
+  // both groups (dwords 2c', 2c'+1 of each: group c' = c / 4).
   const int wcol = wn * 32 + (lane & 31);
   const int wtile = min(cb * (BN / kTileCols) + wcol / kTileCols, N / kTileCols - 1);
   const uint8_t* w_lane = wt + (int64_t)wtile * KB * 1024 + ((wcol % kTileCols) + 32 * (lane >> 5)) * 16;
@@ -567,21 +574,17 @@ __global__ __launch_bounds__(1024, 1) void msd_gemm64w_kernel(
       }
     }
   };
-  // the int4 chunk lanes of stage s (converter waves)
-  auto load_w = [&](int s, uint4 (&wr)[2]) {
-    const uint8_t* p = w_lane + (int64_t)(kb0 + s) * 1024;
-    wr[0] = *reinterpret_cast<const uint4*>(p);
-    wr[1] = *reinterpret_cast<const uint4*>(p + 256);
+  // the converter wave's half of its int4 chunk lanes of stage s: dwords
+  // 2cst, 2cst+1 of each
+  auto load_w = [&](int s, uint2 (&wr)[2]) {
+    const uint8_t* p = w_lane + (int64_t)(kb0 + s) * 1024 + 8 * cst;
+    wr[0] = *reinterpret_cast<const uint2*>(p);
+    wr[1] = *reinterpret_cast<const uint2*>(p + 256);
   };
-  // int4 chunk lanes -> the e2m3 operand lanes of both groups (step st:
-  // dwords 2st, 2st+1 of each chunk lane)
-  auto convert = [&](const uint4 (&wr)[2], uint8_t* swf) {
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const uint32_t dw[4] = {st ? wr[0].z : wr[0].x, st ? wr[0].w : wr[0].y,
-                              st ? wr[1].z : wr[1].x, st ? wr[1].w : wr[1].y};
-      store6(swf + st * WF_GROUP + wn * TILE, lane, weight_operand6(dw));
-    }
+  // those dwords -> the e2m3 operand lane of group cst of the stage
+  auto convert = [&](const uint2 (&wr)[2], uint8_t* swf) {
+    const uint32_t dw[4] = {wr[0].x, wr[0].y, wr[1].x, wr[1].y};
+    store6(swf + cst * WF_GROUP + wn * TILE, lane, weight_operand6(dw));
   };
 
   float yacc[16];
@@ -650,7 +653,7 @@ __global__ __launch_bounds__(1024, 1) void msd_gemm64w_kernel(
   // keep every LDS access on its side, and the explicit wait drains the LDS
   // operations and every copy except, in the converter waves, the two int4
   // loads issued last.
-  uint4 wr[2];
+  uint2 wr[2];
   auto iteration = [&](auto P, int s) {
     constexpr int B = decltype(P)::value;
     uint8_t* sx = B ? sX1 : sX0;
