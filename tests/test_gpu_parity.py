@@ -322,11 +322,13 @@ def test_decode_contraction_shapes(torch_dev, M, K, N, gs, gb, ge):
 # More column tiles than CUs (N/16 > 256): the decode contraction's workgroups
 # each cover a run of column tiles with the level chunks held in registers.
 # One and two row slices, both group sizes, up to 4 and up to 8 blocks per
-# wave, waves without blocks (K = 640), and a last workgroup with fewer tiles
-# (one, for the odd-count path).
+# wave, waves without blocks (K = 640, K = 512), and a last workgroup with
+# fewer tiles (one, for the odd-count path).  Runs of 5 and 7 tiles (N =
+# 16640 and 28672) take the loop over tile pairs several times before the
+# run's last tile leaves it.
 MULTI_CASES = [  # (M, K, N, gs)
     (16, 4096, 4128, 128), (9, 8192, 5152, 64), (32, 4096, 6144, 128), (20, 2048, 8224, 64),
-    (5, 640, 4640, 128), (16, 8192, 4160, 128),
+    (5, 640, 4640, 128), (16, 8192, 4160, 128), (16, 1024, 16640, 128), (12, 512, 28672, 64),
 ]
 
 
